@@ -1,0 +1,65 @@
+"""KV-cache write and block copy on numpy arrays (test infrastructure only).
+
+Both operations move bits, so they work on any dtype; bf16 caches are
+passed as uint16 arrays of bit patterns and the results are bit-exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def reshape_and_cache(key_cache: np.ndarray, value_cache: np.ndarray,
+                      key: np.ndarray, value: np.ndarray,
+                      slot_mapping: np.ndarray) -> None:
+    """Write token t's K and V rows to flat row slot_mapping[t] of the cache.
+
+    The cache is block-major [num_blocks, B, Hkv, D]; viewed as
+    [num_blocks * B, Hkv, D], flat row s belongs to block s // B at offset
+    s % B.  "PagedAttention: fragmentation, blocks, block tables": 3. The
+    slot mapping (the padding id is written for tokens that have no slot;
+    block i owns a contiguous range of the backing storage) and step 9 of
+    the worked allocation (each layer's write stores the token at its flat
+    row).
+
+    Reading: a slot that is negative (the padding id, -1) or past the end
+    of the pool is skipped.  Slots are unique within a call.
+    """
+    nb, bs, hkv, d = key_cache.shape
+    assert value_cache.shape == key_cache.shape
+    kflat = key_cache.reshape(nb * bs, hkv, d)
+    vflat = value_cache.reshape(nb * bs, hkv, d)
+    for t, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if 0 <= s < nb * bs:
+            kflat[s] = key[t]
+            vflat[s] = value[t]
+
+
+def copy_blocks(caches, pairs, num_blocks: int) -> None:
+    """cache[dst] <- cache[src] for every (src, dst) pair, whole blocks.
+
+    Each cache is viewed as bytes [num_blocks, -1]; all sources are read
+    before any destination is written, as the fancy-index assignment in
+    the copy-on-write section of "PagedAttention: fragmentation, blocks,
+    block tables" does (one block copy covers every byte of the block).
+
+    Reading: a destination named twice, or a destination that is also a
+    source, makes the result order-dependent and is rejected; ids must lie
+    in [0, num_blocks).
+    """
+    pairs = [(int(s), int(d)) for s, d in pairs]
+    srcs = [s for s, _ in pairs]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block is named twice")
+    if set(dsts) & set(srcs):
+        raise ValueError("a destination block is also a source")
+    for b in srcs + dsts:
+        if not 0 <= b < num_blocks:
+            raise ValueError(f"block id {b} out of range")
+    if not pairs:
+        return
+    for cache in caches:
+        view = cache.reshape(-1).view(np.uint8).reshape(num_blocks, -1)
+        rows = view[srcs].copy()
+        view[dsts] = rows

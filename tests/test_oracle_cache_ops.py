@@ -1,0 +1,69 @@
+"""Pins of the oracle's cache write and block copy."""
+
+import numpy as np
+import pytest
+
+from oracle import attention, cache_ops
+from oracle.pool_model import PoolModel
+from paged_kv_cache_327_amd import workloads
+from tests.oracle_side import NAN_BF16
+
+
+def test_scatter_round_trips_through_table_gather():
+    """Written by flat slot, read back by walking the table: two different
+    index paths must agree on every logical row."""
+    B, nb, hkv, d = 4, 12, 2, 8
+    pool = PoolModel(nb, B, np.random.default_rng(0).permutation(nb))
+    kc = np.full((nb, B, hkv, d), NAN_BF16, dtype=np.uint16)
+    vc = kc.copy()
+    pool.add_seq(0)
+    k, v = workloads.seq_kv_bits(1, 0, 23, hkv, d)
+    slots, _ = pool.append(0, 10)
+    cache_ops.reshape_and_cache(kc, vc, k[:10], v[:10], np.array(slots))
+    slots, _ = pool.append(0, 13)
+    cache_ops.reshape_and_cache(kc, vc, k[10:], v[10:], np.array(slots))
+    for g in range(hkv):
+        got = attention.gather_sequence(kc, pool.block_table(0), 23, g)
+        assert np.array_equal(got, attention.bf16_to_f64(k[:, g]))
+        got = attention.gather_sequence(vc, pool.block_table(0), 23, g)
+        assert np.array_equal(got, attention.bf16_to_f64(v[:, g]))
+    # exactly 23 rows written, the tail slot of the last block untouched
+    assert np.sum(np.all(kc == NAN_BF16, axis=(2, 3))) == nb * B - 23
+
+
+def test_padding_and_out_of_range_slots_are_skipped():
+    kc = np.zeros((2, 2, 1, 4), dtype=np.uint16)
+    vc = kc.copy()
+    k = np.arange(16, dtype=np.uint16).reshape(4, 1, 4) + 1
+    v = k + 100
+    cache_ops.reshape_and_cache(kc, vc, k, v, np.array([-1, 3, 4, 0]))
+    flat = kc.reshape(4, 1, 4)
+    assert np.array_equal(flat[3], k[1]) and np.array_equal(flat[0], k[3])
+    assert np.all(flat[1] == 0) and np.all(flat[2] == 0)
+    assert np.array_equal(vc.reshape(4, 1, 4)[3], v[1])
+
+
+def test_copy_blocks_matches_fancy_index():
+    rng = np.random.default_rng(3)
+    nb = 10
+    caches = [rng.integers(0, 2**16, size=(nb, 4, 2, 8), dtype=np.uint16) for _ in range(3)]
+    pairs = [(1, 7), (1, 8), (4, 2)]
+    expect = []
+    for c in caches:
+        e = c.copy()
+        e[[7, 8, 2]] = c[[1, 1, 4]]
+        expect.append(e)
+    cache_ops.copy_blocks(caches, pairs, nb)
+    for c, e in zip(caches, expect):
+        assert np.array_equal(c, e)
+
+
+def test_copy_blocks_rejects_ambiguous_pairs():
+    c = np.zeros((4, 2), dtype=np.uint16)
+    with pytest.raises(ValueError):
+        cache_ops.copy_blocks([c], [(0, 1), (2, 1)], 4)
+    with pytest.raises(ValueError):
+        cache_ops.copy_blocks([c], [(0, 1), (1, 2)], 4)
+    with pytest.raises(ValueError):
+        cache_ops.copy_blocks([c], [(0, 4)], 4)
+    cache_ops.copy_blocks([c], [], 4)
