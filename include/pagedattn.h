@@ -1,0 +1,276 @@
+/*
+ * libpagedattn -- paged attention over a block-paged KV cache on MI355X (gfx950).
+ *
+ * The KV cache is cut into fixed-size blocks of block_size (B) tokens; each
+ * sequence owns an append-only list of physical block ids (its block table),
+ * and every attention call gathers K/V by walking that list in logical order.
+ * ("PagedAttention: fragmentation, blocks, block tables", sections 1-3 and the
+ * attention-metadata section; "The pantry of pigeonholes", "The mechanism";
+ * "Memory management", Concept.)
+ *
+ * Conventions
+ *   - Every call returns int status: PA_OK, PA_ERR_INVALID (bad argument, shape,
+ *     pointer, id or duplicate), PA_ERR_NO_SPACE (the pool cannot supply the
+ *     blocks: the allocate-returns-None case of the slot-allocation section) or
+ *     PA_ERR_HIP (a HIP launch failed).  pa_last_error() describes the most
+ *     recent failure on the calling thread.
+ *   - Pool calls are all-or-nothing: on any error the pool is unchanged (CPU
+ *     reference allocator section: a failed allocation leaves the sequence
+ *     intact; "Memory management", Code: the capacity test precedes any change).
+ *   - Ownership: the library owns the pool's host memory behind the opaque
+ *     handle.  The caller owns every device buffer.  The library never
+ *     allocates device memory; decode split-K scratch is a caller workspace
+ *     sized by pa_paged_decode_workspace_size().
+ *   - Device calls are asynchronous on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream) and never synchronize.  Argument errors are
+ *     detected on the host before anything is enqueued.
+ *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *
+ * KV-cache layout (fixed)
+ *   key_cache and value_cache are separate bf16 arrays.  Physical block b of a
+ *   cache starts at element b * cache_block_stride and is laid out
+ *   [B][num_kv_heads][head_dim] (token-major), so with
+ *   cache_block_stride == B * num_kv_heads * head_dim the cache is the flat
+ *   row-major [num_blocks * B][num_kv_heads][head_dim] array whose row s is
+ *   slot s.  Block i then owns the contiguous range [i*page, (i+1)*page)
+ *   (block-major storage, slot-mapping section).  A larger stride lets one
+ *   allocation interleave several layers or K with V.
+ *
+ * Block tables are int32 [num_seqs][bt_stride]; row s lists sequence s's
+ * physical blocks in logical order and only its first ceil(seq_lens[s] / B)
+ * entries are read (attention-metadata section).  Entries past that may hold
+ * anything.  Every entry that is read must lie in [0, num_blocks); kernels
+ * clamp entries into that range so that a corrupt table cannot make them read
+ * outside the cache (the result is then wrong, but no fault occurs).
+ *
+ * Supported kernel shapes: head_dim in {64, 128}; num_q_heads a multiple of
+ * num_kv_heads with num_q_heads / num_kv_heads <= 8 (query head h reads KV
+ * head h / (num_q_heads / num_kv_heads)); block_size a power of two in
+ * [1, 256].  Anything else returns PA_ERR_INVALID.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,
+  PA_ERR_NO_SPACE = -2,
+  PA_ERR_HIP = -3
+};
+
+/* Text of the most recent error on this thread ("" if none).  The pointer
+ * stays valid until the next failing call on the same thread. */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Host block pool (CPU only, not thread-safe: one pool per thread at a time) */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pa_pool pa_pool;
+
+/* Create a pool of num_blocks blocks of block_size tokens.  All blocks start
+ * free with reference count 0, queued in ascending id order, or in the order
+ * of initial_free_order (a permutation of 0..num_blocks-1) when it is not
+ * NULL.  There is no reserved null block: every id is allocatable.
+ * ("PagedAttention: fragmentation, blocks, block tables", 1. The block pool:
+ * one metadata entry per physical block, all queued at construction.)
+ * Errors: PA_ERR_INVALID for non-positive sizes, a non-permutation or a NULL
+ * `out`. */
+int pa_pool_create(int32_t num_blocks, int32_t block_size,
+                   const int32_t* initial_free_order, pa_pool** out);
+
+/* Destroy a pool (NULL is ignored). */
+void pa_pool_destroy(pa_pool* pool);
+
+/* Register a sequence with an empty block table.  Errors: PA_ERR_INVALID if
+ * seq_id already exists. */
+int pa_pool_add_seq(pa_pool* pool, int64_t seq_id);
+
+/* New sequence dst_seq shares every block of src_seq (same table, same
+ * length); each shared block's reference count grows by one.  Full blocks are
+ * then shared outright and a partial tail is copied on first write ("Memory
+ * management", Maths; copy-on-write section: sharing by reference counts).
+ * Errors: PA_ERR_INVALID if src_seq is unknown or dst_seq exists. */
+int pa_pool_fork(pa_pool* pool, int64_t src_seq, int64_t dst_seq);
+
+/* Append n_tokens >= 1 tokens to seq_id.
+ *   needed = ceil((len + n) / B) - held;  copy = (len % B != 0) and
+ *   refcount(tail) > 1.  If needed + copy exceeds the free blocks, return
+ *   PA_ERR_NO_SPACE and change nothing.  Otherwise, if copy: pop dst from the
+ *   head of the free queue (ref 1), drop one reference of the shared tail src,
+ *   replace the tail entry in place and report (src, dst) in cow_pair_out; then
+ *   pop `needed` blocks (ref 1) onto the table, and write the slot of every new
+ *   position p in [len, len + n):  slot = table[p / B] * B + p % B.
+ * ("Memory management", Code: append with copy-on-write; "PagedAttention:
+ * fragmentation, blocks, block tables": get_new_blocks pops from the head,
+ * the block table is append-only, 3. The slot mapping, and the copy-on-write
+ * section's in-place redirect with a queued (src, dst) copy.)
+ * slots_out: host int64 [n_tokens].  cow_pair_out: host int32 [2], set to
+ * {-1, -1} when no copy is needed.  The caller must copy block src to dst
+ * (pa_copy_blocks) before any write to dst and before src can be reused.
+ * Errors: PA_ERR_INVALID (unknown seq, n_tokens < 1, NULL outputs),
+ * PA_ERR_NO_SPACE (pool unchanged). */
+int pa_pool_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens,
+                   int64_t* slots_out, int32_t* cow_pair_out);
+
+/* pa_pool_append for n_seqs sequences in order.  slots_out receives the slots
+ * of all sequences concatenated (sum of n_tokens entries); cow_pairs_out is
+ * [n_seqs][2].  Stops at the first failing sequence and returns its error;
+ * *n_done (required) is the number of sequences appended, whose results stay
+ * committed (each single append is all-or-nothing). */
+int pa_pool_append_batch(pa_pool* pool, const int64_t* seq_ids, const int32_t* n_tokens,
+                         int32_t n_seqs, int64_t* slots_out, int32_t* cow_pairs_out,
+                         int32_t* n_done);
+
+/* Release seq_id: walk its blocks from the tail to the head, drop one
+ * reference each, and put the blocks that reach zero at the head of the free
+ * queue in that order, so the sequence's tail block is the next one reused.
+ * ("PagedAttention: fragmentation, blocks, block tables", 1. The block pool:
+ * free_blocks takes blocks ordered by eviction priority, first evicted first;
+ * non-cached blocks go to the front; a request frees its blocks in reverse.)
+ * Errors: PA_ERR_INVALID if seq_id is unknown. */
+int pa_pool_free_seq(pa_pool* pool, int64_t seq_id);
+
+/* Write the block tables of n_seqs sequences into table_out (host int32
+ * [n_seqs][bt_stride]): row i gets ceil(len_i / B) block ids; the rest of the
+ * row is not written.  seq_lens_out (host int32 [n_seqs], nullable) gets the
+ * lengths.  Errors: PA_ERR_INVALID for an unknown sequence, a row longer than
+ * bt_stride or a length above INT32_MAX (nothing written). */
+int pa_pool_block_table(const pa_pool* pool, const int64_t* seq_ids, int32_t n_seqs,
+                        int32_t* table_out, int32_t bt_stride, int32_t* seq_lens_out);
+
+/* Number of free blocks (the capacity test is a subtraction against it). */
+int pa_pool_num_free(const pa_pool* pool, int32_t* out);
+/* Reference count of block_id.  Errors: PA_ERR_INVALID if out of range. */
+int pa_pool_refcount(const pa_pool* pool, int32_t block_id, int32_t* out);
+/* Token count of seq_id. */
+int pa_pool_seq_len(const pa_pool* pool, int64_t seq_id, int64_t* out);
+/* The free queue from head to tail: writes min(cap, free) ids, *n_out = free. */
+int pa_pool_free_order(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
+
+/* Check the allocator invariants (CPU reference allocator section): free and
+ * allocated blocks are disjoint and cover every block once; every table entry
+ * is a valid id whose reference count equals its number of owners; no table
+ * repeats a block; each table holds exactly ceil(len / B) blocks.
+ * Returns PA_OK or PA_ERR_INVALID with the first violation in pa_last_error. */
+int pa_pool_check(const pa_pool* pool);
+
+/* Blocks that fit in pool_bytes: floor(floor(pool_bytes / bytes_per_token) /
+ * block_size) -- the two floor divisions of the first page's budget
+ * paragraph.  Returns -1 for non-positive bytes_per_token or block_size or a
+ * negative pool_bytes. */
+int64_t pa_blocks_for_bytes(int64_t pool_bytes, int64_t bytes_per_token, int32_t block_size);
+
+/* ------------------------------------------------------------------------ */
+/* Device calls (gfx950), asynchronous on `stream`                           */
+/* ------------------------------------------------------------------------ */
+
+/* Store each new token's K and V rows at its slot: row t of key/value
+ * ([num_tokens][num_kv_heads][head_dim] bf16, consecutive tokens
+ * key_row_stride / value_row_stride elements apart, heads contiguous) goes to
+ * slot slot_mapping[t], i.e. block slot / B at offset slot % B.  A slot of -1
+ * (the padding id) -- or any slot outside [0, num_blocks * B) -- is skipped.
+ * Slots must be unique within a call.
+ * ("PagedAttention: fragmentation, blocks, block tables", 3. The slot mapping:
+ * one int64 per scheduled token, a flat index into block-major storage, the
+ * padding id for tokens without a slot; worked allocation, step 9.)
+ * All pointers are device pointers, 16-byte aligned; strides multiples of 8.
+ * Bit-exact copy. */
+int pa_reshape_and_cache(const void* key, int64_t key_row_stride,
+                         const void* value, int64_t value_row_stride,
+                         void* key_cache, void* value_cache, int64_t cache_block_stride,
+                         int32_t num_blocks, const int64_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, void* stream);
+
+/* Copy whole blocks: for every cache c and pair (src, dst),
+ * bytes [0, block_bytes) of block dst <- the same bytes of block src, where
+ * block b of cache c starts at caches[c] + b * cache_block_stride_bytes.
+ * All sources are read before any destination is written.
+ * ("PagedAttention: fragmentation, blocks, block tables", copy-on-write
+ * section: the pairs travel from the scheduler as (src, dst) ids and one
+ * copy covers every byte of the block in every listed tensor.)
+ * caches: HOST array of n_caches device pointers.  pairs: HOST int32
+ * [n_pairs][2] (src, dst), e.g. the pairs pa_pool_append returned; the library
+ * passes them to the kernel by value, so no staging copy is needed.
+ * Errors: PA_ERR_INVALID for an id outside [0, num_blocks), a destination
+ * named twice, a destination that is also a source, block_bytes not a
+ * positive multiple of 16 or above the stride, or unaligned pointers. */
+int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes,
+                   int64_t cache_block_stride_bytes, int32_t num_blocks,
+                   const int32_t* pairs, int32_t n_pairs, void* stream);
+
+/* Bytes of workspace pa_paged_decode needs (0 when one partition covers
+ * max_seq_len, i.e. no split). */
+size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_seq_len,
+                                      int32_t partition_size);
+
+/* Single-query attention per sequence over its paged K/V.
+ * For sequence s and query head h (KV head g = h / (num_q_heads/num_kv_heads)):
+ *   x_t = scale * <q[s,h], K_t>  for the seq_lens[s] tokens t of the sequence,
+ *   out[s,h] = sum_t softmax(x)_t V_t   (bf16), lse[s,h] = ln sum_t exp(x_t),
+ * where token t is row t % B of block block_tables[s][t / B].
+ * ("PagedAttention: fragmentation, blocks, block tables", attention-metadata
+ * section: the kernel gathers past K/V by walking row s of the block table for
+ * ceil(seq_lens[s] / B) entries; seq_lens counts the tokens already written,
+ * including this step's.  Split-K, named there without detail: partition p
+ * covers tokens [p*P, (p+1)*P) and partitions are merged with the
+ * log-sum-exp identity.)
+ * q, out: device bf16 [num_seqs][num_q_heads][head_dim], contiguous.
+ * lse: device fp32 [num_seqs][num_q_heads] or NULL.
+ * seq_lens: device int32 [num_seqs]; each must be <= max_seq_len (longer
+ * sequences are truncated to max_seq_len); a length of 0 yields out = 0 and
+ * lse = -inf.  ceil(max_seq_len / B) must not exceed bt_stride.
+ * partition_size: 0 = one partition per sequence; otherwise a multiple of 64
+ * and of block_size.  workspace: device buffer of at least
+ * pa_paged_decode_workspace_size(...) bytes (may be NULL when that is 0),
+ * 256-byte aligned; its contents on entry do not matter.
+ * Arithmetic: fp32 accumulation of bf16 products; softmax weights are rounded
+ * to bf16 before they multiply V. */
+int pa_paged_decode(void* out, float* lse, const void* q,
+                    const void* key_cache, const void* value_cache,
+                    int64_t cache_block_stride, int32_t num_blocks,
+                    const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                    int32_t partition_size, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Chunked-prefill attention of query chunks over their paged context.
+ * Request i's queries are rows query_start_loc[i] .. query_start_loc[i+1]-1 of
+ * q; they are the last q_i = query_start_loc[i+1] - query_start_loc[i] tokens
+ * of its seq_lens[i] tokens, already written to the cache.  Query j of request
+ * i (absolute position c_i + j, c_i = seq_lens[i] - q_i) attends to keys
+ * 0 .. c_i + j when causal != 0, else to all seq_lens[i] keys.
+ * ("PagedAttention: fragmentation, blocks, block tables", attention-metadata
+ * section: query_start_loc, seq_lens, max_query_len, max_seq_len, the block
+ * table and the gather by table walk.)
+ * q, out: device bf16 [total_q][num_q_heads][head_dim], contiguous, with
+ * total_q = query_start_loc[num_seqs].  query_start_loc: device int32
+ * [num_seqs + 1], non-decreasing, starting at 0; seq_lens: device int32
+ * [num_seqs] with q_i <= seq_lens[i] <= max_seq_len; max_query_len bounds
+ * every q_i.  ceil(max_seq_len / B) must not exceed bt_stride.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; softmax weights are
+ * rounded to bf16 before the PV product. */
+int pa_paged_prefill(void* out, const void* q,
+                     const void* key_cache, const void* value_cache,
+                     int64_t cache_block_stride, int32_t num_blocks,
+                     const int32_t* block_tables, int32_t bt_stride,
+                     const int32_t* query_start_loc, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, float scale, int32_t causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

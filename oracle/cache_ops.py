@@ -38,7 +38,7 @@ def reshape_and_cache(key_cache: np.ndarray, value_cache: np.ndarray,
 def copy_blocks(caches, pairs, num_blocks: int) -> None:
     """cache[dst] <- cache[src] for every (src, dst) pair, whole blocks.
 
-    Each cache is viewed as bytes [num_blocks, -1]; all sources are read
+    Axis 0 of each cache indexes blocks; all sources are read
     before any destination is written, as the fancy-index assignment in
     the copy-on-write section of "PagedAttention: fragmentation, blocks,
     block tables" does (one block copy covers every byte of the block).
@@ -60,6 +60,9 @@ def copy_blocks(caches, pairs, num_blocks: int) -> None:
     if not pairs:
         return
     for cache in caches:
-        view = cache.reshape(-1).view(np.uint8).reshape(num_blocks, -1)
-        rows = view[srcs].copy()
-        view[dsts] = rows
+        # axis 0 indexes blocks; each block row holds all of its bytes, and
+        # indexing a (possibly strided) view writes through to its base
+        if cache.shape[0] != num_blocks:
+            raise ValueError("axis 0 of every cache must index the blocks")
+        rows = cache[srcs].copy()
+        cache[dsts] = rows

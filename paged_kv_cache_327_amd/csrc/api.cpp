@@ -1,0 +1,232 @@
+// C-ABI entry points of the device calls: every argument is validated on the
+// host before anything is enqueued, then the HIP launcher runs.  Pool entry
+// points live in pool.cpp.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "internal.hpp"
+#include "pagedattn.h"
+
+namespace pa {
+namespace {
+thread_local std::string g_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+}  // namespace pa
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+  int r = 0;
+  while ((int64_t{1} << r) < x) ++r;
+  return r;
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_heads(const char* fn, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+  if (head_dim != 64 && head_dim != 128) return pa::fail(PA_ERR_INVALID, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8)
+    return pa::fail(PA_ERR_INVALID, "%s: num_q_heads %d must be a multiple (<= 8x) of num_kv_heads %d", fn,
+                    num_q_heads, num_kv_heads);
+  if (!is_pow2(block_size) || block_size > 256)
+    return pa::fail(PA_ERR_INVALID, "%s: block_size %d is not a power of two in [1, 256]", fn, block_size);
+  return PA_OK;
+}
+
+int check_cache(const char* fn, const void* kc, const void* vc, int64_t block_stride, int32_t num_blocks,
+                int32_t block_size, int64_t row_elems) {
+  if (!kc || !vc) return pa::fail(PA_ERR_INVALID, "%s: NULL cache pointer", fn);
+  if (!aligned(kc, 16) || !aligned(vc, 16)) return pa::fail(PA_ERR_INVALID, "%s: caches must be 16-byte aligned", fn);
+  if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID, "%s: num_blocks %d must be positive", fn, num_blocks);
+  if (block_stride < (int64_t)block_size * row_elems || block_stride % 8 != 0)
+    return pa::fail(PA_ERR_INVALID, "%s: cache_block_stride %lld must be a multiple of 8 and >= B*Hkv*D = %lld", fn,
+                    (long long)block_stride, (long long)((int64_t)block_size * row_elems));
+  return PA_OK;
+}
+
+int hip_status(const char* fn, int err) {
+  if (err != 0) return pa::fail(PA_ERR_HIP, "%s: HIP error %d (%s)", fn, err, pa::hip_error_string(err));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_error.c_str(); }
+
+int pa_reshape_and_cache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                         void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, void* stream) {
+  pa::clear_error();
+  const char* fn = "reshape_and_cache";
+  if (int rc = check_heads(fn, num_kv_heads, num_kv_heads, head_dim, block_size)) return rc;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (num_tokens < 0) return pa::fail(PA_ERR_INVALID, "%s: num_tokens %d < 0", fn, num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return pa::fail(PA_ERR_INVALID, "%s: NULL input", fn);
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
+    return pa::fail(PA_ERR_INVALID, "%s: key/value must be 16-byte aligned", fn);
+  if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 || value_row_stride % 8)
+    return pa::fail(PA_ERR_INVALID, "%s: row strides must be multiples of 8 and >= Hkv*D", fn);
+  pa::ReshapeArgs a{key, key_row_stride, value, value_row_stride, key_cache, value_cache, cache_block_stride,
+                    (int64_t)num_blocks * block_size, slot_mapping, num_tokens, (int32_t)row, ilog2(block_size)};
+  return hip_status(fn, pa::launch_reshape_and_cache(a, stream));
+}
+
+int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
+                   int32_t num_blocks, const int32_t* pairs, int32_t n_pairs, void* stream) {
+  pa::clear_error();
+  const char* fn = "copy_blocks";
+  if (n_pairs < 0 || n_caches < 0) return pa::fail(PA_ERR_INVALID, "%s: negative count", fn);
+  if (n_pairs == 0 || n_caches == 0) return PA_OK;
+  if (!caches || !pairs) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (block_bytes <= 0 || block_bytes % 16 || stride_bytes < block_bytes || stride_bytes % 16)
+    return pa::fail(PA_ERR_INVALID, "%s: block_bytes %lld must be a positive multiple of 16 <= stride %lld", fn,
+                    (long long)block_bytes, (long long)stride_bytes);
+  if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  for (int32_t c = 0; c < n_caches; ++c)
+    if (!caches[c] || !aligned(caches[c], 16)) return pa::fail(PA_ERR_INVALID, "%s: cache %d NULL or unaligned", fn, c);
+  std::unordered_set<int32_t> dsts, srcs;
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+      return pa::fail(PA_ERR_INVALID, "%s: pair %d (%d, %d) outside [0, %d)", fn, i, s, d, num_blocks);
+    if (!dsts.insert(d).second) return pa::fail(PA_ERR_INVALID, "%s: destination %d named twice", fn, d);
+    srcs.insert(s);
+  }
+  for (int32_t d : dsts)
+    if (srcs.count(d)) return pa::fail(PA_ERR_INVALID, "%s: block %d is both a source and a destination", fn, d);
+  return hip_status(fn, pa::launch_copy_blocks(caches, n_caches, block_bytes, stride_bytes, pairs, n_pairs, stream));
+}
+
+size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                                      int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition_size <= 0) return 0;
+  const int64_t parts = ((int64_t)max_seq_len + partition_size - 1) / partition_size;
+  if (parts <= 1) return 0;
+  const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+  const int64_t out_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+  return (size_t)(out_bytes + rows * 4);
+}
+
+int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,
+                    int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_seq_len, int32_t partition_size, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  pa::clear_error();
+  const char* fn = "paged_decode";
+  if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (num_seqs < 0) return pa::fail(PA_ERR_INVALID, "%s: num_seqs < 0", fn);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !block_tables || !seq_lens) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(out, 16) || !aligned(q, 16) || (lse && !aligned(lse, 4)))
+    return pa::fail(PA_ERR_INVALID, "%s: q/out must be 16-byte aligned", fn);
+  if (max_seq_len <= 0) return pa::fail(PA_ERR_INVALID, "%s: max_seq_len must be positive", fn);
+  if (((int64_t)max_seq_len + block_size - 1) / block_size > bt_stride)
+    return pa::fail(PA_ERR_INVALID, "%s: ceil(max_seq_len / B) exceeds bt_stride %d", fn, bt_stride);
+  if (partition_size < 0 || (partition_size > 0 && (partition_size % 64 || partition_size % block_size)))
+    return pa::fail(PA_ERR_INVALID, "%s: partition_size %d must be 0 or a multiple of 64 and of B", fn,
+                    partition_size);
+  if (!(scale == scale)) return pa::fail(PA_ERR_INVALID, "%s: scale is NaN", fn);
+  int32_t P = partition_size;
+  if (P == 0 || P >= max_seq_len) P = (int32_t)(((int64_t)max_seq_len + 63) / 64 * 64);
+  const int64_t parts = ((int64_t)max_seq_len + P - 1) / P;
+  const size_t need = pa_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, P);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+  if (parts > 65535) return pa::fail(PA_ERR_INVALID, "%s: too many partitions (%lld)", fn, (long long)parts);
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.cache_block_stride = cache_block_stride;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.log2_block_size = ilog2(block_size);
+  a.max_seq_len = max_seq_len;
+  a.partition_size = P;
+  a.max_parts = (int32_t)parts;
+  a.scale = scale;
+  if (parts > 1) {
+    const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
+    a.ws_out = static_cast<float*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((rows * head_dim * 4) + 255) / 256 * 256);
+  }
+  return hip_status(fn, pa::launch_paged_decode(a, stream));
+}
+
+int pa_paged_prefill(void* out, const void* q, const void* key_cache, const void* value_cache,
+                     int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                     const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+                     int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, float scale, int32_t causal, void* stream) {
+  pa::clear_error();
+  const char* fn = "paged_prefill";
+  if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (num_seqs < 0 || max_query_len < 0) return pa::fail(PA_ERR_INVALID, "%s: negative size", fn);
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !block_tables || !query_start_loc || !seq_lens)
+    return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(out, 16) || !aligned(q, 16)) return pa::fail(PA_ERR_INVALID, "%s: q/out must be 16-byte aligned", fn);
+  if (max_seq_len <= 0 || max_query_len > max_seq_len)
+    return pa::fail(PA_ERR_INVALID, "%s: need 0 < max_query_len <= max_seq_len", fn);
+  if (((int64_t)max_seq_len + block_size - 1) / block_size > bt_stride)
+    return pa::fail(PA_ERR_INVALID, "%s: ceil(max_seq_len / B) exceeds bt_stride %d", fn, bt_stride);
+  if (!(scale == scale)) return pa::fail(PA_ERR_INVALID, "%s: scale is NaN", fn);
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.cache_block_stride = cache_block_stride;
+  a.num_blocks = num_blocks;
+  a.block_tables = block_tables;
+  a.bt_stride = bt_stride;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.log2_block_size = ilog2(block_size);
+  a.scale = scale;
+  a.causal = causal;
+  return hip_status(fn, pa::launch_paged_prefill(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal declarations shared by the C-ABI layer and the HIP launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+// Records the thread-local error text and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Launchers (defined in the .hip translation units).  They enqueue on
+// `stream` and return a hipError_t value (0 on success); arguments have been
+// validated by the caller.
+struct ReshapeArgs {
+  const void* key;
+  int64_t key_row_stride;
+  const void* value;
+  int64_t value_row_stride;
+  void* key_cache;
+  void* value_cache;
+  int64_t cache_block_stride;
+  int64_t num_slots;  // num_blocks * block_size
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_elems;  // num_kv_heads * head_dim
+  int32_t log2_block_size;
+};
+int launch_reshape_and_cache(const ReshapeArgs& a, void* stream);
+
+int launch_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes,
+                       int64_t stride_bytes, const int32_t* pairs, int32_t n_pairs,
+                       void* stream);
+
+struct DecodeArgs {
+  void* out;
+  float* lse;
+  const void* q;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t cache_block_stride;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t log2_block_size;
+  int32_t max_seq_len;
+  int32_t partition_size;  // > 0, multiple of 64 and of the block size
+  int32_t max_parts;
+  float scale;
+  float* ws_out;  // [S][Hq][max_parts][D]   (max_parts > 1 only)
+  float* ws_lse;  // [S][Hq][max_parts]
+};
+int launch_paged_decode(const DecodeArgs& a, void* stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* key_cache;
+  const void* value_cache;
+  int64_t cache_block_stride;
+  int32_t num_blocks;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  int32_t num_seqs, max_query_len, max_seq_len;
+  int32_t num_q_heads, num_kv_heads, head_dim;
+  int32_t log2_block_size;
+  float scale;
+  int32_t causal;
+};
+int launch_paged_prefill(const PrefillArgs& a, void* stream);
+
+const char* hip_error_string(int err);
+
+}  // namespace pa

@@ -1,0 +1,108 @@
+// KV-cache write by slot mapping and whole-block copy-on-write copies.
+//
+// Both kernels move bits with 16-byte vector loads and stores and are bound
+// by HBM bandwidth.
+#include "../internal.hpp"
+#include "common.hpp"
+
+namespace pa {
+namespace {
+
+// One wave per token: the wave reads the token's slot once (wave-uniform,
+// so it is a scalar load) and copies its K and V rows (Hkv*D bf16 each) in
+// 16-byte pieces.  "PagedAttention: fragmentation, blocks, block tables",
+// 3. The slot mapping: the write goes to flat row slot of block-major storage,
+// block slot / B at offset slot % B; the padding id (-1) writes nothing.
+__global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.num_tokens) return;
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot >> a.log2_block_size;
+  const int64_t off = slot & ((int64_t{1} << a.log2_block_size) - 1);
+  const int64_t dst = blk * a.cache_block_stride + off * a.row_elems;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + t * a.key_row_stride);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.value) + t * a.value_row_stride);
+  uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
+  uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
+  const int nvec = a.row_elems >> 3;
+  for (int c = lane; c < nvec; c += 64) {
+    const uint4 k = ks[c];
+    const uint4 v = vs[c];
+    kd[c] = k;
+    vd[c] = v;
+  }
+}
+
+constexpr int kMaxCopyCaches = 64;
+constexpr int kMaxCopyPairs = 128;
+constexpr int kCopyUnroll = 4;  // 16-byte vectors per thread per pass
+
+// Pairs and cache pointers travel in the kernel arguments (about 1.6 KiB), so
+// the host's pair list needs no staging buffer.
+struct CopyBatch {
+  char* caches[kMaxCopyCaches];
+  int32_t pairs[2 * kMaxCopyPairs];
+  int64_t block_bytes;
+  int64_t stride_bytes;
+};
+
+// grid = (chunks per block, pairs, caches).  Each chunk is 256 threads x
+// kCopyUnroll x 16 B.  No destination is a source (checked on the host), so
+// the copies are independent and the order of the pairs does not matter.
+// "PagedAttention: fragmentation, blocks, block tables", copy-on-write
+// section: blocks[dst] = blocks[src] over the byte view of every cache tensor.
+__global__ void __launch_bounds__(256) copy_blocks_kernel(CopyBatch b) {
+  const int pair = blockIdx.y, cache = blockIdx.z;
+  const int64_t src = b.pairs[2 * pair], dst = b.pairs[2 * pair + 1];
+  const uint4* s = reinterpret_cast<const uint4*>(b.caches[cache] + src * b.stride_bytes);
+  uint4* d = reinterpret_cast<uint4*>(b.caches[cache] + dst * b.stride_bytes);
+  const int64_t nvec = b.block_bytes >> 4;
+  const int64_t base = (int64_t)blockIdx.x * (256 * kCopyUnroll) + threadIdx.x;
+  uint4 v[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < nvec) v[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < nvec) d[i] = v[u];
+  }
+}
+
+}  // namespace
+
+int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
+  const unsigned grid = (unsigned)((a.num_tokens + 3) / 4);
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
+                       const int32_t* pairs, int32_t n_pairs, void* stream) {
+  const int64_t nvec = block_bytes >> 4;
+  const unsigned chunks = (unsigned)((nvec + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll));
+  for (int32_t c0 = 0; c0 < n_caches; c0 += kMaxCopyCaches) {
+    const int32_t nc = n_caches - c0 < kMaxCopyCaches ? n_caches - c0 : kMaxCopyCaches;
+    for (int32_t p0 = 0; p0 < n_pairs; p0 += kMaxCopyPairs) {
+      const int32_t np = n_pairs - p0 < kMaxCopyPairs ? n_pairs - p0 : kMaxCopyPairs;
+      CopyBatch b{};
+      for (int32_t i = 0; i < nc; ++i) b.caches[i] = static_cast<char*>(caches[c0 + i]);
+      for (int32_t i = 0; i < 2 * np; ++i) b.pairs[i] = pairs[2 * p0 + i];
+      b.block_bytes = block_bytes;
+      b.stride_bytes = stride_bytes;
+      hipLaunchKernelGGL(copy_blocks_kernel, dim3(chunks, (unsigned)np, (unsigned)nc), dim3(256), 0,
+                         (hipStream_t)stream, b);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return (int)e;
+    }
+  }
+  return 0;
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace pa

@@ -33,12 +33,13 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def seq_kv_bits(seed: int, seq: int, n_tokens: int, num_kv_heads: int, head_dim: int,
-                layer: int = 0):
-    """Logical K and V rows [n, Hkv, D] (bf16 bits) of one sequence.
+                layer: int = 0, part: int = 0):
+    """K and V rows [n, Hkv, D] (bf16 bits) of one piece of one sequence:
+    part 0 is its context, part 1 the tokens of the measured step.
 
-    Each sequence has its own stream, so any sequence can be regenerated
-    alone for a sampled check."""
-    rng = np.random.default_rng([seed, 11, layer, seq])
+    Each (layer, sequence, part) has its own stream, so any piece can be
+    regenerated alone for a sampled check."""
+    rng = np.random.default_rng([seed, 11, layer, seq, part])
     k = normal_bf16(rng, (n_tokens, num_kv_heads, head_dim))
     v = normal_bf16(rng, (n_tokens, num_kv_heads, head_dim))
     return k, v
@@ -72,6 +73,42 @@ class Workload:
     num_layers: int = 1
     forks: list = field(default_factory=list)
     shared_prefix: int = 0
+    q_lens: list = None
+
+    def __post_init__(self):
+        if self.q_lens is None:
+            self.q_lens = list(self.new_lens)
+
+    def pieces(self, seq: int):
+        """(source sequence, part, n_tokens) pieces that make up ``seq`` in
+        logical order: a forked sequence starts with its source's context."""
+        src = seq
+        for a, b in self.forks:
+            if b == seq:
+                src = a
+        out = []
+        if self.ctx_lens[src]:
+            out.append((src, 0, self.ctx_lens[src]))
+        out.append((seq, 1, self.new_lens[seq]))
+        return out
+
+    def logical_kv(self, seq: int, layer: int = 0):
+        ks, vs = [], []
+        for src, part, n in self.pieces(seq):
+            k, v = seq_kv_bits(self.seed, src, n, self.num_kv_heads, self.head_dim, layer, part)
+            ks.append(k)
+            vs.append(v)
+        return np.concatenate(ks), np.concatenate(vs)
+
+    def step_kv(self, seq: int, layer: int = 0):
+        return seq_kv_bits(self.seed, seq, self.new_lens[seq], self.num_kv_heads, self.head_dim, layer, 1)
+
+    def ctx_kv(self, seq: int, layer: int = 0):
+        return seq_kv_bits(self.seed, seq, self.ctx_lens[seq], self.num_kv_heads, self.head_dim, layer, 0)
+
+    def queries(self, layer: int = 0):
+        """bf16 bits [sum(q_lens), Hq, D]: the step's query rows, sequence by sequence."""
+        return query_bits(self.seed, int(sum(self.q_lens)), self.num_q_heads, self.head_dim, layer)
 
     @property
     def num_seqs(self) -> int:
@@ -133,7 +170,8 @@ def prefix_cow(batch: int = 256, prompt: int = 2050, num_blocks: int = 16384) ->
     return Workload("prefix_cow_decode", seed, 32, 8, 128, 16, num_blocks,
                     ctx_lens=[prompt] * batch, new_lens=suffix,
                     free_order=rng.permutation(num_blocks),
-                    forks=[(0, i) for i in range(1, batch)], shared_prefix=prompt)
+                    forks=[(0, i) for i in range(1, batch)], shared_prefix=prompt,
+                    q_lens=[1] * batch)
 
 
 def mixed_step(block_size: int, n_chunks: int = 16, chunk: int = 512, n_decode: int = 240,
@@ -152,6 +190,20 @@ def mixed_step(block_size: int, n_chunks: int = 16, chunk: int = 512, n_decode: 
                     ctx_lens=ctx_p + [n - 1 for n in dec],
                     new_lens=[chunk] * n_chunks + [1] * n_decode,
                     free_order=order)
+
+
+def custom(name: str, seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+           block_size: int, lens, q_lens=None, extra_blocks: int = 3, order_seed=None) -> Workload:
+    """A small ad-hoc case: sequence i holds lens[i] tokens, the last
+    min(q_lens[i], lens[i]) of them written in the step; q_lens[i] query rows
+    (default 1 each, i.e. decode -- a sequence of length 0 still has a query)."""
+    q_lens = list(q_lens) if q_lens is not None else [1] * len(lens)
+    new = [min(q, n) for q, n in zip(q_lens, lens)]
+    ctx = [n - q for n, q in zip(lens, new)]
+    nb = sum(-(-n // block_size) for n in lens) + extra_blocks
+    order = np.random.default_rng(order_seed if order_seed is not None else seed).permutation(nb)
+    return Workload(name, seed, num_q_heads, num_kv_heads, head_dim, block_size, nb,
+                    ctx_lens=ctx, new_lens=new, free_order=order, q_lens=q_lens)
 
 
 def pool_ops(seed: int, n_ops: int = 200, max_seqs: int = 12, max_append: int = 40):

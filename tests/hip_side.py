@@ -1,0 +1,85 @@
+"""Test helpers that run a workload's set-up and step through the HIP
+library (C++ pool + kernels) only.  Nothing here imports the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from paged_kv_cache_327_amd import binding as B
+
+
+def to_device(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 device tensor (bit-exact)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def nan_cache(wl, device="cuda"):
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    return (torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device),
+            torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device))
+
+
+class HipStep:
+    """The workload's set-up and step through the library: the C++ pool,
+    pa_copy_blocks for the step's copy-on-write pairs and
+    pa_reshape_and_cache for every write."""
+
+    def __init__(self, wl, layer=0, bt_width=None, device="cuda", caches=None):
+        S = wl.num_seqs
+        self.wl = wl
+        self.pool = B.pa_pool_create(wl.num_blocks, wl.block_size, wl.free_order)
+        self.kc, self.vc = caches if caches is not None else nan_cache(wl, device)
+        forked = {b for _, b in wl.forks}
+        ctx_slots, ks, vs = [], [], []
+        for s in range(S):
+            if s in forked:
+                continue
+            B.pa_pool_add_seq(self.pool, s)
+            if wl.ctx_lens[s]:
+                slots, pair = B.pa_pool_append(self.pool, s, wl.ctx_lens[s])
+                assert pair is None
+                k, v = wl.ctx_kv(s, layer)
+                ctx_slots.append(slots)
+                ks.append(k)
+                vs.append(v)
+            for a, b in wl.forks:
+                if a == s:
+                    B.pa_pool_fork(self.pool, a, b)
+        if ctx_slots:
+            self.write(np.concatenate(ks), np.concatenate(vs), np.concatenate(ctx_slots))
+        seqs = [s for s in range(S) if wl.new_lens[s]]
+        slots, pairs = B.pa_pool_append_batch(self.pool, seqs, [wl.new_lens[s] for s in seqs])
+        self.step_slots = slots
+        self.pairs = [tuple(p) for p in pairs.tolist() if p[0] >= 0]
+        B.pa_copy_blocks([self.kc, self.vc], self.pairs)
+        if seqs:
+            kv = [wl.step_kv(s, layer) for s in seqs]
+            self.write(np.concatenate([k for k, _ in kv]), np.concatenate([v for _, v in kv]), slots)
+        width = bt_width or max(1, -(-max(wl.seq_lens + [1]) // wl.block_size))
+        self.table, self.seq_lens = B.pa_pool_block_table(self.pool, list(range(S)), width, fill=0)
+        self.table_dev = torch.from_numpy(self.table).to(device)
+        self.seq_lens_dev = torch.from_numpy(self.seq_lens).to(device)
+
+    def write(self, k_bits, v_bits, slots):
+        k = to_device(k_bits, self.kc.device)
+        v = to_device(v_bits, self.kc.device)
+        sl = torch.from_numpy(np.asarray(slots, dtype=np.int64)).to(self.kc.device)
+        B.pa_reshape_and_cache(k, v, self.kc, self.vc, sl)
+
+    def decode(self, q_bits, partition_size=512, rows=None, max_seq_len=None):
+        rows = list(range(self.wl.num_seqs)) if rows is None else list(rows)
+        dev = self.kc.device
+        q = to_device(q_bits, dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        bt = self.table_dev[rows].contiguous()
+        sl = self.seq_lens_dev[rows].contiguous()
+        msl = max_seq_len or max(1, int(self.seq_lens[rows].max()))
+        B.pa_paged_decode(out, q, self.kc, self.vc, bt, sl, msl, self.wl.scale,
+                          partition_size=partition_size, lse=lse)
+        return out, lse

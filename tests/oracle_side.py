@@ -49,3 +49,47 @@ def logical_kv(seed, lens, hkv, d, layer=0):
         ks.append(k)
         vs.append(v)
     return ks, vs
+
+
+class OracleStep:
+    """A workload's set-up and step run through the oracle pool model and
+    numpy caches: context appends, forks, step appends with their
+    copy-on-write copies, then the step's cache writes."""
+
+    def __init__(self, wl, layer=0, bt_width=None):
+        S = wl.num_seqs
+        self.wl = wl
+        self.pool = PoolModel(wl.num_blocks, wl.block_size, wl.free_order)
+        shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+        self.kc = np.full(shape, NAN_BF16, dtype=np.uint16)
+        self.vc = self.kc.copy()
+        forked = {b for _, b in wl.forks}
+        for s in range(S):
+            if s in forked:
+                continue
+            self.pool.add_seq(s)
+            if wl.ctx_lens[s]:
+                slots, pair = self.pool.append(s, wl.ctx_lens[s])
+                assert pair is None
+                k, v = wl.ctx_kv(s, layer)
+                cache_ops.reshape_and_cache(self.kc, self.vc, k, v, np.array(slots))
+            for a, b in wl.forks:
+                if a == s:
+                    self.pool.fork(a, b)
+        self.step_slots, self.pairs = [], []
+        for s in range(S):
+            if wl.new_lens[s]:
+                slots, pair = self.pool.append(s, wl.new_lens[s])
+                self.step_slots.extend(slots)
+                if pair is not None:
+                    self.pairs.append(pair)
+        cache_ops.copy_blocks([self.kc, self.vc], self.pairs, wl.num_blocks)
+        for s in range(S):
+            if wl.new_lens[s]:
+                k, v = wl.step_kv(s, layer)
+                n0 = sum(wl.new_lens[:s])
+                cache_ops.reshape_and_cache(self.kc, self.vc, k, v,
+                                            np.array(self.step_slots[n0:n0 + wl.new_lens[s]]))
+        self.step_slots = np.array(self.step_slots, dtype=np.int64)
+        self.table = table_array(self.pool, range(S), bt_width)
+        self.seq_lens = np.array([self.pool.seq_len(s) for s in range(S)], dtype=np.int32)

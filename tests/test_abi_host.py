@@ -1,0 +1,187 @@
+"""CPU tier for the C-ABI library: it loads, exports everything the header
+declares, its host pool matches the oracle pool model bit for bit, and the
+device calls reject bad arguments on the host (no kernel is launched)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle import sizing
+from oracle.pool_model import NoSpace as ModelNoSpace
+from oracle.pool_model import PoolModel
+from paged_kv_cache_327_amd import binding as B
+from paged_kv_cache_327_amd import workloads
+
+
+def test_library_exports_every_declared_symbol():
+    names = B.header_symbols()
+    assert len(names) >= 20
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B._SIGS) == set(names)
+
+
+def state(pool, seqs):
+    table, lens = B.pa_pool_block_table(pool, list(seqs), 4096, fill=-1) if seqs else (None, None)
+    tables = {s: table[i][table[i] >= 0].tolist() for i, s in enumerate(seqs)} if seqs else {}
+    refs = [B.pa_pool_refcount(pool, b) for b in range(pool.num_blocks)]
+    return tables, (lens.tolist() if seqs else []), refs, B.pa_pool_free_order(pool)
+
+
+def model_state(m, seqs):
+    return ({s: m.block_table(s) for s in seqs}, [m.seq_len(s) for s in seqs], list(m.ref), m.free_order())
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_pool_matches_oracle_model(seed):
+    """25 seeded runs of 200 operations: outcomes, slots, copy pairs, tables,
+    lengths, refcounts and the free-queue order agree after every step."""
+    nb, bs = 24, 4
+    order = np.random.default_rng([seed, 3]).permutation(nb)
+    m = PoolModel(nb, bs, order)
+    p = B.pa_pool_create(nb, bs, order)
+    live = []
+    for op in workloads.pool_ops(seed, 200):
+        if op[0] == "add":
+            m.add_seq(op[1])
+            B.pa_pool_add_seq(p, op[1])
+            live.append(op[1])
+        elif op[0] == "fork":
+            m.fork(op[1], op[2])
+            B.pa_pool_fork(p, op[1], op[2])
+            live.append(op[2])
+        elif op[0] == "free":
+            m.free_seq(op[1])
+            B.pa_pool_free_seq(p, op[1])
+            live.remove(op[1])
+        else:
+            try:
+                want = m.append(op[1], op[2])
+            except ModelNoSpace:
+                want = "nospace"
+            try:
+                slots, pair = B.pa_pool_append(p, op[1], op[2])
+                got = (slots.tolist(), pair)
+            except B.NoSpace:
+                got = "nospace"
+            if want != "nospace":
+                want = (want[0], want[1])
+            assert got == want, (seed, op)
+        B.pa_pool_check(p)
+        assert state(p, live) == model_state(m, live), (seed, op)
+        assert B.pa_pool_num_free(p) == m.num_free()
+
+
+def test_r7_walk_native(golden):
+    e = golden["r7_walk"]["printed"]
+    n = e["held"] + e["free_before"]
+    others = [b for b in range(n) if b != e["popped_block"]]
+    order = others[:e["held"]] + [e["popped_block"]] + others[e["held"]:]
+    p = B.pa_pool_create(n, e["block_size"], order)
+    B.pa_pool_add_seq(p, 3)
+    B.pa_pool_append(p, 3, e["committed"])
+    slots, pair = B.pa_pool_append(p, 3, e["new"])
+    assert pair is None and slots.tolist() == [e["slot"]]
+    table, lens = B.pa_pool_block_table(p, [3], 300)
+    assert lens[0] == e["committed"] + e["new"]
+    assert table[0, e["row_len_after"] - 1] == e["popped_block"]
+    assert B.pa_pool_num_free(p) == e["free_before"] - e["to_allocate"]
+
+
+def test_failed_append_is_all_or_nothing_native():
+    p = B.pa_pool_create(1, 4)
+    B.pa_pool_add_seq(p, 0)
+    B.pa_pool_append(p, 0, 1)
+    B.pa_pool_fork(p, 0, 1)
+    before = state(p, [0, 1])
+    with pytest.raises(B.NoSpace):
+        B.pa_pool_append(p, 1, 1)
+    assert state(p, [0, 1]) == before
+    B.pa_pool_check(p)
+
+
+def test_append_batch_stops_at_first_failure():
+    p = B.pa_pool_create(4, 4)
+    for s in range(3):
+        B.pa_pool_add_seq(p, s)
+    with pytest.raises(B.NoSpace) as ei:
+        B.pa_pool_append_batch(p, [0, 1, 2], [5, 5, 5])
+    assert ei.value.n_done == 2
+    assert B.pa_pool_seq_len(p, 1) == 5 and B.pa_pool_seq_len(p, 2) == 0
+    slots, pairs = B.pa_pool_append_batch(p, [1], [3])
+    assert pairs.tolist() == [[-1, -1]] and len(slots) == 3
+    B.pa_pool_check(p)
+
+
+def test_pool_argument_errors():
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_create(0, 16)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_create(3, 16, [0, 0, 1])
+    p = B.pa_pool_create(4, 4)
+    B.pa_pool_add_seq(p, 7)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_add_seq(p, 7)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_append(p, 8, 1)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_append(p, 7, 0)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_fork(p, 7, 7)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_refcount(p, 4)
+    B.pa_pool_append(p, 7, 9)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_block_table(p, [7], 2)   # 3 blocks do not fit a row of 2
+    assert "bt_stride" in B.lib().pa_last_error().decode()
+
+
+def test_blocks_for_bytes_matches_oracle(golden):
+    bpt = sizing.kv_bytes_per_token(32, 8, 128, 2)
+    for pool_bytes in (0, 1, bpt - 1, bpt, 16 * bpt, int(52.3155 * 2**30), 120 * 10**9, 2**62):
+        for b in (1, 16, 32):
+            assert B.pa_blocks_for_bytes(pool_bytes, bpt, b) == sizing.blocks_for_bytes(pool_bytes, bpt, b)
+    assert B.pa_blocks_for_bytes(int(52.3155 * 2**30), bpt, 16) == golden["pool_blocks_b16"]["printed"]
+    assert B.pa_blocks_for_bytes(10, 0, 16) == -1
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_device_calls_validate_on_host():
+    """Each of these fails argument checks before any HIP call."""
+    L = B.lib()
+    fake = 1 << 20  # aligned non-null address; never dereferenced
+    # head_dim 96 is not supported
+    assert L.pa_reshape_and_cache(_vp(fake), 96, _vp(fake), 96, _vp(fake), _vp(fake), 16 * 96, 4, _vp(fake),
+                                  1, 1, 96, 16, None) == B.PA_ERR_INVALID
+    # block size 12 is not a power of two
+    assert L.pa_reshape_and_cache(_vp(fake), 128, _vp(fake), 128, _vp(fake), _vp(fake), 12 * 128, 4, _vp(fake),
+                                  1, 1, 128, 12, None) == B.PA_ERR_INVALID
+    # zero tokens is a no-op that touches nothing
+    assert L.pa_reshape_and_cache(None, 128, None, 128, _vp(fake), _vp(fake), 16 * 128, 4, None,
+                                  0, 1, 128, 16, None) == B.PA_OK
+    # copy pairs: duplicate destination, and a destination that is a source
+    ptrs = (ctypes.c_void_p * 1)(fake)
+    for pairs in ([0, 1, 2, 1], [0, 1, 1, 2], [0, 9]):
+        arr = np.array(pairs, dtype=np.int32)
+        assert L.pa_copy_blocks(ptrs, 1, 4096, 4096, 4, arr.ctypes.data_as(B.P_i32), len(pairs) // 2,
+                                None) == B.PA_ERR_INVALID
+    # decode: q heads not a multiple of kv heads; partition not a multiple of 64;
+    # table too narrow for max_seq_len; missing workspace
+    args = dict(hq=32, hkv=8, d=128, bs=16, msl=1000, part=512, bt=64, ws=None, wsb=0)
+
+    def dec(**kw):
+        a = dict(args, **kw)
+        return L.pa_paged_decode(_vp(fake), None, _vp(fake), _vp(fake), _vp(fake), a["bs"] * a["hkv"] * a["d"], 100,
+                                 _vp(fake), a["bt"], _vp(fake), 4, a["hq"], a["hkv"], a["d"], a["bs"], a["msl"],
+                                 a["part"], 0.1, a["ws"], a["wsb"], None)
+    assert dec(hq=30) == B.PA_ERR_INVALID
+    assert dec(part=100) == B.PA_ERR_INVALID
+    assert dec(bt=10, part=0) == B.PA_ERR_INVALID
+    assert dec() == B.PA_ERR_INVALID and "workspace" in L.pa_last_error().decode()
+    assert L.pa_paged_decode_workspace_size(4, 32, 128, 1000, 512) > 0
+    assert L.pa_paged_decode_workspace_size(4, 32, 128, 500, 512) == 0

@@ -67,3 +67,14 @@ def test_copy_blocks_rejects_ambiguous_pairs():
     with pytest.raises(ValueError):
         cache_ops.copy_blocks([c], [(0, 4)], 4)
     cache_ops.copy_blocks([c], [], 4)
+
+
+def test_copy_blocks_writes_through_strided_block_views():
+    """Blocks may sit at a stride above their size (interleaved layouts);
+    the copy must land in the underlying array and leave the gaps alone."""
+    base = np.arange(6 * 10, dtype=np.uint16).reshape(6, 10)
+    view = base[:, :8]
+    expect = base.copy()
+    expect[[4, 5], :8] = base[[0, 2], :8]
+    cache_ops.copy_blocks([view], [(0, 4), (2, 5)], 6)
+    assert np.array_equal(base, expect)
