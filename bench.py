@@ -1,0 +1,344 @@
+"""Benchmark of the paged-attention decode step on one MI355X.
+
+One step is the whole path for one batch:
+  1. the host pool appends one token to each of the 64 sequences (new block
+     ids, slots, copy-on-write pairs) and writes the block table;
+  2. table, lengths and slots go host -> device from pinned staging buffers;
+  3. pending copy-on-write block copies run (none arise in this workload);
+  4. the step's new K/V rows are written to their slots;
+  5. paged decode (partition pass, plus the log-sum-exp merge when a
+     sequence spans several partitions) attends over the cache.
+
+Workload: Llama-3-8B-shaped decode (32 query / 8 KV heads, head_dim 128,
+bf16, block_size 16), batch 64, each sequence 512 prompt + U{0..100}
+generated tokens (+1 per step), 8192-block pool per instance with seeded
+random placement, values ~N(0, 1).  Several independent instances are used
+round-robin so that a step never finds its 141 MiB of K/V still in the
+256 MiB last-level cache from the step before.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s; prefill TFLOP/s"
+DECODE_KERNEL = "decode_partition_kernel<128, 4>"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_traffic.txt")
+COPY_CALIBRATION_BYTES = 512 << 20
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for rel in ("paged_kv_cache_327_amd/csrc/kernels/paged_decode.hip",
+                "paged_kv_cache_327_amd/csrc/kernels/common.hpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(seq_lens, num_kv_heads, head_dim):
+    """K and V rows of every attended token (bf16)."""
+    return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * 2 * num_kv_heads * head_dim * 2
+
+
+def decode_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, block_size):
+    """Algorithmic bytes of one decode call: K/V rows, q in and out (bf16)
+    and the block-table entries walked."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    qo = len(seq_lens) * num_q_heads * head_dim * 2 * 2
+    table = int(np.sum(-(-seq_lens // block_size))) * 4
+    return kv_bytes(seq_lens, num_kv_heads, head_dim) + qo + table
+
+
+class Instance:
+    """One pool with its caches, a pinned staging buffer and the step's inputs.
+
+    The per-step metadata (block table, lengths, slots) is packed into one
+    pinned int32 buffer so that a single host->device copy moves it.  The
+    pool writes straight into that buffer."""
+
+    def __init__(self, wl, torch, B, hip_side, workloads, max_seq_len, partition_size, workspace):
+        self.wl = wl
+        self.state = hip_side.HipStep(wl)          # set-up: contexts + one step's token
+        S = wl.num_seqs
+        self.S = S
+        self.width = -(-max_seq_len // wl.block_size)
+        n_i32 = S * self.width + S + 2 * S          # table | lens | slots (int64 as 2 x int32)
+        self.h_stage = torch.zeros(n_i32, dtype=torch.int32).pin_memory()
+        self.d_stage = torch.zeros(n_i32, dtype=torch.int32, device="cuda")
+        hs = self.h_stage.numpy()
+        self.h_table = hs[:S * self.width].reshape(S, self.width)
+        self.h_lens = hs[S * self.width:S * self.width + S]
+        self.h_slots = hs[S * self.width + S:].view(np.int64)
+        ds = self.d_stage
+        self.d_table = ds[:S * self.width].view(S, self.width)
+        self.d_lens = ds[S * self.width:S * self.width + S]
+        self.d_slots = ds[S * self.width + S:].view(torch.int64)
+        rng = np.random.default_rng([wl.seed, 99])
+        self.new_k = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
+        self.new_v = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
+        self.q = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_q_heads, wl.head_dim)))
+        self.out = torch.empty_like(self.q)
+        self.staged = torch.cuda.Event()
+        self.staged.record()
+        self.seq_ids = np.arange(S, dtype=np.int64)
+        self.ones = np.ones(S, dtype=np.int32)
+        self.pairs = np.empty((S, 2), dtype=np.int32)
+        self.done = B.c_i32(0)
+        kc, vc = self.state.kc, self.state.vc
+        L = B.lib()
+        self.lib = L
+        # argument tuples of the C calls (validated once by the binding's
+        # checks in HipStep; the device pointers do not change)
+        self.append_args = (self.state.pool.handle, self.seq_ids.ctypes.data_as(B.P_i64),
+                            self.ones.ctypes.data_as(B.P_i32), S,
+                            self.h_slots.ctypes.data_as(B.P_i64), self.pairs.ctypes.data_as(B.P_i32),
+                            B.ctypes.byref(self.done))
+        self.table_args = (self.state.pool.handle, self.seq_ids.ctypes.data_as(B.P_i64), S,
+                           self.h_table.ctypes.data_as(B.P_i32), self.width, self.h_lens.ctypes.data_as(B.P_i32))
+        bstride = kc.stride(0)
+        self.reshape_args = (self.new_k.data_ptr(), self.new_k.stride(0), self.new_v.data_ptr(),
+                             self.new_v.stride(0), kc.data_ptr(), vc.data_ptr(), bstride, wl.num_blocks,
+                             self.d_slots.data_ptr(), S, wl.num_kv_heads, wl.head_dim, wl.block_size)
+        self.decode_args = (self.out.data_ptr(), None, self.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bstride,
+                            wl.num_blocks, self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(), S,
+                            wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, max_seq_len,
+                            partition_size, wl.scale, workspace.data_ptr(), workspace.numel())
+
+    def decode(self, stream):
+        rc = self.lib.pa_paged_decode(*self.decode_args, stream)
+        if rc != 0:
+            raise RuntimeError(self.lib.pa_last_error().decode())
+
+
+def run_step(inst, B, stream):
+    """One decode step on one instance; returns the attended lengths."""
+    L = inst.lib
+    inst.staged.synchronize()                     # the previous copy out of the staging buffer is done
+    rc = L.pa_pool_append_batch(*inst.append_args)
+    if rc != 0:
+        raise RuntimeError(L.pa_last_error().decode())
+    rc = L.pa_pool_block_table(*inst.table_args)
+    if rc != 0:
+        raise RuntimeError(L.pa_last_error().decode())
+    inst.d_stage.copy_(inst.h_stage, non_blocking=True)
+    inst.staged.record()
+    cow = inst.pairs[inst.pairs[:, 0] >= 0]
+    if len(cow):
+        B.pa_copy_blocks([inst.state.kc, inst.state.vc], cow)
+    rc = L.pa_reshape_and_cache(*inst.reshape_args, stream)
+    if rc != 0:
+        raise RuntimeError(L.pa_last_error().decode())
+    inst.decode(stream)
+    return inst.h_lens.copy()
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle (numpy fp64, single thread) on the same workload: the full
+    64-sequence decode batch, repeated until about budget_s of CPU time."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention
+    from tests.oracle_side import OracleStep
+    o = OracleStep(wl)
+    from paged_kv_cache_327_amd import workloads
+    q = workloads.query_bits(wl.seed, wl.num_seqs, wl.num_q_heads, wl.head_dim)
+    reps = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            attention.paged_decode(q, o.kc, o.vc, o.table, o.seq_lens, wl.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 400:
+                break
+    per = el / reps
+    return {"value": round(kv_bytes(o.seq_lens, wl.num_kv_heads, wl.head_dim) / per / 1e9, 4),
+            "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full {wl.num_seqs}-sequence decode batch of {wl.name} (fp64 numpy, 1 BLAS thread), "
+                      f"{reps} reps in {el:.1f} s; {wl.num_seqs / per:.1f} seqs/s"}
+
+
+def traffic_from_counters(alg_bytes):
+    """HBM bytes per decode launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary (each counter scaled by what it reads for a plain copy of known
+    size); None when the summary is missing or was taken on other decode
+    kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("decode_source_hash") != decode_source_hash():
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
+
+
+def counter_run(kind, reps):
+    """Launch only one kernel kind, for rocprofv3 --pmc passes:
+    'decode' = the decode call of this workload on rotating pools,
+    'copy' = a plain device copy of COPY_CALIBRATION_BYTES (calibration)."""
+    import torch
+
+    from paged_kv_cache_327_amd import binding as B
+    from paged_kv_cache_327_amd import workloads
+    from tests import hip_side
+    if kind == "copy":
+        x = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(f"copy of {COPY_CALIBRATION_BYTES} bytes x {reps}", flush=True)
+        return
+    wls = [workloads.llama_decode(seed_offset=i) for i in range(4)]
+    msl = max(max(w.seq_lens) for w in wls) + 1
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    insts = [Instance(w, torch, B, hip_side, workloads, msl + 1, 0, ws) for w in wls]
+    stream = torch.cuda.current_stream().cuda_stream
+    lens = [run_step(i, B, stream) for i in insts]      # stage tables and lengths (one decode step each)
+    torch.cuda.synchronize()
+    for k in range(reps):
+        insts[k % 4].decode(stream)
+    torch.cuda.synchronize()
+    print(f"decode x {reps}; algorithmic bytes per launch "
+          f"{np.mean([decode_bytes(lens[k % 4], 32, 8, 128, 16) for k in range(reps)]):.0f}", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="decode split-K partition (0 = one partition per sequence)")
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--kernel-reps", type=int, default=48,
+                    help="back-to-back decode launches timed with HIP events for the roofline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-run", choices=["decode", "copy"],
+                    help="only launch one kernel kind (for rocprofv3 --pmc passes) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; there is no multi-GPU path. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.counter_run:
+        counter_run(args.counter_run, 12)
+        return
+
+    import torch
+
+    from paged_kv_cache_327_amd import binding as B
+    from paged_kv_cache_327_amd import workloads
+    from tests import hip_side
+
+    B.lib()  # fail loudly if the library is missing
+    wls = [workloads.llama_decode(seed_offset=i) for i in range(args.instances)]
+    max_seq_len = max(max(w.seq_lens) for w in wls) + args.warmup + args.steps + 1
+    wl = wls[0]
+    S = wl.num_seqs
+    ws_bytes = B.pa_paged_decode_workspace_size(S, wl.num_q_heads, wl.head_dim, max_seq_len,
+                                                args.partition_size)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    print(f"[bench] set-up: {args.instances} instances of {wl.name}", file=sys.stderr, flush=True)
+    insts = [Instance(w, torch, B, hip_side, workloads, max_seq_len, args.partition_size, workspace)
+             for w in wls]
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_step(insts[i % len(insts)], B, stream)
+    torch.cuda.synchronize()
+    print("[bench] warm-up done", file=sys.stderr, flush=True)
+
+    # whole-step throughput
+    step_lens = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step_lens.append(run_step(insts[k % len(insts)], B, stream))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print("[bench] timed steps done", file=sys.stderr, flush=True)
+
+    # dominant kernel: back-to-back decode launches on the same stream,
+    # rotating over the pools, bracketed by HIP events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    insts[0].decode(stream)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(args.kernel_reps):
+        insts[k % len(insts)].decode(stream)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_s = e0.elapsed_time(e1) / 1e3 / args.kernel_reps
+    cur_lens = [np.array(i.h_lens) for i in insts]
+    alg_per_launch = np.mean([decode_bytes(cur_lens[k % len(insts)], wl.num_q_heads, wl.num_kv_heads,
+                                           wl.head_dim, wl.block_size) for k in range(args.kernel_reps)])
+    achieved = alg_per_launch / dec_s / 1e9
+
+    ms_per_step = elapsed / args.steps * 1e3
+    kv_per_step = np.mean([kv_bytes(l, wl.num_kv_heads, wl.head_dim) for l in step_lens])
+    value = kv_per_step / (ms_per_step / 1e3) / 1e9
+    nparts = -(-max_seq_len // args.partition_size) if args.partition_size else 1
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": S, "num_q_heads": wl.num_q_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "num_blocks": wl.num_blocks, "context": "512 + U{0..100} (+1 per step)",
+                   "partition_size": args.partition_size, "pool_instances": args.instances},
+        "seqs_per_s": round(S / (ms_per_step / 1e3), 1),
+        "step_hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "decode_kernel_us": round(dec_s * 1e6, 2),
+        "decode_seqs_per_s": round(S / dec_s, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": DECODE_KERNEL + (" + decode_merge_kernel<128>" if nparts > 1 else ""),
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_counters(alg_per_launch),
+            "algorithmic_bytes_per_launch": int(alg_per_launch),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

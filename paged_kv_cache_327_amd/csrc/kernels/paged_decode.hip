@@ -20,8 +20,8 @@
 //    K/V registers (the GQA sharing): q.k with v_dot2_f32_bf16, summed over the
 //    8 lanes with DPP; softmax weights are rounded to bf16 and multiplied into
 //    V with v_dot2_f32_bf16 on token pairs, accumulating in fp32.
-//  * A wave handles 16-token tiles (2 tokens per group) and prefetches the
-//    next tile's K/V before computing the current one.
+//  * A wave handles 16-token tiles (2 tokens per group) and keeps the next
+//    two tiles' K/V loads in flight while it computes the current one.
 //  * Online softmax in the log2 domain; the running maximum is only raised
 //    when a logit exceeds it by more than 8 (weights stay <= 2^8), which keeps
 //    the result exact and makes rescales rare.
@@ -56,7 +56,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   __shared__ float s_acc[kWaves][G][D];
 
   const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (SGPR) so that the tile loop below branches on scalars
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 3, li = lane & 7;
 
   int len = a.seq_lens[s];
@@ -106,41 +108,36 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // Tokens past c1 are redirected to token c0 (always valid) so every load
-    // stays inside the cache; their logits are masked below.
+    // Tokens past c1 are redirected to token c0 (always valid), so every
+    // load stays inside the cache and can be issued unconditionally: with no
+    // branch around the prefetches the compiler's wait counts stay exact and
+    // the next tiles' loads remain in flight while this one is computed.
+    // All K loads are issued before the V loads so q.k can start first.
     auto load = [&](int t0, KV<D>& r) {
+      int64_t off[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         int t = t0 + grp + 8 * u;
         t = t < c1 ? t : c0;
         const int64_t blk = s_bt[(t >> lgB) - j0];
-        const int64_t off = blk * bstride + (int64_t)(t & Bmask) * row_elems;
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-          r.k[u][k] = *reinterpret_cast<const uint4*>(kbase + off + 64 * k);
-          r.v[u][k] = *reinterpret_cast<const uint4*>(vbase + off + 64 * k);
-        }
+        off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems;
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kbase + off[u] + 64 * k);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vbase + off[u] + 64 * k);
     };
 
     auto compute = [&](int t0, const KV<D>& r) {
       const bool valid0 = t0 + grp < c1;
       const bool valid1 = t0 + grp + 8 < c1;
-      // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
-      uint32_t vp[PPL][8];
+      float x[G][2];
 #pragma unroll
-      for (int k = 0; k < PPL; ++k) {
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&r.v[0][k]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&r.v[1][k]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vp[k][2 * i] = __builtin_amdgcn_perm(v1[i], v0[i], 0x05040100u);
-          vp[k][2 * i + 1] = __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float x[2];
+      for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           float d = 0.f;
@@ -151,11 +148,14 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) d = dot2_bf16(qq[i], kk[i], d);
           }
-          x[u] = sum_lanes8(d) * scale;
+          x[h][u] = sum_lanes8(d) * scale;
         }
-        x[0] = valid0 ? x[0] : kNegInf;
-        x[1] = valid1 ? x[1] : kNegInf;
-        const float mx = fmaxf(x[0], x[1]);
+      uint32_t pp[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float x0 = valid0 ? x[h][0] : kNegInf;
+        const float x1 = valid1 ? x[h][1] : kNegInf;
+        const float mx = fmaxf(x0, x1);
         if (mx > m[h] + kRescaleSlack) {
           const float alpha = fast_exp2(m[h] - mx);
           l[h] *= alpha;
@@ -165,30 +165,56 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
             for (int i = 0; i < 8; ++i) acc[h][k][i] *= alpha;
           m[h] = mx;
         }
-        const float p0 = valid0 ? fast_exp2(x[0] - m[h]) : 0.f;
-        const float p1 = valid1 ? fast_exp2(x[1] - m[h]) : 0.f;
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        l[h] += bf16_lo(pp) + bf16_hi(pp);
+        const float p0 = valid0 ? fast_exp2(x0 - m[h]) : 0.f;
+        const float p1 = valid1 ? fast_exp2(x1 - m[h]) : 0.f;
+        pp[h] = pack_bf16x2(p0, p1);
+        l[h] += bf16_lo(pp[h]) + bf16_hi(pp[h]);
+      }
+      // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
 #pragma unroll
-        for (int k = 0; k < PPL; ++k)
+      for (int k = 0; k < PPL; ++k) {
+        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&r.v[0][k]);
+        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&r.v[1][k]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][k][i] = dot2_bf16(pp, vp[k][i], acc[h][k][i]);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = __builtin_amdgcn_perm(v1[i], v0[i], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][k][2 * i] = dot2_bf16(pp[h], lo, acc[h][k][2 * i]);
+            acc[h][k][2 * i + 1] = dot2_bf16(pp[h], hi, acc[h][k][2 * i + 1]);
+          }
+        }
       }
     };
 
-    KV<D> ra, rb;
+    // Three register buffers: while tile t is computed, tiles t + 64 and
+    // t + 128 are in flight.  The loop runs whole triples and has a single,
+    // bottom-tested exit (an exit in the middle gives the compiler a path
+    // back into the loop with loads pending, and it then drains every load
+    // at the top); the last 0-2 tiles are computed after it from buffers
+    // already loaded.  All branches here are wave-uniform.
+    constexpr int kStep = kWaves * kTile;
     int t = c0 + wave * kTile;
-    if (t < c1) load(t, ra);
-    while (t < c1) {
-      int tn = t + kWaves * kTile;
-      if (tn < c1) load(tn, rb);
-      compute(t, ra);
-      t = tn;
-      if (t >= c1) break;
-      tn = t + kWaves * kTile;
-      if (tn < c1) load(tn, ra);
-      compute(t, rb);
-      t = tn;
+    const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
+    if (n_tiles > 0) {
+      KV<D> r0, r1, r2;
+      load(t, r0);
+      load(t + kStep, r1);
+      int i = 0;
+      for (; i + 3 <= n_tiles; i += 3) {
+        load(t + 2 * kStep, r2);
+        compute(t, r0);
+        t += kStep;
+        load(t + 2 * kStep, r0);
+        compute(t, r1);
+        t += kStep;
+        load(t + 2 * kStep, r1);
+        compute(t, r2);
+        t += kStep;
+      }
+      if (n_tiles - i >= 1) compute(t, r0);
+      if (n_tiles - i >= 2) compute(t + kStep, r1);
     }
   }
 
