@@ -1,9 +1,300 @@
-// Chunked-prefill attention over a paged KV cache (MFMA bf16) -- not built yet.
+// Chunked-prefill attention over a paged KV cache on gfx950 MFMA.
+//
+// What is computed ("PagedAttention: fragmentation, blocks, block tables",
+// attention-metadata section): request i's queries are rows
+// query_start_loc[i] .. query_start_loc[i+1]-1 and are the last q_i of its
+// seq_lens[i] tokens; query j (absolute position c_i + j) attends to the keys
+// 0 .. c_i + j (causal) gathered through row i of the block table.  The
+// kernel design below is ours; the pages give none.
+//
+// Work-group = 4 waves = (request i, a group of HW query heads sharing one KV
+// head, a tile of 32 * (4 / HW) queries).  Each wave owns one head and 32
+// queries.  Key tiles of 64 keys are gathered through the block table into
+// LDS once per work-group and used by all of its waves (the GQA sharing):
+//   * K is stored row-major [key][d]; V is stored transposed [d][key] so that
+//     both MFMA operands read contiguous LDS.  Keys past the sequence end are
+//     written as zeros (their loads are redirected to key 0), so NaN bytes in
+//     unwritten slots can never reach a product.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
+//     so the softmax max and sum are in-lane (plus one exchange between the
+//     two lane halves).
+//   * P^T comes straight out of the S^T registers (rounded to bf16); the key
+//     order inside each 16-key MFMA step is permuted identically on P^T and on
+//     V^T, which leaves the sum unchanged and needs no data movement.
+//   * O^T += V^T P^T accumulates in fp32; the online softmax raises its
+//     running maximum only when a score exceeds it by more than 8 (log2
+//     units), which keeps the result exact and rescales rare.
+//   * The next key tile's K/V loads are in flight while the current tile is
+//     computed (register staging, double-buffered LDS, one barrier per tile);
+//     block-table entries are fetched one further tile ahead.
 #include "../internal.hpp"
 #include "common.hpp"
 
 namespace pa {
+namespace {
 
-int launch_paged_prefill(const PrefillArgs&, void*) { return (int)hipErrorNotSupported; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kKeys = 64;        // keys per tile
+constexpr int kQ = 32;           // queries per wave
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kSlack = 8.0f;
+
+template <int D>
+struct Smem {
+  static constexpr int kRow = D + 8;           // K row stride (elements), padded
+  static constexpr int kVtRow = kKeys + 4;     // V^T row stride (elements), padded
+  uint16_t k[2][kKeys * kRow];
+  uint16_t vt[2][D * kVtRow];
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int D, int HW>
+__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+  constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
+  constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;                 // 32-row blocks of head_dim in O^T
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int UPT = 32 * CPR / 256;        // (key pair, chunk) units per thread
+  __shared__ Smem<D> sm;
+
+  const int i = blockIdx.z;                  // request
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, col = lane & 31;
+
+  const int q_begin = a.query_start_loc[i];
+  const int q_len = a.query_start_loc[i + 1] - q_begin;
+  int kv_len = a.seq_lens[i];
+  kv_len = kv_len > a.max_seq_len ? a.max_seq_len : kv_len;
+  const int ctx = kv_len - q_len;            // absolute position of query 0
+  const int span = kQ * QS;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * span;   // heaviest tiles first
+  if (q_len <= 0 || q0 >= q_len || ctx < 0) return;
+
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h = blockIdx.y * HW + wave % HW;             // this wave's query head
+  const int g = (blockIdx.y * HW) / G;                   // shared KV head
+  const int qw = q0 + (wave / HW) * kQ;                  // this wave's first query
+  const int lgB = a.log2_block_size;
+  const int Bmask = (1 << lgB) - 1;
+  const int64_t row_elems = (int64_t)a.num_kv_heads * D;
+  const int64_t bstride = a.cache_block_stride;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.key_cache) + (int64_t)g * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.value_cache) + (int64_t)g * D;
+  const int32_t* bt_row = a.block_tables + (int64_t)i * a.bt_stride;
+  const float scale = a.scale * kLog2e;
+
+  // keys this work-group needs: causal -> up to the position of its last query
+  const int q_last = (q0 + span < q_len ? q0 + span : q_len) - 1;
+  const int kv_end = a.causal ? ctx + q_last + 1 : kv_len;
+  const int n_tiles = (kv_end + kKeys - 1) / kKeys;
+
+  // Q^T operand: lane holds query qw + col, d = 16 ks + 8 hf .. +8.
+  uint4 qreg[DS];
+  {
+    int qi = qw + col;
+    qi = qi < q_len ? qi : q_len - 1;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 16 * ks + 8 * hf);
+  }
+  const int qpos = ctx + qw + col;           // absolute position of this lane's query
+
+  // Tile loading: unit u = (key pair kp, 16-byte chunk c).
+  int kp_[UPT], ch_[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int unit = tid + 256 * u;
+    kp_[u] = unit / CPR;
+    ch_[u] = unit % CPR;
+  }
+  int blk_next[UPT][2];                       // table entries, one tile ahead of the loads
+  uint4 kr[UPT][2], vr[UPT][2];               // staged K/V of the tile being loaded
+
+  auto fetch_table = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        int p = tile * kKeys + 2 * kp_[u] + e;
+        p = p < kv_end ? p : 0;
+        int b = bt_row[p >> lgB];
+        blk_next[u][e] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      }
+  };
+  auto issue_loads = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        int p = tile * kKeys + 2 * kp_[u] + e;
+        p = p < kv_end ? p : 0;
+        const int64_t off = (int64_t)blk_next[u][e] * bstride + (int64_t)(p & Bmask) * row_elems + 8 * ch_[u];
+        kr[u][e] = *reinterpret_cast<const uint4*>(kc + off);
+        vr[u][e] = *reinterpret_cast<const uint4*>(vc + off);
+      }
+  };
+  auto store_tile = [&](int tile, int buf) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      uint4 k0 = kr[u][0], k1 = kr[u][1], v0 = vr[u][0], v1 = vr[u][1];
+      const int key = 2 * kp_[u];
+      if (tile * kKeys + key >= kv_end) { k0 = make_uint4(0, 0, 0, 0); v0 = k0; }
+      if (tile * kKeys + key + 1 >= kv_end) { k1 = make_uint4(0, 0, 0, 0); v1 = k1; }
+      *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kRow + 8 * ch_[u]]) = k0;
+      *reinterpret_cast<uint4*>(&sm.k[buf][(key + 1) * Smem<D>::kRow + 8 * ch_[u]]) = k1;
+      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&v0);
+      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v1);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = 8 * ch_[u] + 2 * w;
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d * Smem<D>::kVtRow + key]) =
+            __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(d + 1) * Smem<D>::kVtRow + key]) =
+            __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+      }
+    }
+  };
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
+  float m = kNegInf, l = 0.f;
+
+  // Staging is unconditional: tiles past the end read key 0 (always valid)
+  // and store zeros, so no branch separates a load from its use.
+  fetch_table(0);
+  issue_loads(0);
+  fetch_table(1);
+  store_tile(0, 0);
+  issue_loads(1);
+  fetch_table(2);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const uint16_t* K = sm.k[buf];
+    const uint16_t* Vt = sm.vt[buf];
+    // S^T[key][query] for the two 32-key halves of the tile
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&K[(kb * 32 + col) * Smem<D>::kRow + 16 * ks + 8 * hf]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[ks]), s[kb], 0, 0, 0);
+      }
+    }
+    // scale, mask, tile max (keys of this lane: 32 kb + 8 (r / 4) + 4 hf + r % 4)
+    const int n0 = t * kKeys;
+    const bool need_mask = n0 + kKeys - 1 > (a.causal ? ctx + qw : kv_len - 1);
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[kb][r] * scale;
+        if (need_mask) {
+          const int key = n0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool ok = a.causal ? key <= qpos : key < kv_len;
+          x = ok ? x : kNegInf;
+        }
+        s[kb][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (mt > m + kSlack) {
+      const float alpha = fast_exp2(m - mt);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+      m = mt;
+    }
+    // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s.
+    uint32_t pb[2][2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(s[kb][8 * ks + 2 * w] - m);
+          const float e1 = fast_exp2(s[kb][8 * ks + 2 * w + 1] - m);
+          const uint32_t pk = pack_bf16x2(e0, e1);
+          pb[kb][ks][w] = pk;
+          l += bf16_lo(pk) + bf16_hi(pk);
+        }
+    // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
+    // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 pv = make_uint4(pb[kb][ks][0], pb[kb][ks][1], pb[kb][ks][2], pb[kb][ks][3]);
+        const int key0 = 32 * kb + 16 * ks + 4 * hf;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const uint16_t* vrow = &Vt[(32 * b + col) * Smem<D>::kVtRow + key0];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pv), o[b], 0, 0, 0);
+        }
+      }
+    // stage the next tile into the other buffer and start the one after
+    store_tile(t + 1, buf ^ 1);
+    issue_loads(t + 2);
+    fetch_table(t + 3);
+    __syncthreads();
+  }
+
+  // normalise and write: lane owns query qw + col, d = 32 b + 8 (r / 4) + 4 hf + r % 4
+  l += __shfl_xor(l, 32);
+  const int qi = qw + col;
+  if (qi < q_len) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const uint32_t lo = pack_bf16x2(o[b][4 * rr] * inv, o[b][4 * rr + 1] * inv);
+        const uint32_t hi = pack_bf16x2(o[b][4 * rr + 2] * inv, o[b][4 * rr + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * b + 8 * rr + 4 * hf) = make_uint2(lo, hi);
+      }
+  }
+}
+
+template <int D, int HW>
+int launch_hw(const PrefillArgs& a, hipStream_t st) {
+  const int span = kQ * (4 / HW);
+  const unsigned qtiles = (unsigned)((a.max_query_len + span - 1) / span);
+  hipLaunchKernelGGL((prefill_kernel<D, HW>), dim3(qtiles, a.num_q_heads / HW, a.num_seqs), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int launch_d(const PrefillArgs& a, hipStream_t st) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (G % 4 == 0) return launch_hw<D, 4>(a, st);
+  if (G % 2 == 0) return launch_hw<D, 2>(a, st);
+  return launch_hw<D, 1>(a, st);
+}
+
+}  // namespace
+
+int launch_paged_prefill(const PrefillArgs& a, void* stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  return a.head_dim == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
 
 }  // namespace pa

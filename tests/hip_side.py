@@ -83,3 +83,19 @@ class HipStep:
         B.pa_paged_decode(out, q, self.kc, self.vc, bt, sl, msl, self.wl.scale,
                           partition_size=partition_size, lse=lse)
         return out, lse
+
+    def prefill(self, q_bits, seqs, causal=True, max_seq_len=None):
+        """Prefill attention for sequences ``seqs`` (in order); q_bits holds
+        their query rows back to back (wl.q_lens rows each)."""
+        dev = self.kc.device
+        seqs = list(seqs)
+        q_lens = [self.wl.q_lens[s] for s in seqs]
+        qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+        q = to_device(q_bits, dev)
+        out = torch.empty_like(q)
+        bt = self.table_dev[seqs].contiguous()
+        sl = self.seq_lens_dev[seqs].contiguous()
+        msl = max_seq_len or max(1, int(self.seq_lens[seqs].max()))
+        B.pa_paged_prefill(out, q, self.kc, self.vc, bt, torch.from_numpy(qsl).to(dev), sl,
+                           max(q_lens), msl, self.wl.scale, causal=causal)
+        return out
