@@ -51,7 +51,7 @@ struct Smem {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int D, int HW>
+template <int D, int HW, bool CAUSAL>
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
@@ -85,11 +85,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const uint16_t* kc = static_cast<const uint16_t*>(a.key_cache) + (int64_t)g * D;
   const uint16_t* vc = static_cast<const uint16_t*>(a.value_cache) + (int64_t)g * D;
   const int32_t* bt_row = a.block_tables + (int64_t)i * a.bt_stride;
-  const float scale = a.scale * kLog2e;
+  // A negative scale is applied as |scale| on -q (flipping q's sign bits is
+  // exact), so the running maximum can always be taken on raw scores.
+  const float scale = fabsf(a.scale) * kLog2e;
+  const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
 
   // keys this work-group needs: causal -> up to the position of its last query
   const int q_last = (q0 + span < q_len ? q0 + span : q_len) - 1;
-  const int kv_end = a.causal ? ctx + q_last + 1 : kv_len;
+  const int kv_end = CAUSAL ? ctx + q_last + 1 : kv_len;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
 
   // Q^T operand: lane holds query qw + col, d = 16 ks + 8 hf .. +8.
@@ -99,7 +102,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     qi = qi < q_len ? qi : q_len - 1;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < DS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 16 * ks + 8 * hf);
+    for (int ks = 0; ks < DS; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * ks + 8 * hf);
+      qreg[ks] = make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
+    }
   }
   const int qpos = ctx + qw + col;           // absolute position of this lane's query
 
@@ -192,24 +198,29 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[ks]), s[kb], 0, 0, 0);
       }
     }
-    // scale, mask, tile max (keys of this lane: 32 kb + 8 (r / 4) + 4 hf + r % 4)
+    // mask and tile max on raw scores.  Register r of half kb holds key
+    // n0 + 32 kb + 8 (r / 4) + 4 hf + r % 4; a key is visible iff its offset
+    // 32 kb + 8 (r / 4) + r % 4 is at most `lim` (one compare per score, on
+    // tiles that reach past this wave's first query only).
     const int n0 = t * kKeys;
-    const bool need_mask = n0 + kKeys - 1 > (a.causal ? ctx + qw : kv_len - 1);
+    const int lim = (CAUSAL ? qpos : kv_len - 1) - n0 - 4 * hf;
+    const bool need_mask = n0 + kKeys - 1 > (CAUSAL ? ctx + qw : kv_len - 1);
     float mt = kNegInf;
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * scale;
-        if (need_mask) {
-          const int key = n0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool ok = a.causal ? key <= qpos : key < kv_len;
-          x = ok ? x : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[kb][r] : kNegInf;
+          mt = fmaxf(mt, s[kb][r]);
         }
-        s[kb][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale;
     if (mt > m + kSlack) {
       const float alpha = fast_exp2(m - mt);
       l *= alpha;
@@ -219,7 +230,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
       m = mt;
     }
-    // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s.
+    // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s;
+    // weights are exp2(score * scale - m), and their bf16 values are summed.
     uint32_t pb[2][2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -227,11 +239,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(s[kb][8 * ks + 2 * w] - m);
-          const float e1 = fast_exp2(s[kb][8 * ks + 2 * w + 1] - m);
+          const float e0 = fast_exp2(fmaf(s[kb][8 * ks + 2 * w], scale, -m));
+          const float e1 = fast_exp2(fmaf(s[kb][8 * ks + 2 * w + 1], scale, -m));
           const uint32_t pk = pack_bf16x2(e0, e1);
           pb[kb][ks][w] = pk;
-          l += bf16_lo(pk) + bf16_hi(pk);
+          l = dot2_bf16(pk, 0x3F803F80u, l);
         }
     // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
     // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.
@@ -277,8 +289,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 template <int D, int HW>
 int launch_hw(const PrefillArgs& a, hipStream_t st) {
   const int span = kQ * (4 / HW);
-  const unsigned qtiles = (unsigned)((a.max_query_len + span - 1) / span);
-  hipLaunchKernelGGL((prefill_kernel<D, HW>), dim3(qtiles, a.num_q_heads / HW, a.num_seqs), dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.max_query_len + span - 1) / span), a.num_q_heads / HW, a.num_seqs);
+  if (a.causal)
+    hipLaunchKernelGGL((prefill_kernel<D, HW, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, HW, false>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
