@@ -11,10 +11,10 @@
 // head, a tile of 32 * (4 / HW) queries).  Each wave owns one head and 32
 // queries.  Key tiles of 64 keys are gathered through the block table into
 // LDS once per work-group and used by all of its waves (the GQA sharing):
-//   * K is stored row-major [key][d]; V is stored transposed [d][key] so that
-//     both MFMA operands read contiguous LDS.  Keys past the sequence end are
-//     written as zeros (their loads are redirected to key 0), so NaN bytes in
-//     unwritten slots can never reach a product.
+//   * K and V are stored row-major [key][d]; the V^T operand is read with
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16).  Keys past the
+//     sequence end are written as zeros (their loads are redirected to key
+//     0), so NaN bytes in unwritten slots can never reach a product.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
 //     so the softmax max and sum are in-lane (plus one exchange between the
 //     two lane halves).
@@ -41,15 +41,28 @@ constexpr int kQ = 32;           // queries per wave
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kSlack = 8.0f;
 
+// Both tiles are row-major [key][d].  K rows are padded to D + 8 elements
+// (the 32 rows read by one S^T operand fall on distinct banks); V rows to
+// D + 16 (the four rows of one transposing read fall on disjoint banks).
 template <int D>
 struct Smem {
-  static constexpr int kRow = D + 8;           // K row stride (elements), padded
-  static constexpr int kVtRow = kKeys + 4;     // V^T row stride (elements), padded
+  static constexpr int kRow = D + 8;
+  static constexpr int kVRow = D + 16;
   uint16_t k[2][kKeys * kRow];
-  uint16_t vt[2][D * kVtRow];
+  uint16_t v[2][kKeys * kVRow];
 };
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a + b receives
+// element b of the 8-byte rows addressed by lanes a, a + 4, a + 8, a + 12.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <int D, int HW, bool CAUSAL>
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
@@ -152,16 +165,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       if (tile * kKeys + key + 1 >= kv_end) { k1 = make_uint4(0, 0, 0, 0); v1 = k1; }
       *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kRow + 8 * ch_[u]]) = k0;
       *reinterpret_cast<uint4*>(&sm.k[buf][(key + 1) * Smem<D>::kRow + 8 * ch_[u]]) = k1;
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&v0);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&v1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = 8 * ch_[u] + 2 * w;
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][d * Smem<D>::kVtRow + key]) =
-            __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][(d + 1) * Smem<D>::kVtRow + key]) =
-            __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
-      }
+      *reinterpret_cast<uint4*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * ch_[u]]) = v0;
+      *reinterpret_cast<uint4*>(&sm.v[buf][(key + 1) * Smem<D>::kVRow + 8 * ch_[u]]) = v1;
     }
   };
 
@@ -185,17 +190,31 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const uint16_t* K = sm.k[buf];
-    const uint16_t* Vt = sm.vt[buf];
-    // S^T[key][query] for the two 32-key halves of the tile
+    const uint16_t* V = sm.v[buf];
+    // S^T[key][query] for the two 32-key halves of the tile.  The two halves
+    // are independent accumulations: their MFMAs alternate, and the next
+    // k-step's K operands are read from LDS before this step's MFMAs issue.
     f32x16_t s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    {
+      const uint16_t* krow0 = &K[col * Smem<D>::kRow + 8 * hf];
+      const uint16_t* krow1 = &K[(32 + col) * Smem<D>::kRow + 8 * hf];
+      uint4 ka0 = *reinterpret_cast<const uint4*>(krow0);
+      uint4 ka1 = *reinterpret_cast<const uint4*>(krow1);
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&K[(kb * 32 + col) * Smem<D>::kRow + 16 * ks + 8 * hf]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), as_bf16x8(qreg[ks]), s[kb], 0, 0, 0);
+        uint4 kn0 = ka0, kn1 = ka1;
+        if (ks + 1 < DS) {
+          kn0 = *reinterpret_cast<const uint4*>(krow0 + 16 * (ks + 1));
+          kn1 = *reinterpret_cast<const uint4*>(krow1 + 16 * (ks + 1));
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka0), as_bf16x8(qreg[ks]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka1), as_bf16x8(qreg[ks]), s[1], 0, 0, 0);
+        ka0 = kn0;
+        ka1 = kn1;
       }
     }
     // mask and tile max on raw scores.  Register r of half kb holds key
@@ -246,22 +265,35 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
           l = dot2_bf16(pk, 0x3F803F80u, l);
         }
     // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
-    // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.
+    // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.  The V^T
+    // operand (lane: d = 32 b + col) comes from row-major V with transposing
+    // reads: in each 16-lane group (d = dg .. dg + 15), lane a + 4 c points at
+    // V[key0 + c][dg + 4 a], which hands lane j the 4 keys of d = dg + j.
+    const int tr_a = lane & 3, tr_c = (lane >> 2) & 3, tr_g = (lane >> 4) & 1;
+    const uint16_t* vbase = &V[tr_c * Smem<D>::kVRow + 16 * tr_g + 4 * tr_a + 4 * hf * Smem<D>::kVRow];
+    auto read_vt = [&](int step, int b) {
+      const int kb = step >> 1, ks = step & 1;
+      const uint16_t* src = vbase + (32 * kb + 16 * ks) * Smem<D>::kVRow + 32 * b;
+      const uint2 lo = lds_read_tr16(src);
+      const uint2 hi = lds_read_tr16(src + 8 * Smem<D>::kVRow);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+    uint4 va[DB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int b = 0; b < DB; ++b) va[b] = read_vt(0, b);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 pv = make_uint4(pb[kb][ks][0], pb[kb][ks][1], pb[kb][ks][2], pb[kb][ks][3]);
-        const int key0 = 32 * kb + 16 * ks + 4 * hf;
+    for (int step = 0; step < 4; ++step) {
+      const int kb = step >> 1, ks = step & 1;
+      const uint4 pv = make_uint4(pb[kb][ks][0], pb[kb][ks][1], pb[kb][ks][2], pb[kb][ks][3]);
+      uint4 vn[DB];
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const uint16_t* vrow = &Vt[(32 * b + col) * Smem<D>::kVtRow + key0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pv), o[b], 0, 0, 0);
-        }
-      }
+      for (int b = 0; b < DB; ++b) vn[b] = step + 1 < 4 ? read_vt(step + 1, b) : va[b];
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[b]), as_bf16x8(pv), o[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) va[b] = vn[b];
+    }
     // stage the next tile into the other buffer and start the one after
     store_tile(t + 1, buf ^ 1);
     issue_loads(t + 2);
