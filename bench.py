@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s; prefill TFLOP/s"
 DECODE_KERNEL = "decode_partition_kernel<128, 4>"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_traffic.txt")
@@ -191,6 +192,45 @@ def traffic_from_counters(alg_bytes):
     return int(float(vals["hbm_bytes_per_launch"]))
 
 
+def prefill_flops(q_lens, seq_lens, num_q_heads, head_dim):
+    """Algorithmic flops of causal chunked prefill: QK^T and PV over the
+    visible keys only, 4 * D * Hq * (q * c + q (q + 1) / 2) per chunk."""
+    total = 0
+    for q, n in zip(q_lens, seq_lens):
+        c = n - q
+        total += 4 * head_dim * num_q_heads * (q * c + q * (q + 1) // 2)
+    return total
+
+
+def measure_prefill(torch, B, hip_side, workloads, block_size=16, reps=10):
+    """The mixed step's prefill: 16 chunks of 512 queries over U{0..8192}
+    context tokens, Llama-3-8B head shapes, one launch timed back to back."""
+    wl = workloads.mixed_step(block_size, n_decode=0)
+    h = hip_side.HipStep(wl)
+    q = hip_side.to_device(workloads.query_bits(wl.seed, sum(wl.q_lens), wl.num_q_heads, wl.head_dim))
+    out = torch.empty_like(q)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum(wl.q_lens)]), dtype=torch.int32, device="cuda")
+    msl = int(max(wl.seq_lens))
+
+    def launch():
+        B.pa_paged_prefill(out, q, h.kc, h.vc, h.table_dev, qsl, h.seq_lens_dev, max(wl.q_lens), msl, wl.scale)
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    flops = prefill_flops(wl.q_lens, wl.seq_lens, wl.num_q_heads, wl.head_dim)
+    return {"workload": "16 prefill chunks of 512 queries over U{0..8192} context tokens",
+            "block_size": block_size, "kernel": "prefill_kernel<128, 4, true>",
+            "us": round(sec * 1e6, 1), "gflop": round(flops / 1e9, 2),
+            "tflops": round(flops / sec / 1e12, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def counter_run(kind, reps):
     """Launch only one kernel kind, for rocprofv3 --pmc passes:
     'decode' = the decode call of this workload on rotating pools,
@@ -234,6 +274,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=48,
                     help="back-to-back decode launches timed with HIP events for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--counter-run", choices=["decode", "copy"],
                     help="only launch one kernel kind (for rocprofv3 --pmc passes) and exit")
     args = ap.parse_args()
@@ -334,6 +375,11 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_prefill:
+        print("[bench] prefill", file=sys.stderr, flush=True)
+        del insts
+        torch.cuda.empty_cache()
+        line["prefill"] = measure_prefill(torch, B, hip_side, workloads)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)
