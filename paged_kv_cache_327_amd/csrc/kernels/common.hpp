@@ -36,6 +36,24 @@ __device__ __forceinline__ float sum_lanes8(float x) {
   return x;
 }
 
+// Cross-lane moves within rows of 16 lanes (DPP): quad permutes, the
+// half-row mirror (lane i <-> 7 - i) and the row rotation by 8.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppBcast0 = 0x00;      // quad_perm [0, 0, 0, 0]
+constexpr int kDppBcast2 = 0xAA;      // quad_perm [2, 2, 2, 2]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -10,24 +10,32 @@
 // below is ours.
 //
 // Partition pass: one work-group (4 waves) per (partition, KV head g, seq s).
-//  * The partition's block-table entries are staged once in LDS (clamped into
-//    [0, num_blocks)), so a token's physical row costs one LDS read.
 //  * Lanes form groups of 8.  A group owns one token at a time; its 8 lanes
 //    split head_dim into 16-byte pieces (lane i holds d = 8i..8i+7 and, for
 //    D = 128, d = 64+8i..64+8i+7), so every K/V row load is a coalesced
-//    16-byte-per-lane access of the token's contiguous row.
-//  * The G = Hq/Hkv query heads of KV head g are all computed from the same
-//    K/V registers (the GQA sharing): q.k with v_dot2_f32_bf16, summed over the
-//    8 lanes with DPP; softmax weights are rounded to bf16 and multiplied into
-//    V with v_dot2_f32_bf16 on token pairs, accumulating in fp32.
-//  * A wave handles 16-token tiles (2 tokens per group) and keeps the next
-//    two tiles' K/V loads in flight while it computes the current one.
-//  * Online softmax in the log2 domain; the running maximum is only raised
-//    when a logit exceeds it by more than 8 (weights stay <= 2^8), which keeps
-//    the result exact and makes rescales rare.
-//  * Groups and waves are merged with the log-sum-exp identity.  A sequence
-//    with one partition writes its bf16 output directly; otherwise partials
-//    (normalised output, log2 lse) go to the workspace for the merge pass.
+//    16-byte-per-lane access of the token's contiguous row.  A wave handles
+//    16-token tiles (2 tokens per group) and keeps the next two tiles' loads
+//    in flight while it computes the current one.
+//  * Block lookup: with B >= 16 a tile lies inside one block, whose id is a
+//    scalar load from the table row and whose base address is scalar; with
+//    B < 16 the partition's table entries are staged in LDS and each token
+//    looks its block up there.  Ids are clamped into [0, num_blocks).
+//  * The G = Hq/Hkv query heads of KV head g all use the same K/V registers
+//    (the GQA sharing).  q.k partial sums (v_dot2_f32_bf16) are
+//    reduce-scattered over the 8 lanes of a group, so each lane finishes one
+//    (head, token) score and takes one exponential; the bf16 weights are
+//    paired per head and broadcast back to the group with DPP, and p.v runs
+//    on token pairs with v_dot2_f32_bf16 into fp32 accumulators.
+//  * Online softmax in log2 units with one running maximum per head shared by
+//    the whole wave.  It is raised only when a score exceeds it by more than
+//    8 (weights stay <= 2^8): a ballot sends the wave to a rare slow path, so
+//    the fast path has no per-lane branches and the lane groups never need
+//    rescaling against each other.
+//  * Merge: the two groups of each 16-lane row are summed with DPP, rows and
+//    waves go through LDS and are combined with the log-sum-exp identity.  A
+//    sequence with one partition writes its bf16 output directly; otherwise
+//    partials (normalised output, log2 lse) go to the workspace for the merge
+//    pass.
 #include "../internal.hpp"
 #include "common.hpp"
 
@@ -36,7 +44,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;     // tokens per wave iteration
-constexpr int kChunk = 512;   // tokens whose table entries are staged at once
+constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -47,36 +55,69 @@ struct KV {
   uint4 v[2][kPieces];
 };
 
-template <int D, int G>
+// Sum of 8 per-lane values over the 8 lanes of a group, scattered: lane i
+// of the group ends with the total of value i.  Pairs are (i, 7 - i), then
+// (i, i ^ 2), then (i, i ^ 1); each step keeps half and adds the partner's.
+__device__ __forceinline__ float reduce_scatter8(const float (&v)[8], bool up4, bool b1, bool b0) {
+  float w[4], z[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float send = up4 ? v[k] : v[k + 4];
+    const float keep = up4 ? v[k + 4] : v[k];
+    w[k] = keep + dpp<kDppHalfMirror>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float send = b1 ? w[k] : w[k + 2];
+    const float keep = b1 ? w[k + 2] : w[k];
+    z[k] = keep + dpp<kDppXor2>(send);
+  }
+  const float send = b0 ? z[0] : z[1];
+  const float keep = b0 ? z[1] : z[0];
+  return keep + dpp<kDppXor1>(send);
+}
+
+// Lanes 2h and 2h+1 of a group hold value h (h = 0..3); every lane gets all four.
+__device__ __forceinline__ void broadcast4(uint32_t x, bool up4, uint32_t (&out)[4]) {
+  const uint32_t a = dpp<kDppBcast0>(x), b = dpp<kDppBcast2>(x);
+  const uint32_t a2 = dpp<kDppHalfMirror>(a), b2 = dpp<kDppHalfMirror>(b);
+  out[0] = up4 ? a2 : a;
+  out[1] = up4 ? b2 : b;
+  out[2] = up4 ? a : a2;
+  out[3] = up4 ? b : b2;
+}
+
+template <int D, int G, bool BIG>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   constexpr int PPL = D / 64;
-  __shared__ int32_t s_bt[kChunk];
+  constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score slot per lane per set
+  __shared__ int32_t s_bt[BIG ? 1 : kChunk];
+  __shared__ float s_acc[kWaves][4][G][D];
+  __shared__ float s_l[kWaves][4][G];
   __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];
 
   const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (SGPR) so that the tile loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane >> 3, li = lane & 7;
+  const int grp = lane >> 3, li = lane & 7, row = lane >> 4;
+  const bool up4 = (li & 4) != 0, b1 = (li & 2) != 0, b0 = (li & 1) != 0;
 
-  int len = a.seq_lens[s];
-  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int P = a.partition_size;
-  const int nparts = len > 0 ? (len + P - 1) / P : 1;
-  if (part >= nparts) return;
   const int start = part * P;
-  const int end = start + P < len ? start + P : len;
   const int lgB = a.log2_block_size;
   const int Bmask = (1 << lgB) - 1;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
   const int64_t bstride = a.cache_block_stride;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.key_cache) + (int64_t)g * D + 8 * li;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.value_cache) + (int64_t)g * D + 8 * li;
+  const uint16_t* kcache = static_cast<const uint16_t*>(a.key_cache);
+  const uint16_t* vcache = static_cast<const uint16_t*>(a.value_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.bt_stride;
+  const int width = (a.max_seq_len + Bmask) >> lgB;   // table entries that may be read
   const float scale = a.scale * kLog2e;
 
+  // Independent loads first: the length, the queries and (B < 16) the first
+  // chunk's table entries, so that their latencies overlap.
+  int len = a.seq_lens[s];
   uint4 qr[G][PPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -84,91 +125,164 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     for (int k = 0; k < PPL; ++k)
       qr[h][k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
                                                  ((int64_t)s * a.num_q_heads + g * G + h) * D + 64 * k + 8 * li);
-
-  float m[G], l[G], acc[G][PPL][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int k = 0; k < PPL; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][k][i] = 0.f;
-  }
-
-  for (int c0 = start; c0 < end; c0 += kChunk) {
-    const int c1 = c0 + kChunk < end ? c0 + kChunk : end;
+  auto stage_table = [&](int c0) {
     const int j0 = c0 >> lgB;
-    const int nj = ((c1 - 1) >> lgB) - j0 + 1;
-    __syncthreads();
+    int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
+    nj = nj < width - j0 ? nj : width - j0;
     for (int i = tid; i < nj; i += 256) {
       int b = bt_row[j0 + i];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       s_bt[i] = b;
     }
-    __syncthreads();
+  };
+  if (!BIG) stage_table(start);
 
-    // Tokens past c1 are redirected to token c0 (always valid), so every
-    // load stays inside the cache and can be issued unconditionally: with no
-    // branch around the prefetches the compiler's wait counts stay exact and
-    // the next tiles' loads remain in flight while this one is computed.
-    // All K loads are issued before the V loads so q.k can start first.
-    auto load = [&](int t0, KV<D>& r) {
-      int64_t off[2];
+  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  const int nparts = len > 0 ? (len + P - 1) / P : 1;
+  if (part >= nparts) return;
+  const int end = start + P < len ? start + P : len;
+
+  // per-lane constant part of a K/V element offset (BIG: tokens grp, grp + 8
+  // of the tile relative to its first token)
+  const int lane_off = g * D + 8 * li;
+
+  float m_own[NSET], l_own[NSET], acc[G][PPL][8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        int t = t0 + grp + 8 * u;
-        t = t < c1 ? t : c0;
-        const int64_t blk = s_bt[(t >> lgB) - j0];
-        off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems;
+  for (int j = 0; j < NSET; ++j) {
+    m_own[j] = kNegInf;
+    l_own[j] = 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < PPL; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][k][i] = 0.f;
+
+  const int chunk = BIG ? P : kChunk;
+  for (int c0 = start; c0 < end; c0 += chunk) {
+    const int c1 = c0 + chunk < end ? c0 + chunk : end;
+    const int j0 = c0 >> lgB;
+    if (!BIG) {
+      if (c0 != start) {
+        __syncthreads();
+        stage_table(c0);
       }
+      __syncthreads();
+    }
+
+    // Tokens past c1 read token c0 (always valid), so every load stays inside
+    // the cache and can be issued unconditionally: with no branch around the
+    // prefetches the compiler's wait counts stay exact and the next tiles'
+    // loads remain in flight while this one is computed.  All K loads are
+    // issued before the V loads so q.k can start first.
+    auto load = [&](int t0, KV<D>& r) {
+      if (BIG) {
+        const int tc = t0 < c1 ? t0 : c0;          // wave-uniform
+        int blk = __builtin_amdgcn_readfirstlane(bt_row[tc >> lgB]);
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
+        const uint16_t* kb = kcache + base;
+        const uint16_t* vb = vcache + base;
+        // tokens past c1 read the tile's first token (valid): their slots may
+        // hold anything, and a zero weight times a NaN is NaN
+        int64_t roff[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) roff[u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
 #pragma unroll
-        for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kbase + off[u] + 64 * k);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+          for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kb + roff[u] + 64 * k);
 #pragma unroll
-        for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vbase + off[u] + 64 * k);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vb + roff[u] + 64 * k);
+      } else {
+        int64_t off[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          int t = t0 + grp + 8 * u;
+          t = t < c1 ? t : c0;
+          const int64_t blk = s_bt[(t >> lgB) - j0];
+          off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kcache + off[u] + 64 * k);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vcache + off[u] + 64 * k);
+      }
     };
 
     auto compute = [&](int t0, const KV<D>& r) {
       const bool valid0 = t0 + grp < c1;
       const bool valid1 = t0 + grp + 8 < c1;
-      float x[G][2];
+      // partial dots: slot v of set j is head 4 j + v / 2, token v % 2
+      float x[NSET];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int j = 0; j < NSET; ++j) {
+        float w[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int v = 0; v < 8; ++v) {
+          const int h = 4 * j + (v >> 1), u = v & 1;
           float d = 0.f;
+          if (h < G) {
 #pragma unroll
-          for (int k = 0; k < PPL; ++k) {
-            const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h][k]);
-            const uint32_t* kk = reinterpret_cast<const uint32_t*>(&r.k[u][k]);
+            for (int k = 0; k < PPL; ++k) {
+              const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h][k]);
+              const uint32_t* kk = reinterpret_cast<const uint32_t*>(&r.k[u][k]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) d = dot2_bf16(qq[i], kk[i], d);
+              for (int i = 0; i < 4; ++i) d = dot2_bf16(qq[i], kk[i], d);
+            }
           }
-          x[h][u] = sum_lanes8(d) * scale;
+          w[v] = d;
         }
-      uint32_t pp[G];
+        // the reduction is a cross-lane operation: every lane must take part,
+        // so it runs unconditionally and invalid slots are masked afterwards
+        const float xs = reduce_scatter8(w, up4, b1, b0) * scale;
+        const bool ok = (4 * j + (li >> 1) < G) && (b0 ? valid1 : valid0);
+        x[j] = ok ? xs : kNegInf;
+      }
+      // rare slow path: raise the wave's running maxima
+      bool need = false;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float x0 = valid0 ? x[h][0] : kNegInf;
-        const float x1 = valid1 ? x[h][1] : kNegInf;
-        const float mx = fmaxf(x0, x1);
-        if (mx > m[h] + kRescaleSlack) {
-          const float alpha = fast_exp2(m[h] - mx);
-          l[h] *= alpha;
+      for (int j = 0; j < NSET; ++j) need |= x[j] > m_own[j] + kRescaleSlack;
+      if (__any(need)) {
+        uint32_t al[NSET][4];
+#pragma unroll
+        for (int j = 0; j < NSET; ++j) {
+          float mx = x[j];
+          mx = fmaxf(mx, dpp<kDppXor1>(mx));
+          mx = fmaxf(mx, dpp<kDppRor8>(mx));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mn = fmaxf(m_own[j], mx);
+          const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own[j] - mn);
+          l_own[j] *= alpha;
+          m_own[j] = mn;
+          broadcast4(__float_as_uint(alpha), up4, al[j]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float alpha = __uint_as_float(al[h >> 2][h & 3]);
 #pragma unroll
           for (int k = 0; k < PPL; ++k)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[h][k][i] *= alpha;
-          m[h] = mx;
         }
-        const float p0 = valid0 ? fast_exp2(x0 - m[h]) : 0.f;
-        const float p1 = valid1 ? fast_exp2(x1 - m[h]) : 0.f;
-        pp[h] = pack_bf16x2(p0, p1);
-        l[h] += bf16_lo(pp[h]) + bf16_hi(pp[h]);
+      }
+      // weights: one exponential per lane, paired per head, broadcast to the group
+      uint32_t pp[NSET][4];
+#pragma unroll
+      for (int j = 0; j < NSET; ++j) {
+        const float p = x[j] == kNegInf ? 0.f : fast_exp2(x[j] - m_own[j]);
+        const float other = dpp<kDppXor1>(p);
+        const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
+        l_own[j] += b0 ? bf16_hi(pk) : bf16_lo(pk);
+        broadcast4(pk, up4, pp[j]);
       }
       // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
 #pragma unroll
@@ -181,8 +295,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
           const uint32_t hi = __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            acc[h][k][2 * i] = dot2_bf16(pp[h], lo, acc[h][k][2 * i]);
-            acc[h][k][2 * i + 1] = dot2_bf16(pp[h], hi, acc[h][k][2 * i + 1]);
+            const uint32_t w = pp[h >> 2][h & 3];
+            acc[h][k][2 * i] = dot2_bf16(w, lo, acc[h][k][2 * i]);
+            acc[h][k][2 * i + 1] = dot2_bf16(w, hi, acc[h][k][2 * i + 1]);
           }
         }
       }
@@ -218,40 +333,42 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  // Merge the 8 lane groups of the wave (butterfly over lanes 8, 16, 32 apart).
+  // Merge.  All lane groups of a wave share the running maxima, so their
+  // partial sums add directly: the two groups of a row with DPP, the four
+  // rows and four waves through LDS.
 #pragma unroll
-  for (int sh = 8; sh < 64; sh <<= 1) {
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], sh);
-      const float lo = __shfl_xor(l[h], sh);
-      const float M = fmaxf(m[h], mo);
-      const float wa = m[h] == kNegInf ? 0.f : fast_exp2(m[h] - M);
-      const float wb = mo == kNegInf ? 0.f : fast_exp2(mo - M);
-      l[h] = l[h] * wa + lo * wb;
+    for (int k = 0; k < PPL; ++k)
 #pragma unroll
-      for (int k = 0; k < PPL; ++k)
+      for (int i = 0; i < 8; ++i) acc[h][k][i] += dpp<kDppRor8>(acc[h][k][i]);
+  float lp[NSET];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][k][i] = acc[h][k][i] * wa + __shfl_xor(acc[h][k][i], sh) * wb;
-      m[h] = M;
-    }
+  for (int j = 0; j < NSET; ++j) {
+    lp[j] = l_own[j] + dpp<kDppXor1>(l_own[j]);
+    lp[j] += dpp<kDppRor8>(lp[j]);
   }
-  if (lane < 8) {
+  if ((lane & 8) == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int k = 0; k < PPL; ++k)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s_acc[wave][h][64 * k + 8 * li + i] = acc[h][k][i];
-      if (lane == 0) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
+        for (int i = 0; i < 8; ++i) s_acc[wave][row][h][64 * k + 8 * li + i] = acc[h][k][i];
+    if (!b0) {
+#pragma unroll
+      for (int j = 0; j < NSET; ++j) {
+        const int h = 4 * j + (li >> 1);
+        if (h < G) {
+          s_l[wave][row][h] = lp[j];
+          if (row == 0) s_m[wave][h] = m_own[j];
+        }
       }
     }
   }
   __syncthreads();
 
-  // Merge the waves: thread -> (head h, dim d) outputs.
+  // Combine rows and waves: thread -> (head h, dim d) outputs.
   for (int o = tid; o < G * D; o += 256) {
     const int h = o / D, d = o % D;
     float M = kNegInf;
@@ -263,20 +380,26 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       for (int w = 0; w < kWaves; ++w) {
         const float mw = s_m[w][h];
         const float e = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-        L += s_l[w][h] * e;
-        A += s_acc[w][h][d] * e;
+        float lw = 0.f, aw = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          lw += s_l[w][rr][h];
+          aw += s_acc[w][rr][h][d];
+        }
+        L += lw * e;
+        A += aw * e;
       }
     }
     const int hq = g * G + h;
-    const int64_t row = (int64_t)s * a.num_q_heads + hq;
+    const int64_t orow = (int64_t)s * a.num_q_heads + hq;
     const float val = L > 0.f ? A / L : 0.f;
     const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;
     if (nparts == 1) {
-      static_cast<uint16_t*>(a.out)[row * D + d] = to_bf16(val);
-      if (a.lse && d == 0) a.lse[row] = lse2 * kLn2;
+      static_cast<uint16_t*>(a.out)[orow * D + d] = to_bf16(val);
+      if (a.lse && d == 0) a.lse[orow] = lse2 * kLn2;
     } else {
-      a.ws_out[(row * a.max_parts + part) * D + d] = val;
-      if (d == 0) a.ws_lse[row * a.max_parts + part] = lse2;
+      a.ws_out[(orow * a.max_parts + part) * D + d] = val;
+      if (d == 0) a.ws_lse[orow * a.max_parts + part] = lse2;
     }
   }
 }
@@ -311,8 +434,11 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G>
 int launch_g(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, G>), dim3(a.max_parts, a.num_kv_heads, a.num_seqs), dim3(256), 0,
-                     st, a);
+  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
+  if (a.log2_block_size >= 4)
+    hipLaunchKernelGGL((decode_partition_kernel<D, G, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, G, false>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, st, a);
