@@ -322,7 +322,8 @@ def main():
     print("[bench] timed steps done", file=sys.stderr, flush=True)
 
     # dominant kernel: back-to-back decode launches on the same stream,
-    # rotating over the pools, bracketed by HIP events
+    # rotating over the pools, bracketed by one pair of HIP events (an event
+    # between launches adds its own cost to every launch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     insts[0].decode(stream)
     torch.cuda.synchronize()
