@@ -231,6 +231,189 @@ def measure_prefill(torch, B, hip_side, workloads, block_size=16, reps=10):
             "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def time_launches(torch, fn, reps):
+    """Seconds per call of fn (one or more launches on the current stream),
+    from one pair of HIP events around reps back-to-back calls."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def hbm(gbps):
+    return round(gbps / HBM_PEAK_GBPS, 4)
+
+
+def unique_kv_bytes(table, seq_lens, block_size, num_kv_heads, head_dim):
+    """K/V bytes of the distinct physical rows that a decode call attends
+    (blocks shared by several sequences count once)."""
+    rows = {}
+    for r, n in zip(table, seq_lens):
+        n = int(n)
+        for j in range(-(-n // block_size)):
+            b = int(r[j])
+            rows[b] = max(rows.get(b, 0), min(block_size, n - j * block_size))
+    return sum(rows.values()) * 2 * num_kv_heads * head_dim * 2
+
+
+def measure_long_context(torch, B, hip_side, workloads, reps=3):
+    """Decode over the 32-layer pool (26,785 16-token blocks per layer,
+    52.3 GiB, layer-major [layer][K|V][block]); 8 sequences of
+    U{16384..32768} tokens; partitions of 512 tokens plus the merge.  One
+    step decodes every layer with that layer's queries."""
+    wl = workloads.long_context()
+    L, S, P = wl.num_layers, wl.num_seqs, 512
+    kv = torch.full((L, 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), float("nan"),
+                    dtype=torch.bfloat16, device="cuda")
+    h = hip_side.HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]),
+                         layers=[(l, kv[l, 0], kv[l, 1]) for l in range(L)])
+    msl = max(wl.seq_lens)
+    qs = [workloads.device_query(wl.seed, S, wl.num_q_heads, wl.head_dim, layer=l) for l in range(L)]
+    out = torch.empty_like(qs[0])
+    ws = torch.empty(B.pa_paged_decode_workspace_size(S, wl.num_q_heads, wl.head_dim, msl, P),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        for l in range(L):
+            B.pa_paged_decode(out, qs[l], kv[l, 0], kv[l, 1], h.table_dev, h.seq_lens_dev, msl, wl.scale,
+                              partition_size=P, workspace=ws)
+    sec = time_launches(torch, step, reps)
+    per_layer = decode_bytes(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size)
+    gbps = per_layer * L / sec / 1e9
+    res = {"workload": "8 sequences of U{16384..32768} tokens over a 32-layer pool of 26,785 blocks per layer",
+           "pool_gib": round(kv.numel() * 2 / 2**30, 2), "partition_size": P, "layers": L,
+           "step_ms": round(sec * 1e3, 3), "layer_us": round(sec / L * 1e6, 1),
+           "bytes_per_layer": per_layer, "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
+           "seqs_per_s": round(S / sec, 1)}
+    del kv, h, qs
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_prefix_cow(torch, B, hip_side, workloads, reps=20):
+    """256 sequences forked from one 2050-token prompt, each with a suffix
+    of U{1..512} tokens: the 255 copy-on-write copies (one layer, and all 32
+    layers' 64 cache tensors in one call), the suffix writes, and decode.
+    Decode GB/s is given on logical bytes (every sequence's K/V) and on
+    unique bytes (shared prompt blocks once)."""
+    wl = workloads.prefix_cow()
+    h = hip_side.HipStep(wl, gen="device")
+    S = wl.num_seqs
+    pairs = np.array(h.pairs, dtype=np.int32)
+    blk_bytes = wl.block_size * wl.num_kv_heads * wl.head_dim * 2
+    res = {"workload": "256 forks of a 2050-token prompt, suffixes U{1..512}", "cow_pairs": len(pairs)}
+    sec = time_launches(torch, lambda: B.pa_copy_blocks([h.kc, h.vc], pairs), reps)
+    cb = 2 * len(pairs) * blk_bytes * 2
+    res["copy_1_layer"] = {"us": round(sec * 1e6, 2), "bytes": cb, "gbps": round(cb / sec / 1e9, 1)}
+    big = torch.empty((32, 2, wl.num_blocks) + tuple(h.kc.shape[1:]), dtype=torch.bfloat16, device="cuda")
+    caches = [big[l, c] for l in range(32) for c in range(2)]
+    sec = time_launches(torch, lambda: B.pa_copy_blocks(caches, pairs), 5)
+    cb = 2 * len(pairs) * blk_bytes * 64
+    res["copy_32_layers"] = {"us": round(sec * 1e6, 2), "bytes": cb, "gbps": round(cb / sec / 1e9, 1),
+                             "hbm_frac": hbm(cb / sec / 1e9)}
+    del big, caches
+    torch.cuda.empty_cache()
+    seqs = h.step_seqs
+    n0 = np.concatenate([[0], np.cumsum([wl.new_lens[s] for s in seqs])])
+    kn = torch.cat([workloads.device_seq_kv(wl.seed, s, wl.new_lens[s], wl.num_kv_heads, wl.head_dim, 0, 9)[0]
+                    for s in seqs])
+    slots = torch.from_numpy(np.asarray(h.step_slots, dtype=np.int64)).cuda()
+    T = int(n0[-1])
+    # rewriting the same rows leaves the caches as they were
+    kc2, vc2 = h.kc.clone(), h.vc.clone()
+    sec = time_launches(torch, lambda: B.pa_reshape_and_cache(kn, kn, kc2, vc2, slots), reps)
+    rb = 2 * T * wl.num_kv_heads * wl.head_dim * 2 * 2
+    res["reshape"] = {"tokens": T, "us": round(sec * 1e6, 2), "bytes": rb, "gbps": round(rb / sec / 1e9, 1),
+                      "hbm_frac": hbm(rb / sec / 1e9)}
+    del kc2, vc2
+    q = workloads.device_query(wl.seed, S, wl.num_q_heads, wl.head_dim)
+    out = torch.empty_like(q)
+    msl = max(wl.seq_lens)
+    logical = decode_bytes(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size)
+    uniq = unique_kv_bytes(h.table, h.seq_lens, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    for P in (0, 512):
+        ws = torch.empty(max(256, B.pa_paged_decode_workspace_size(S, wl.num_q_heads, wl.head_dim, msl, P)),
+                         dtype=torch.uint8, device="cuda")
+        sec = time_launches(torch, lambda: B.pa_paged_decode(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev,
+                                                             msl, wl.scale, partition_size=P, workspace=ws), reps)
+        res[f"decode_p{P}"] = {"us": round(sec * 1e6, 2), "logical_gbps": round(logical / sec / 1e9, 1),
+                               "unique_gbps": round(uniq / sec / 1e9, 1), "unique_hbm_frac": hbm(uniq / sec / 1e9),
+                               "seqs_per_s": round(S / sec, 1)}
+    res["logical_bytes"], res["unique_kv_bytes"] = logical, uniq
+    del h
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
+    """The mixed step at one block size: writes of the step's 8,432 new
+    tokens, prefill of 16 chunks of 512 queries, decode of 240 sequences
+    (partitions of 512 tokens), on one stream; each call timed alone and the
+    three together."""
+    wl = workloads.mixed_step(block_size)
+    h = hip_side.HipStep(wl, gen="device")
+    chunks = [s for s in range(wl.num_seqs) if wl.q_lens[s] > 1]
+    dec = [s for s in range(wl.num_seqs) if wl.q_lens[s] == 1]
+    seqs = h.step_seqs
+    T = int(sum(wl.new_lens[s] for s in seqs))
+    kn = workloads.device_query(wl.seed, T, wl.num_kv_heads, wl.head_dim, layer=3)
+    slots = torch.from_numpy(np.asarray(h.step_slots, dtype=np.int64)).cuda()
+    qp = workloads.device_query(wl.seed, int(sum(wl.q_lens[s] for s in chunks)), wl.num_q_heads, wl.head_dim)
+    op = torch.empty_like(qp)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum([wl.q_lens[s] for s in chunks])]), dtype=torch.int32,
+                       device="cuda")
+    bt_p = h.table_dev[chunks].contiguous()
+    sl_p = h.seq_lens_dev[chunks].contiguous()
+    msl_p = int(max(wl.seq_lens[s] for s in chunks))
+    qd = workloads.device_query(wl.seed, len(dec), wl.num_q_heads, wl.head_dim, layer=1)
+    od = torch.empty_like(qd)
+    bt_d = h.table_dev[dec].contiguous()
+    sl_d = h.seq_lens_dev[dec].contiguous()
+    dl = [wl.seq_lens[s] for s in dec]
+    msl_d = int(max(dl))
+    ws = torch.empty(B.pa_paged_decode_workspace_size(len(dec), wl.num_q_heads, wl.head_dim, msl_d, 512),
+                     dtype=torch.uint8, device="cuda")
+    # the timed writes go to scratch copies of the caches: same slots, same bytes
+    kc2, vc2 = h.kc.clone(), h.vc.clone()
+
+    def reshape():
+        B.pa_reshape_and_cache(kn, kn, kc2, vc2, slots)
+
+    def prefill():
+        B.pa_paged_prefill(op, qp, h.kc, h.vc, bt_p, qsl, sl_p, max(wl.q_lens), msl_p, wl.scale)
+
+    def decode():
+        B.pa_paged_decode(od, qd, h.kc, h.vc, bt_d, sl_d, msl_d, wl.scale, partition_size=512, workspace=ws)
+
+    def step():
+        reshape()
+        prefill()
+        decode()
+    t_r = time_launches(torch, reshape, reps)
+    t_p = time_launches(torch, prefill, reps)
+    t_d = time_launches(torch, decode, reps)
+    t_s = time_launches(torch, step, reps)
+    flops = prefill_flops([wl.q_lens[s] for s in chunks], [wl.seq_lens[s] for s in chunks], wl.num_q_heads,
+                          wl.head_dim)
+    db = decode_bytes(dl, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, block_size)
+    rb = 2 * T * wl.num_kv_heads * wl.head_dim * 2 * 2
+    res = {"block_size": block_size, "step_ms": round(t_s * 1e3, 3), "tokens_written": T,
+           "reshape_us": round(t_r * 1e6, 2), "reshape_gbps": round(rb / t_r / 1e9, 1),
+           "prefill_us": round(t_p * 1e6, 1), "prefill_gflop": round(flops / 1e9, 2),
+           "prefill_tflops": round(flops / t_p / 1e12, 1),
+           "prefill_mfma_frac": round(flops / t_p / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "decode_us": round(t_d * 1e6, 1), "decode_bytes": db, "decode_gbps": round(db / t_d / 1e9, 1),
+           "decode_hbm_frac": hbm(db / t_d / 1e9), "decode_seqs_per_s": round(len(dec) / t_d, 1)}
+    del h, kc2, vc2
+    torch.cuda.empty_cache()
+    return res
+
+
 def counter_run(kind, reps):
     """Launch only one kernel kind, for rocprofv3 --pmc passes:
     'decode' = the decode call of this workload on rotating pools,
@@ -275,6 +458,8 @@ def main():
                     help="back-to-back decode launches timed with HIP events for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the long-context, prefix-sharing and mixed-step measurements")
     ap.add_argument("--counter-run", choices=["decode", "copy"],
                     help="only launch one kernel kind (for rocprofv3 --pmc passes) and exit")
     args = ap.parse_args()
@@ -381,6 +566,16 @@ def main():
         del insts
         torch.cuda.empty_cache()
         line["prefill"] = measure_prefill(torch, B, hip_side, workloads)
+    if not args.no_configs:
+        cfg = {}
+        print("[bench] long-context 32-layer pool", file=sys.stderr, flush=True)
+        cfg["long_context_decode"] = measure_long_context(torch, B, hip_side, workloads)
+        print("[bench] prefix sharing + copy-on-write", file=sys.stderr, flush=True)
+        cfg["prefix_cow_decode"] = measure_prefix_cow(torch, B, hip_side, workloads)
+        for bs in (1, 16, 32):
+            print(f"[bench] mixed step, block size {bs}", file=sys.stderr, flush=True)
+            cfg[f"mixed_step_b{bs}"] = measure_mixed(torch, B, hip_side, workloads, bs)
+        line["configs"] = cfg
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -234,3 +234,25 @@ def pool_ops(seed: int, n_ops: int = 200, max_seqs: int = 12, max_append: int = 
             s = live.pop(int(rng.integers(len(live))))
             ops.append(("free", s))
     return ops
+
+
+def device_seq_kv(seed: int, seq: int, n_tokens: int, num_kv_heads: int, head_dim: int,
+                  layer: int = 0, part: int = 0, device="cuda"):
+    """Device-side counterpart of seq_kv_bits for workloads too large to
+    draw on the host: K and V [n, Hkv, D] bf16 drawn N(0, 1) by a torch
+    generator seeded per (seed, layer, sequence, part).  A check copies the
+    same tensors back to the host; it never redraws them with numpy."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((((seed * 131 + layer) * 1_000_003 + seq) * 7 + part) % (2**63 - 1))
+    k = torch.randn((n_tokens, num_kv_heads, head_dim), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((n_tokens, num_kv_heads, head_dim), generator=g, device=device, dtype=torch.float32)
+    return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def device_query(seed: int, n_rows: int, num_q_heads: int, head_dim: int, layer: int = 0, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 977 + layer * 31 + 5) % (2**63 - 1))
+    return torch.randn((n_rows, num_q_heads, head_dim), generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)

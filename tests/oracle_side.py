@@ -6,7 +6,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import cache_ops
+from oracle import attention, cache_ops
 from oracle.pool_model import PoolModel
 from paged_kv_cache_327_amd import workloads
 
@@ -30,6 +30,24 @@ def paged_from_logical(ks, vs, block_size, num_blocks, order, pool=None):
             cache_ops.reshape_and_cache(kc, vc, k, v, np.array(slots))
         lens.append(len(k))
     return pool, kc, vc, table_array(pool, range(len(ks))), np.array(lens, dtype=np.int32)
+
+
+def logical_decode(q_bits, k_bits, v_bits, scale):
+    """Oracle decode of one sequence from its logical (contiguous) K/V:
+    q_bits [Hq, D], k_bits / v_bits [n, Hkv, D] bf16 bits.  Query head h
+    reads KV head h // (Hq / Hkv).  Returns out [Hq, D], lse [Hq] (fp64)."""
+    Hq, D = q_bits.shape
+    Hkv = k_bits.shape[1]
+    G = Hq // Hkv
+    q = attention.bf16_to_f64(q_bits)
+    out = np.zeros((Hq, D))
+    lse = np.full(Hq, -np.inf)
+    for g in range(Hkv):
+        o, l = attention.softmax_attend(q[g * G:(g + 1) * G], attention.bf16_to_f64(k_bits[:, g]),
+                                        attention.bf16_to_f64(v_bits[:, g]), scale)
+        out[g * G:(g + 1) * G] = o
+        lse[g * G:(g + 1) * G] = l
+    return out, lse
 
 
 def table_array(pool, seqs, width=None):

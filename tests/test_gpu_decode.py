@@ -8,8 +8,9 @@ import torch
 from oracle import attention
 from paged_kv_cache_327_amd import workloads
 from tests.hip_side import HipStep
+from tests import oracle_side
 from tests.oracle_side import OracleStep
-from tests.parity import assert_attention_close, assert_lse_close
+from tests.parity import LSE_ABS, MAX_ABS, MEAN_ABS, assert_attention_close, assert_lse_close
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +84,63 @@ def test_garbage_past_each_row_is_never_read():
         h.table_dev[s, -(-int(n) // 16):] = torch.tensor([2**31 - 1, -5] * 20, dtype=torch.int32)[: 40 - (-(-int(n) // 16))]
     out, _ = h.decode(q, partition_size=64)
     assert torch.equal(out, ref)
+
+
+def check_sampled(h, q, out, lse, rows, sample, layer=0, what=""):
+    """Oracle decode of sampled rows from the logical K/V exactly as drawn
+    for the caches (copied back from the device when drawn there)."""
+    got = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    errs = []
+    for i in sample:
+        k, v = h.logical_kv_bits(rows[i], layer)
+        want, want_lse = oracle_side.logical_decode(q[i], k, v, h.wl.scale)
+        assert np.all(np.isfinite(got[i])), f"{what}: row {i} not finite"
+        errs.append(np.abs(got[i] - want).ravel())
+        assert np.max(np.abs(got_lse[i] - want_lse)) <= LSE_ABS, f"{what}: lse of row {i}"
+    errs = np.concatenate(errs)
+    assert errs.max() <= MAX_ABS and errs.mean() <= MEAN_ABS, f"{what}: {errs.max():.3g} {errs.mean():.3g}"
+
+
+@pytest.mark.parametrize("block_size", [1, 16, 32])
+def test_mixed_step_decode_sampled(block_size):
+    """The mixed step's 240 decode sequences (lognormal lengths, median
+    1500, up to 32768) over the full 2^20-slot pool, K/V drawn on the
+    device; the oracle checks the longest, the shortest and 14 others."""
+    wl = workloads.mixed_step(block_size)
+    print(f"[decode] {wl.name} sampled", flush=True)
+    h = HipStep(wl, gen="device")
+    rows = [s for s in range(wl.num_seqs) if wl.q_lens[s] == 1]
+    q = workloads.query_bits(wl.seed, len(rows), wl.num_q_heads, wl.head_dim, layer=7)
+    out, lse = h.decode(q, partition_size=512, rows=rows)
+    lens = np.array([wl.seq_lens[s] for s in rows])
+    rng = np.random.default_rng(block_size + 100)
+    sample = sorted({int(np.argmax(lens)), int(np.argmin(lens))} | set(rng.choice(len(rows), 14, replace=False).tolist()))
+    check_sampled(h, q, out, lse, rows, sample, what=wl.name)
+
+
+def test_long_context_32_layer_pool():
+    """Long-context decode over the 32-layer pool (26,785 blocks of 16
+    tokens per layer, 52.3 GiB of K/V, layer-major [layer][K|V][block]):
+    8 sequences of U{16384..32768} tokens, partitions of 512 tokens and the
+    log-sum-exp merge.  Every layer is decoded; the oracle checks all 8
+    sequences of layers 0 and 31 and one sequence of layer 13."""
+    wl = workloads.long_context()
+    print(f"[decode] {wl.name}: 32-layer pool", flush=True)
+    L = wl.num_layers
+    kv = torch.full((L, 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), float("nan"),
+                    dtype=torch.bfloat16, device="cuda")
+    layers = [(l, kv[l, 0], kv[l, 1]) for l in range(L)]
+    h = HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]), layers=layers)
+    rows = list(range(wl.num_seqs))
+    for l in range(L):
+        q = workloads.query_bits(wl.seed, wl.num_seqs, wl.num_q_heads, wl.head_dim, layer=l)
+        out, lse = h.decode(q, partition_size=512, caches=(kv[l, 0], kv[l, 1]))
+        if l in (0, 31):
+            check_sampled(h, q, out, lse, rows, rows, layer=l, what=f"layer {l}")
+        elif l == 13:
+            check_sampled(h, q, out, lse, rows, [5], layer=l, what=f"layer {l}")
+        else:
+            assert torch.isfinite(out.float()).all()
+    del kv, layers, h
+    torch.cuda.empty_cache()
