@@ -12,9 +12,12 @@
 // queries.  Key tiles of 64 keys are gathered through the block table into
 // LDS once per work-group and used by all of its waves (the GQA sharing):
 //   * K and V are stored row-major [key][d]; the V^T operand is read with
-//     gfx950's transposing LDS read (ds_read_b64_tr_b16).  Keys past the
-//     sequence end are written as zeros (their loads are redirected to key
-//     0), so NaN bytes in unwritten slots can never reach a product.
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16).  Loads of keys past
+//     the sequence end are redirected to a written row and those keys are
+//     masked out of the softmax, so bytes of unwritten slots (NaN, say) can
+//     never reach a product.
+//   * With B >= 16 each wave stages one 16-key run of a block per tile: the
+//     block id is a scalar load and the row base a scalar address.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
 //     so the softmax max and sum are in-lane (plus one exchange between the
 //     two lane halves).
@@ -35,9 +38,13 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Staged K/V pieces use a native vector type: copies of it are plain loads
+// and stores, which keeps the staging arrays in registers.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKeys = 64;        // keys per tile
 constexpr int kQ = 32;           // queries per wave
+constexpr int kXcds = 8;         // accelerator dies of an MI355X, one L2 each
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kSlack = 8.0f;
 
@@ -64,7 +71,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D, int HW, bool CAUSAL>
+template <int D, int HW, bool CAUSAL, bool BIG>
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
@@ -73,7 +80,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   constexpr int UPT = 32 * CPR / 256;        // (key pair, chunk) units per thread
   __shared__ Smem<D> sm;
 
-  const int i = blockIdx.z;                  // request
+  // Work-groups are dealt to the 8 XCDs round-robin by linear id, and each
+  // XCD has its own L2.  Work item (request i, head group y, query tile) is
+  // placed so that all query tiles of one (i, y) land on the same XCD, one
+  // after another: they walk the same K/V tiles at about the same time, so
+  // the XCD's L2 serves those tiles to all of them.  Group n = i * Y + y goes
+  // to XCD n % 8; with 8 head groups each XCD owns one KV head.
+  const int X = (a.max_query_len + kQ * QS - 1) / (kQ * QS);   // query tiles per request
+  const int Y = a.num_q_heads / HW;                             // head groups
+  const int xcd = blockIdx.x & (kXcds - 1), k_in_xcd = blockIdx.x / kXcds;
+  const int grp = xcd + kXcds * (k_in_xcd / X);
+  if (grp >= a.num_seqs * Y) return;
+  const int i = grp / Y, y = grp % Y;         // request, head group
+  const int xt = k_in_xcd % X;                // 0 = the request's last (heaviest) query tile
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, col = lane & 31;
@@ -84,12 +103,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   kv_len = kv_len > a.max_seq_len ? a.max_seq_len : kv_len;
   const int ctx = kv_len - q_len;            // absolute position of query 0
   const int span = kQ * QS;
-  const int q0 = (gridDim.x - 1 - blockIdx.x) * span;   // heaviest tiles first
+  const int q0 = (X - 1 - xt) * span;                    // heaviest tiles first
   if (q_len <= 0 || q0 >= q_len || ctx < 0) return;
 
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int h = blockIdx.y * HW + wave % HW;             // this wave's query head
-  const int g = (blockIdx.y * HW) / G;                   // shared KV head
+  const int h = y * HW + wave % HW;                      // this wave's query head
+  const int g = (y * HW) / G;                            // shared KV head
   const int qw = q0 + (wave / HW) * kQ;                  // this wave's first query
   const int lgB = a.log2_block_size;
   const int Bmask = (1 << lgB) - 1;
@@ -122,7 +141,25 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   }
   const int qpos = ctx + qw + col;           // absolute position of this lane's query
 
-  // Tile loading: unit u = (key pair kp, 16-byte chunk c).
+  // Tile staging.  Keys at or past kv_end are loaded from a valid row
+  // instead (the wave's first key of the tile, or key 0) and are removed from the
+  // softmax by the score mask below, so whatever bytes unwritten slots hold
+  // never reach a product and the loads need no branch.
+  //   BIG (B >= 16): wave w stages keys n0 + 16 w .. n0 + 16 w + 15, which lie
+  //   in one block; the block id is a scalar load and the row base a scalar
+  //   address, each lane adds a fixed 32-bit offset.
+  //   otherwise: unit u = (key pair kp, 16-byte chunk c); every key looks up
+  //   its own block.
+  constexpr int KPI = 64 / CPR;              // BIG: keys per load instruction
+  constexpr int NI = BIG ? 16 / KPI : 2 * UPT;
+  const int kr0 = lane / CPR, chunk = lane % CPR;
+  uint32_t voff[BIG ? NI : 1];
+  if constexpr (BIG) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      voff[j] = (uint32_t)(((KPI * j + kr0) * row_elems + (int64_t)g * D + 8 * chunk) * 2);
+  }
+  const uint32_t voff_row0 = (uint32_t)(((int64_t)g * D + 8 * chunk) * 2);
   int kp_[UPT], ch_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
@@ -130,43 +167,73 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     kp_[u] = unit / CPR;
     ch_[u] = unit % CPR;
   }
-  int blk_next[UPT][2];                       // table entries, one tile ahead of the loads
-  uint4 kr[UPT][2], vr[UPT][2];               // staged K/V of the tile being loaded
+  int blk_next[BIG ? 1 : UPT][2];             // table entries, one tile ahead of the loads
+  u32x4_t kr[NI], vr[NI];                     // staged K/V of the tile being loaded
 
+  auto wave_key = [&](int tile) {
+    const int kw = tile * kKeys + 16 * wave;
+    return kw < kv_end ? kw : 0;
+  };
   auto fetch_table = [&](int tile) {
+    if constexpr (BIG) {
+      int b = bt_row[wave_key(tile) >> lgB];
+      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      blk_next[0][0] = __builtin_amdgcn_readfirstlane(b);
+    } else {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u)
+      for (int u = 0; u < UPT; ++u)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        int p = tile * kKeys + 2 * kp_[u] + e;
-        p = p < kv_end ? p : 0;
-        int b = bt_row[p >> lgB];
-        blk_next[u][e] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      }
+        for (int e = 0; e < 2; ++e) {
+          int p = tile * kKeys + 2 * kp_[u] + e;
+          p = p < kv_end ? p : 0;
+          int b = bt_row[p >> lgB];
+          blk_next[u][e] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+        }
+    }
   };
   auto issue_loads = [&](int tile) {
+    if constexpr (BIG) {
+      const int kw = wave_key(tile);
+      const int lim = kv_end - 1 - kw;        // rows 0 .. lim of the wave's 16 are keys
+      const int64_t base = ((int64_t)blk_next[0][0] * bstride + (int64_t)(kw & Bmask) * row_elems) * 2;
+      const char* kb = reinterpret_cast<const char*>(a.key_cache) + base;
+      const char* vb = reinterpret_cast<const char*>(a.value_cache) + base;
 #pragma unroll
-    for (int u = 0; u < UPT; ++u)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        int p = tile * kKeys + 2 * kp_[u] + e;
-        p = p < kv_end ? p : 0;
-        const int64_t off = (int64_t)blk_next[u][e] * bstride + (int64_t)(p & Bmask) * row_elems + 8 * ch_[u];
-        kr[u][e] = *reinterpret_cast<const uint4*>(kc + off);
-        vr[u][e] = *reinterpret_cast<const uint4*>(vc + off);
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t off = KPI * j + kr0 <= lim ? voff[j] : voff_row0;
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
       }
-  };
-  auto store_tile = [&](int tile, int buf) {
+    } else {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      uint4 k0 = kr[u][0], k1 = kr[u][1], v0 = vr[u][0], v1 = vr[u][1];
-      const int key = 2 * kp_[u];
-      if (tile * kKeys + key >= kv_end) { k0 = make_uint4(0, 0, 0, 0); v0 = k0; }
-      if (tile * kKeys + key + 1 >= kv_end) { k1 = make_uint4(0, 0, 0, 0); v1 = k1; }
-      *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kRow + 8 * ch_[u]]) = k0;
-      *reinterpret_cast<uint4*>(&sm.k[buf][(key + 1) * Smem<D>::kRow + 8 * ch_[u]]) = k1;
-      *reinterpret_cast<uint4*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * ch_[u]]) = v0;
-      *reinterpret_cast<uint4*>(&sm.v[buf][(key + 1) * Smem<D>::kVRow + 8 * ch_[u]]) = v1;
+      for (int u = 0; u < UPT; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          int p = tile * kKeys + 2 * kp_[u] + e;
+          p = p < kv_end ? p : 0;
+          const int64_t off = (int64_t)blk_next[u][e] * bstride + (int64_t)(p & Bmask) * row_elems + 8 * ch_[u];
+          kr[2 * u + e] = *reinterpret_cast<const u32x4_t*>(kc + off);
+          vr[2 * u + e] = *reinterpret_cast<const u32x4_t*>(vc + off);
+        }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (BIG) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int key = 16 * wave + KPI * j + kr0;
+        *reinterpret_cast<u32x4_t*>(&sm.k[buf][key * Smem<D>::kRow + 8 * chunk]) = kr[j];
+        *reinterpret_cast<u32x4_t*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * chunk]) = vr[j];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = 2 * kp_[u] + e;
+          *reinterpret_cast<u32x4_t*>(&sm.k[buf][key * Smem<D>::kRow + 8 * ch_[u]]) = kr[2 * u + e];
+          *reinterpret_cast<u32x4_t*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * ch_[u]]) = vr[2 * u + e];
+        }
     }
   };
 
@@ -177,12 +244,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  // Staging is unconditional: tiles past the end read key 0 (always valid)
-  // and store zeros, so no branch separates a load from its use.
+  // Staging is unconditional: tiles past the end read valid rows, so no
+  // branch separates a load from its use.
   fetch_table(0);
   issue_loads(0);
   fetch_table(1);
-  store_tile(0, 0);
+  store_tile(0);
   issue_loads(1);
   fetch_table(2);
   __syncthreads();
@@ -295,7 +362,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       for (int b = 0; b < DB; ++b) va[b] = vn[b];
     }
     // stage the next tile into the other buffer and start the one after
-    store_tile(t + 1, buf ^ 1);
+    store_tile(buf ^ 1);
     issue_loads(t + 2);
     fetch_table(t + 3);
     __syncthreads();
@@ -321,11 +388,20 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 template <int D, int HW>
 int launch_hw(const PrefillArgs& a, hipStream_t st) {
   const int span = kQ * (4 / HW);
-  const dim3 grid((unsigned)((a.max_query_len + span - 1) / span), a.num_q_heads / HW, a.num_seqs);
-  if (a.causal)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, true>), grid, dim3(256), 0, st, a);
+  const int64_t X = (a.max_query_len + span - 1) / span;
+  const int64_t groups = (int64_t)a.num_seqs * (a.num_q_heads / HW);
+  const int64_t n = X * kXcds * ((groups + kXcds - 1) / kXcds);
+  if (n * 256 > 0xffffffffLL) return (int)hipErrorInvalidConfiguration;   // grid size in work-items is 32-bit
+  const dim3 grid((unsigned)n);
+  const bool big = a.log2_block_size >= 4;
+  if (a.causal && big)
+    hipLaunchKernelGGL((prefill_kernel<D, HW, true, true>), grid, dim3(256), 0, st, a);
+  else if (a.causal)
+    hipLaunchKernelGGL((prefill_kernel<D, HW, true, false>), grid, dim3(256), 0, st, a);
+  else if (big)
+    hipLaunchKernelGGL((prefill_kernel<D, HW, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, HW, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, HW, false, false>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
