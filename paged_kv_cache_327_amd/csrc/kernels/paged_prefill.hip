@@ -45,6 +45,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKeys = 64;        // keys per tile
 constexpr int kQ = 32;           // queries per wave
 constexpr int kXcds = 8;         // accelerator dies of an MI355X, one L2 each
+constexpr int kSortMax = 256;    // requests ordered by work up to this many
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kSlack = 8.0f;
 
@@ -91,9 +92,39 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const int xcd = blockIdx.x & (kXcds - 1), k_in_xcd = blockIdx.x / kXcds;
   const int grp = xcd + kXcds * (k_in_xcd / X);
   if (grp >= a.num_seqs * Y) return;
-  const int i = grp / Y, y = grp % Y;         // request, head group
+  const int y = grp % Y;                      // head group
   const int xt = k_in_xcd % X;                // 0 = the request's last (heaviest) query tile
   const int tid = threadIdx.x, lane = tid & 63;
+
+  // Requests are taken in order of decreasing work, q_len (2 kv_len - q_len)
+  // (twice the visible query-key pairs), ties in index order, so that the
+  // longest start first and the work-groups of an XCD finish together.  The
+  // rank is found by counting; with more than kSortMax requests the index
+  // order is kept.
+  int i = grp / Y;
+  if (a.num_seqs > 1 && a.num_seqs <= kSortMax) {
+    __shared__ int64_t s_cost[kSortMax];
+    __shared__ int s_req;
+    for (int c = tid; c < a.num_seqs; c += 256) {
+      const int ql = a.query_start_loc[c + 1] - a.query_start_loc[c];
+      int kv = a.seq_lens[c];
+      kv = kv > a.max_seq_len ? a.max_seq_len : kv;
+      s_cost[c] = ql > 0 && kv >= ql ? (int64_t)ql * (2 * (int64_t)kv - ql) : 0;
+    }
+    __syncthreads();
+    const int rank = i;
+    for (int c = tid; c < a.num_seqs; c += 256) {
+      const int64_t mine = s_cost[c];
+      int r = 0;
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const int64_t o = s_cost[j];
+        r += (o > mine) | ((o == mine) & (j < c));
+      }
+      if (r == rank) s_req = c;
+    }
+    __syncthreads();
+    i = s_req;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, col = lane & 31;
 
