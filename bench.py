@@ -214,35 +214,41 @@ def measure_prefill(torch, B, hip_side, workloads, block_size=16, reps=10):
 
     def launch():
         B.pa_paged_prefill(out, q, h.kc, h.vc, h.table_dev, qsl, h.seq_lens_dev, max(wl.q_lens), msl, wl.scale)
-    launch()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        launch()
-    e1.record()
-    torch.cuda.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / reps
+    sec = time_launches(torch, launch, reps)
     flops = prefill_flops(wl.q_lens, wl.seq_lens, wl.num_q_heads, wl.head_dim)
     return {"workload": "16 prefill chunks of 512 queries over U{0..8192} context tokens",
-            "block_size": block_size, "kernel": "prefill_kernel<128, 4, true>",
+            "block_size": block_size, "kernel": "prefill_kernel<128, 4, true, true>",
             "us": round(sec * 1e6, 1), "gflop": round(flops / 1e9, 2),
             "tflops": round(flops / sec / 1e12, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def time_launches(torch, fn, reps):
-    """Seconds per call of fn (one or more launches on the current stream),
-    from one pair of HIP events around reps back-to-back calls."""
-    fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / reps
+def warm_clocks(torch, fn, seconds=0.3):
+    """Keep the GPU busy with fn for about `seconds` so that its clocks have
+    left their idle state before a measurement (a cold MI355X runs the first
+    tens of milliseconds of work markedly slower)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_launches(torch, fn, reps, windows=3):
+    """Seconds per call of fn (one or more launches on the current stream):
+    the median over `windows` of one pair of HIP events around reps
+    back-to-back calls, after a clock warm-up with the same calls."""
+    warm_clocks(torch, fn)
+    per = []
+    for _ in range(windows):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return sorted(per)[len(per) // 2]
 
 
 def hbm(gbps):
@@ -290,6 +296,19 @@ def measure_long_context(torch, B, hip_side, workloads, reps=3):
            "step_ms": round(sec * 1e3, 3), "layer_us": round(sec / L * 1e6, 1),
            "bytes_per_layer": per_layer, "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
            "seqs_per_s": round(S / sec, 1)}
+    # the same step with partitions of 2048 tokens (fewer, longer work-groups)
+    P2 = 2048
+    ws2 = torch.empty(B.pa_paged_decode_workspace_size(S, wl.num_q_heads, wl.head_dim, msl, P2),
+                      dtype=torch.uint8, device="cuda")
+
+    def step2():
+        for l in range(L):
+            B.pa_paged_decode(out, qs[l], kv[l, 0], kv[l, 1], h.table_dev, h.seq_lens_dev, msl, wl.scale,
+                              partition_size=P2, workspace=ws2)
+    sec2 = time_launches(torch, step2, reps)
+    res[f"partition_{P2}"] = {"step_ms": round(sec2 * 1e3, 3), "layer_us": round(sec2 / L * 1e6, 1),
+                              "gbps": round(per_layer * L / sec2 / 1e9, 1),
+                              "hbm_frac": hbm(per_layer * L / sec2 / 1e9), "seqs_per_s": round(S / sec2, 1)}
     del kv, h, qs
     torch.cuda.empty_cache()
     return res
@@ -353,8 +372,9 @@ def measure_prefix_cow(torch, B, hip_side, workloads, reps=20):
 def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
     """The mixed step at one block size: writes of the step's 8,432 new
     tokens, prefill of 16 chunks of 512 queries, decode of 240 sequences
-    (partitions of 512 tokens), on one stream; each call timed alone and the
+    (partitions of 2048 tokens), on one stream; each call timed alone and the
     three together."""
+    P = 2048
     wl = workloads.mixed_step(block_size)
     h = hip_side.HipStep(wl, gen="device")
     chunks = [s for s in range(wl.num_seqs) if wl.q_lens[s] > 1]
@@ -376,7 +396,7 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
     sl_d = h.seq_lens_dev[dec].contiguous()
     dl = [wl.seq_lens[s] for s in dec]
     msl_d = int(max(dl))
-    ws = torch.empty(B.pa_paged_decode_workspace_size(len(dec), wl.num_q_heads, wl.head_dim, msl_d, 512),
+    ws = torch.empty(B.pa_paged_decode_workspace_size(len(dec), wl.num_q_heads, wl.head_dim, msl_d, P),
                      dtype=torch.uint8, device="cuda")
     # the timed writes go to scratch copies of the caches: same slots, same bytes
     kc2, vc2 = h.kc.clone(), h.vc.clone()
@@ -388,7 +408,7 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
         B.pa_paged_prefill(op, qp, h.kc, h.vc, bt_p, qsl, sl_p, max(wl.q_lens), msl_p, wl.scale)
 
     def decode():
-        B.pa_paged_decode(od, qd, h.kc, h.vc, bt_d, sl_d, msl_d, wl.scale, partition_size=512, workspace=ws)
+        B.pa_paged_decode(od, qd, h.kc, h.vc, bt_d, sl_d, msl_d, wl.scale, partition_size=P, workspace=ws)
 
     def step():
         reshape()
@@ -402,7 +422,7 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
                           wl.head_dim)
     db = decode_bytes(dl, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, block_size)
     rb = 2 * T * wl.num_kv_heads * wl.head_dim * 2 * 2
-    res = {"block_size": block_size, "step_ms": round(t_s * 1e3, 3), "tokens_written": T,
+    res = {"block_size": block_size, "decode_partition_size": P, "step_ms": round(t_s * 1e3, 3), "tokens_written": T,
            "reshape_us": round(t_r * 1e6, 2), "reshape_gbps": round(rb / t_r / 1e9, 1),
            "prefill_us": round(t_p * 1e6, 1), "prefill_gflop": round(flops / 1e9, 2),
            "prefill_tflops": round(flops / t_p / 1e12, 1),
@@ -491,9 +511,12 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, len(insts))):    # every pool staged at least once
         run_step(insts[i % len(insts)], B, stream)
     torch.cuda.synchronize()
+    # bring the clocks up with decode launches on the staged pools (they leave
+    # the pools unchanged)
+    warm_clocks(torch, lambda: [inst.decode(stream) for inst in insts], 0.5)
     print("[bench] warm-up done", file=sys.stderr, flush=True)
 
     # whole-step throughput
@@ -507,20 +530,17 @@ def main():
     print("[bench] timed steps done", file=sys.stderr, flush=True)
 
     # dominant kernel: back-to-back decode launches on the same stream,
-    # rotating over the pools, bracketed by one pair of HIP events (an event
-    # between launches adds its own cost to every launch)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    insts[0].decode(stream)
-    torch.cuda.synchronize()
-    e0.record()
-    for k in range(args.kernel_reps):
-        insts[k % len(insts)].decode(stream)
-    e1.record()
-    torch.cuda.synchronize()
-    dec_s = e0.elapsed_time(e1) / 1e3 / args.kernel_reps
+    # rotating over the pools, bracketed by one pair of HIP events per window
+    # (an event between launches adds its own cost to every launch)
+    rot = [0]
+
+    def decode_next():
+        insts[rot[0] % len(insts)].decode(stream)
+        rot[0] += 1
+    dec_s = time_launches(torch, decode_next, args.kernel_reps)
     cur_lens = [np.array(i.h_lens) for i in insts]
-    alg_per_launch = np.mean([decode_bytes(cur_lens[k % len(insts)], wl.num_q_heads, wl.num_kv_heads,
-                                           wl.head_dim, wl.block_size) for k in range(args.kernel_reps)])
+    alg_per_launch = np.mean([decode_bytes(cur_lens[k], wl.num_q_heads, wl.num_kv_heads,
+                                           wl.head_dim, wl.block_size) for k in range(len(insts))])
     achieved = alg_per_launch / dec_s / 1e9
 
     ms_per_step = elapsed / args.steps * 1e3

@@ -44,6 +44,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;     // tokens per wave iteration
+constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
 constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
@@ -136,11 +137,26 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   };
   if (!BIG) stage_table(start);
+  // BIG: the table entries of this wave's first two tiles and of the
+  // partition's first token, fetched before the length is known (indexes
+  // are kept inside the row), so that the first K/V loads wait for one
+  // round trip instead of two.
+  int pre0 = 0, pre1 = 0, pre_start = 0;
+  if constexpr (BIG) {
+    const int wmax = width - 1;
+    const int tw = start + wave * kTile;
+    const int i0 = tw >> lgB, i1 = (tw + kWaves * kTile) >> lgB, is = start >> lgB;
+    pre0 = bt_row[i0 < wmax ? i0 : wmax];
+    pre1 = bt_row[i1 < wmax ? i1 : wmax];
+    pre_start = bt_row[is < wmax ? is : wmax];
+  }
 
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  const int nparts = len > 0 ? (len + P - 1) / P : 1;
-  if (part >= nparts) return;
-  const int end = start + P < len ? start + P : len;
+  // A partition past the sequence's last one gets an empty range and returns
+  // before the merge; there is no early exit here, which would let the
+  // compiler move the table loads above behind it.
+  const bool live = part * P < len || part == 0;
+  const int end = !live ? start : (start + P < len ? start + P : len);
 
   // per-lane constant part of a K/V element offset (BIG: tokens grp, grp + 8
   // of the tile relative to its first token)
@@ -159,27 +175,20 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][k][i] = 0.f;
 
-  const int chunk = BIG ? P : kChunk;
-  for (int c0 = start; c0 < end; c0 += chunk) {
-    const int c1 = c0 + chunk < end ? c0 + chunk : end;
-    const int j0 = c0 >> lgB;
-    if (!BIG) {
-      if (c0 != start) {
-        __syncthreads();
-        stage_table(c0);
-      }
-      __syncthreads();
-    }
+  // Tokens c0 .. c1 - 1 (B < 16: their table entries are in LDS from j0 on).
+  auto range = [&](const int c0, const int c1, const int j0) __attribute__((always_inline)) {
 
     // Tokens past c1 read token c0 (always valid), so every load stays inside
     // the cache and can be issued unconditionally: with no branch around the
     // prefetches the compiler's wait counts stay exact and the next tiles'
     // loads remain in flight while this one is computed.  All K loads are
     // issued before the V loads so q.k can start first.
-    auto load = [&](int t0, KV<D>& r) {
+    // (with `fetched`, the block id is `pre`, fetched early for tile t0, or
+    // pre_start for a tile past c1)
+    auto load = [&](int t0, KV<D>& r, bool fetched = false, int pre = 0) __attribute__((always_inline)) {
       if (BIG) {
         const int tc = t0 < c1 ? t0 : c0;          // wave-uniform
-        int blk = __builtin_amdgcn_readfirstlane(bt_row[tc >> lgB]);
+        int blk = __builtin_amdgcn_readfirstlane(fetched ? (t0 < c1 ? pre : pre_start) : bt_row[tc >> lgB]);
         blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
         const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
         const uint16_t* kb = kcache + base;
@@ -217,7 +226,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       }
     };
 
-    auto compute = [&](int t0, const KV<D>& r) {
+    auto compute = [&](int t0, const KV<D>& r) __attribute__((always_inline)) {
       const bool valid0 = t0 + grp < c1;
       const bool valid1 = t0 + grp + 8 < c1;
       // partial dots: slot v of set j is head 4 j + v / 2, token v % 2
@@ -303,35 +312,50 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       }
     };
 
-    // Three register buffers: while tile t is computed, tiles t + 64 and
-    // t + 128 are in flight.  The loop runs whole triples and has a single,
-    // bottom-tested exit (an exit in the middle gives the compiler a path
-    // back into the loop with loads pending, and it then drains every load
-    // at the top); the last 0-2 tiles are computed after it from buffers
-    // already loaded.  All branches here are wave-uniform.
+    // kBuffers register buffers: while tile t is computed, the next
+    // kBuffers - 1 tiles of the wave are in flight.  The loop runs whole
+    // rounds of kBuffers tiles and has a single, bottom-tested exit (an exit
+    // in the middle gives the compiler a path back into the loop with loads
+    // pending, and it then drains every load at the top); the last tiles are
+    // computed after it from buffers already loaded.  All branches here are
+    // wave-uniform.  The first loads are issued whatever n_tiles is (they
+    // stay inside the cache), so nothing delays them.
     constexpr int kStep = kWaves * kTile;
     int t = c0 + wave * kTile;
     const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
-    if (n_tiles > 0) {
-      KV<D> r0, r1, r2;
-      load(t, r0);
-      load(t + kStep, r1);
-      int i = 0;
-      for (; i + 3 <= n_tiles; i += 3) {
-        load(t + 2 * kStep, r2);
-        compute(t, r0);
-        t += kStep;
-        load(t + 2 * kStep, r0);
-        compute(t, r1);
-        t += kStep;
-        load(t + 2 * kStep, r1);
-        compute(t, r2);
+    KV<D> r[kBuffers];
+#pragma unroll
+    for (int k = 0; k + 1 < kBuffers; ++k) load(t + k * kStep, r[k], BIG && k < 2, k == 0 ? pre0 : pre1);
+    int i = 0;
+    for (; i + kBuffers <= n_tiles; i += kBuffers) {
+#pragma unroll
+      for (int k = 0; k < kBuffers; ++k) {
+        load(t + (kBuffers - 1) * kStep, r[(k + kBuffers - 1) % kBuffers]);
+        compute(t, r[k]);
         t += kStep;
       }
-      if (n_tiles - i >= 1) compute(t, r0);
-      if (n_tiles - i >= 2) compute(t + kStep, r1);
+    }
+#pragma unroll
+    for (int k = 0; k + 1 < kBuffers; ++k)
+      if (n_tiles - i > k) compute(t + k * kStep, r[k]);
+  };
+  if constexpr (BIG) {
+    // one range: no outer loop, whose header would drain the query loads
+    // before the first K/V loads are issued
+    range(start, end, start >> lgB);
+  } else {
+    for (int c0 = start; c0 < end; c0 += kChunk) {
+      if (c0 != start) {
+        __syncthreads();
+        stage_table(c0);
+      }
+      __syncthreads();
+      range(c0, c0 + kChunk < end ? c0 + kChunk : end, c0 >> lgB);
     }
   }
+
+  if (!live) return;
+  const int nparts = len > 0 ? (len + P - 1) / P : 1;
 
   // Merge.  All lane groups of a wave share the running maxima, so their
   // partial sums add directly: the two groups of a row with DPP, the four
