@@ -144,3 +144,32 @@ def test_long_context_32_layer_pool():
             assert torch.isfinite(out.float()).all()
     del kv, layers, h
     torch.cuda.empty_cache()
+
+
+def test_split_workspace_reuse_is_deterministic():
+    """A split-K call reused with the same workspace, call after call, gives
+    the same complete result each time (the partials are rewritten, nothing
+    carries over), for a batch with more work items than fit on the device."""
+    from paged_kv_cache_327_amd import binding as B
+    lens = [5, 700, 3000, 64, 1025, 1, 2049, 333] * 12
+    wl = workloads.custom("workspace_reuse", 46, 32, 8, 128, 16, lens)
+    h, o = HipStep(wl), OracleStep(wl)
+    q = decode_queries(wl)
+    msl = max(lens)
+    need = B.pa_paged_decode_workspace_size(len(lens), 32, 128, msl, 128)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")     # garbage on entry
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    want, want_lse = attention.paged_decode(q, o.kc, o.vc, o.table, o.seq_lens, wl.scale)
+    first = None
+    for rep in range(3):
+        out = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda")
+        B.pa_paged_decode(out, qd, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale,
+                          partition_size=128, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+            assert_attention_close(out, want, what="workspace reuse")
+            assert_lse_close(lse, want_lse)
+        else:
+            assert torch.equal(out, first)
