@@ -16,7 +16,8 @@ Sources (the three web pages on PagedAttention):
 Modules
   sizing      closed forms of the pages' capacity arithmetic
   pool_model  the host block pool (free queue, refcounts, tables, CoW)
-  cache_ops   the slot scatter and the whole-block copy
+  cache_ops   the slot mapping from the block table, the slot scatter and the
+              whole-block copy
   attention   fp64 decode and chunked-prefill attention by table gather
 
 Every floating-point result is computed in fp64 from exact bf16 inputs.

@@ -9,6 +9,40 @@ from __future__ import annotations
 import numpy as np
 
 
+PAD_SLOT = -1
+
+
+def slot_mapping(block_tables: np.ndarray, query_start_loc, seq_lens, block_size: int,
+                 num_tokens: int) -> np.ndarray:
+    """Slots of a step's new tokens, from the block table.
+
+    "PagedAttention: fragmentation, blocks, block tables", 3. The slot
+    mapping: with one context-parallel rank the kernel's arithmetic reduces
+    to slot = block_table[req][pos // B] * B + pos % B, and positions that
+    have no slot get the padding id.  Request i's step tokens are rows
+    query_start_loc[i] .. query_start_loc[i+1]-1 and are the last q_i of its
+    seq_lens[i] positions (the attention-metadata section).
+
+    Readings: rows past query_start_loc[-1] (padding up to num_tokens), a
+    position below 0 and a table index past the row get the padding id -1.
+    """
+    bt = np.asarray(block_tables)
+    qsl = [int(x) for x in query_start_loc]
+    out = np.full(num_tokens, PAD_SLOT, dtype=np.int64)
+    for i in range(len(qsl) - 1):
+        q = qsl[i + 1] - qsl[i]
+        first = int(seq_lens[i]) - q
+        for j in range(q):
+            t = qsl[i] + j
+            if t >= num_tokens:
+                break
+            pos = first + j
+            if pos < 0 or pos // block_size >= bt.shape[1]:
+                continue
+            out[t] = int(bt[i, pos // block_size]) * block_size + pos % block_size
+    return out
+
+
 def reshape_and_cache(key_cache: np.ndarray, value_cache: np.ndarray,
                       key: np.ndarray, value: np.ndarray,
                       slot_mapping: np.ndarray) -> None:

@@ -78,3 +78,59 @@ def test_copy_blocks_writes_through_strided_block_views():
     expect[[4, 5], :8] = base[[0, 2], :8]
     cache_ops.copy_blocks([view], [(0, 4), (2, 5)], 6)
     assert np.array_equal(base, expect)
+
+
+def test_slot_mapping_worked_example(golden):
+    """The pages' worked step: request r7 at position 4096 with block 1913
+    as entry 256 of its row writes slot 30,608."""
+    w = golden["r7_walk"]["printed"]
+    B = w["block_size"]
+    bt = np.zeros((4, w["row_len_after"]), dtype=np.int32)
+    bt[3, w["pos"] // B] = w["popped_block"]
+    # four requests, only r7 (row 3) has one new token at its last position
+    qsl = [0, 0, 0, 0, 1]
+    lens = [0, 0, 0, w["pos"] + 1]
+    got = cache_ops.slot_mapping(bt, qsl, lens, B, num_tokens=3)
+    assert got.tolist() == [w["slot"], -1, -1]
+
+
+def test_slot_mapping_agrees_with_the_pool_appends():
+    """Appends through the pool model emit slots on the host; recomputing
+    them from the block table afterwards must give the same numbers, for
+    block sizes 1, 4 and 16, ragged chunks and requests with no new tokens."""
+    rng = np.random.default_rng(12)
+    for B in (1, 4, 16):
+        nb = 4096 // B
+        pool = PoolModel(nb, B, rng.permutation(nb))
+        ctx = rng.integers(0, 300, 9)
+        new = rng.integers(0, 40, 9)
+        new[3] = 0
+        for s, c in enumerate(ctx):
+            pool.add_seq(s)
+            if c:
+                pool.append(s, int(c))
+        want = []
+        for s, n in enumerate(new):
+            if n:
+                slots, _ = pool.append(s, int(n))
+                want.extend(slots)
+        qsl = np.concatenate([[0], np.cumsum(new)])
+        lens = (ctx + new).tolist()
+        width = max(len(pool.block_table(s)) for s in range(9))
+        bt = np.zeros((9, width + 2), dtype=np.int32)
+        for s in range(9):
+            row = pool.block_table(s)
+            bt[s, :len(row)] = row
+        got = cache_ops.slot_mapping(bt, qsl, lens, B, num_tokens=int(qsl[-1]) + 5)
+        assert got[:qsl[-1]].tolist() == want
+        assert (got[qsl[-1]:] == -1).all()
+
+
+def test_slot_mapping_padding_ids():
+    """Negative positions (more new tokens than the sequence holds) and
+    table indexes past the row get the padding id."""
+    bt = np.array([[7, 9]], dtype=np.int32)
+    got = cache_ops.slot_mapping(bt, [0, 3], [2], 4, num_tokens=3)
+    assert got.tolist() == [-1, 28, 29]
+    got = cache_ops.slot_mapping(bt, [0, 2], [10], 4, num_tokens=2)
+    assert got.tolist() == [-1, -1]          # positions 8, 9 -> table index 2, past the row
