@@ -370,10 +370,10 @@ def measure_prefix_cow(torch, B, hip_side, workloads, reps=20):
 
 
 def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
-    """The mixed step at one block size: writes of the step's 8,432 new
-    tokens, prefill of 16 chunks of 512 queries, decode of 240 sequences
-    (partitions of 2048 tokens), on one stream; each call timed alone and the
-    three together."""
+    """The mixed step at one block size: the step's slots from the block
+    table, writes of its 8,432 new tokens, prefill of 16 chunks of 512
+    queries, decode of 240 sequences (partitions of 2048 tokens), on one
+    stream; each call timed alone and the four together."""
     P = 2048
     wl = workloads.mixed_step(block_size)
     h = hip_side.HipStep(wl, gen="device")
@@ -382,7 +382,6 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
     seqs = h.step_seqs
     T = int(sum(wl.new_lens[s] for s in seqs))
     kn = workloads.device_query(wl.seed, T, wl.num_kv_heads, wl.head_dim, layer=3)
-    slots = torch.from_numpy(np.asarray(h.step_slots, dtype=np.int64)).cuda()
     qp = workloads.device_query(wl.seed, int(sum(wl.q_lens[s] for s in chunks)), wl.num_q_heads, wl.head_dim)
     op = torch.empty_like(qp)
     qsl = torch.tensor(np.concatenate([[0], np.cumsum([wl.q_lens[s] for s in chunks])]), dtype=torch.int32,
@@ -400,9 +399,17 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
                      dtype=torch.uint8, device="cuda")
     # the timed writes go to scratch copies of the caches: same slots, same bytes
     kc2, vc2 = h.kc.clone(), h.vc.clone()
+    # the step's slots computed on the device from the block table (they equal
+    # the host pool's, checked by the tests)
+    qsl_all = torch.tensor(np.concatenate([[0], np.cumsum([wl.new_lens[s] for s in range(wl.num_seqs)])]),
+                           dtype=torch.int32, device="cuda")
+    dslots = torch.empty(T, dtype=torch.int64, device="cuda")
+
+    def slot_mapping():
+        B.pa_slot_mapping(h.table_dev, qsl_all, h.seq_lens_dev, block_size, T, out=dslots)
 
     def reshape():
-        B.pa_reshape_and_cache(kn, kn, kc2, vc2, slots)
+        B.pa_reshape_and_cache(kn, kn, kc2, vc2, dslots)
 
     def prefill():
         B.pa_paged_prefill(op, qp, h.kc, h.vc, bt_p, qsl, sl_p, max(wl.q_lens), msl_p, wl.scale)
@@ -411,9 +418,12 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
         B.pa_paged_decode(od, qd, h.kc, h.vc, bt_d, sl_d, msl_d, wl.scale, partition_size=P, workspace=ws)
 
     def step():
+        slot_mapping()
         reshape()
         prefill()
         decode()
+    slot_mapping()
+    t_m = time_launches(torch, slot_mapping, reps)
     t_r = time_launches(torch, reshape, reps)
     t_p = time_launches(torch, prefill, reps)
     t_d = time_launches(torch, decode, reps)
@@ -423,6 +433,7 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
     db = decode_bytes(dl, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, block_size)
     rb = 2 * T * wl.num_kv_heads * wl.head_dim * 2 * 2
     res = {"block_size": block_size, "decode_partition_size": P, "step_ms": round(t_s * 1e3, 3), "tokens_written": T,
+           "slot_mapping_us": round(t_m * 1e6, 2),
            "reshape_us": round(t_r * 1e6, 2), "reshape_gbps": round(rb / t_r / 1e9, 1),
            "prefill_us": round(t_p * 1e6, 1), "prefill_gflop": round(flops / 1e9, 2),
            "prefill_tflops": round(flops / t_p / 1e12, 1),

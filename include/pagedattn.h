@@ -172,6 +172,29 @@ int64_t pa_blocks_for_bytes(int64_t pool_bytes, int64_t bytes_per_token, int32_t
 /* Device calls (gfx950), asynchronous on `stream`                           */
 /* ------------------------------------------------------------------------ */
 
+/* Compute the step's slot mapping on the device from the block table.
+ * Request i owns step tokens query_start_loc[i] .. query_start_loc[i+1]-1,
+ * the last q_i = query_start_loc[i+1] - query_start_loc[i] of its
+ * seq_lens[i] positions: token query_start_loc[i] + j sits at position
+ * p = seq_lens[i] - q_i + j and gets
+ *   slot_mapping[query_start_loc[i] + j] = block_tables[i][p / B] * B + p % B.
+ * Tokens from query_start_loc[num_seqs] up to num_tokens (padding), a
+ * negative p and p / B >= bt_stride get the padding id -1.
+ * ("PagedAttention: fragmentation, blocks, block tables", 3. The slot mapping:
+ * with one context-parallel rank the slot kernel reduces to this formula;
+ * attention-metadata section for query_start_loc and seq_lens.)
+ * slot_mapping: device int64 [num_tokens] (written).  block_tables: device
+ * int32, row i at block_tables + i * bt_stride.  query_start_loc: device int32
+ * [num_seqs + 1], non-decreasing, query_start_loc[num_seqs] <= num_tokens is
+ * not required (tokens past num_tokens are not written).  seq_lens: device
+ * int32 [num_seqs].  block_size: power of two <= 256.
+ * Errors: PA_ERR_INVALID for NULL pointers, negative counts, bt_stride < 1 or
+ * a bad block_size.  Integer work, bit-exact. */
+int pa_slot_mapping(int64_t* slot_mapping, int32_t num_tokens,
+                    const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* query_start_loc, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t block_size, void* stream);
+
 /* Store each new token's K and V rows at its slot: row t of key/value
  * ([num_tokens][num_kv_heads][head_dim] bf16, consecutive tokens
  * key_row_stride / value_row_stride elements apart, heads contiguous) goes to

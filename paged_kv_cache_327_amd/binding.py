@@ -59,6 +59,7 @@ _SIGS = {
     "pa_pool_free_order": (c_i32, [c_vp, P_i32, c_i32, P_i32]),
     "pa_pool_check": (c_i32, [c_vp]),
     "pa_blocks_for_bytes": (c_i64, [c_i64, c_i64, c_i32]),
+    "pa_slot_mapping": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "pa_reshape_and_cache": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp,
                                      c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_i32, P_i32, c_i32, c_vp]),
@@ -254,6 +255,30 @@ def _cache_geometry(kc, vc):
     if kc.stride()[1:] != (hkv * d, d, 1):
         raise InvalidArgument(PA_ERR_INVALID, "cache blocks must be contiguous [B, Hkv, D]")
     return nb, bs, hkv, d, kc.stride(0)
+
+
+def pa_slot_mapping(block_tables, query_start_loc, seq_lens, block_size, num_tokens, out=None, stream=None):
+    """Slots of a step's tokens computed on the device: block_tables int32
+    [S, W] (unit column stride), query_start_loc int32 [S+1], seq_lens int32
+    [S], all device tensors; returns (or fills) an int64 device tensor
+    [num_tokens]."""
+    import torch
+    S = seq_lens.shape[0]
+    for t, name in ((block_tables, "block_tables"), (query_start_loc, "query_start_loc"), (seq_lens, "seq_lens")):
+        if t.dtype != torch.int32 or not t.is_cuda:
+            raise InvalidArgument(PA_ERR_INVALID, f"{name} must be an int32 device tensor")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or block_tables.stride(1) != 1 \
+            or query_start_loc.shape != (S + 1,) or not query_start_loc.is_contiguous() \
+            or not seq_lens.is_contiguous():
+        raise InvalidArgument(PA_ERR_INVALID, "need block_tables [S, W], query_start_loc [S+1], seq_lens [S]")
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=seq_lens.device)
+    elif out.dtype != torch.int64 or out.shape != (num_tokens,) or not out.is_contiguous() or not out.is_cuda:
+        raise InvalidArgument(PA_ERR_INVALID, "out must be a contiguous int64 device tensor [num_tokens]")
+    _check(lib().pa_slot_mapping(out.data_ptr(), num_tokens, block_tables.data_ptr(), block_tables.stride(0),
+                                 query_start_loc.data_ptr(), seq_lens.data_ptr(), S, block_size,
+                                 _stream(seq_lens, stream)))
+    return out
 
 
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):

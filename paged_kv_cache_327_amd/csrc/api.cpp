@@ -71,6 +71,23 @@ extern "C" {
 
 const char* pa_last_error(void) { return pa::g_error.c_str(); }
 
+int pa_slot_mapping(int64_t* slot_mapping, int32_t num_tokens, const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t block_size,
+                    void* stream) {
+  pa::clear_error();
+  const char* fn = "slot_mapping";
+  if (num_tokens < 0 || num_seqs < 0) return pa::fail(PA_ERR_INVALID, "%s: negative count", fn);
+  if (block_size < 1 || block_size > 256 || (block_size & (block_size - 1)))
+    return pa::fail(PA_ERR_INVALID, "%s: block_size %d must be a power of two <= 256", fn, block_size);
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || (num_seqs > 0 && (!block_tables || !query_start_loc || !seq_lens)))
+    return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (num_seqs > 0 && bt_stride < 1) return pa::fail(PA_ERR_INVALID, "%s: bt_stride %d < 1", fn, bt_stride);
+  pa::SlotArgs a{slot_mapping, num_tokens, block_tables, bt_stride, query_start_loc, seq_lens, num_seqs,
+                 ilog2(block_size)};
+  return hip_status(fn, pa::launch_slot_mapping(a, stream));
+}
+
 int pa_reshape_and_cache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
                          void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

@@ -29,6 +29,18 @@ struct ReshapeArgs {
 };
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream);
 
+struct SlotArgs {
+  int64_t* slot_mapping;
+  int32_t num_tokens;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t log2_block_size;
+};
+int launch_slot_mapping(const SlotArgs& a, void* stream);
+
 int launch_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes,
                        int64_t stride_bytes, const int32_t* pairs, int32_t n_pairs,
                        void* stream);

@@ -1,7 +1,9 @@
-// KV-cache write by slot mapping and whole-block copy-on-write copies.
+// Slot mapping, KV-cache write by slot mapping and whole-block copy-on-write
+// copies.
 //
-// Both kernels move bits with 16-byte vector loads and stores and are bound
-// by HBM bandwidth.
+// The write and the copy move bits with 16-byte vector loads and stores and
+// are bound by HBM bandwidth; the slot mapping is integer work on a few
+// thousand tokens.
 #include "../internal.hpp"
 #include "common.hpp"
 
@@ -33,6 +35,34 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
     kd[c] = k;
     vd[c] = v;
   }
+}
+
+// One thread per step token.  Its request is the last i with
+// query_start_loc[i] <= t (binary search over the num_seqs + 1 entries; the
+// loop is bounded by log2 of that count even if the entries are not sorted,
+// and every index stays inside the arrays).  "PagedAttention: fragmentation,
+// blocks, block tables", 3. The slot mapping: slot = table[req][pos / B] * B +
+// pos % B, the padding id for tokens without a slot.
+__global__ void __launch_bounds__(256) slot_mapping_kernel(SlotArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.num_tokens) return;
+  int64_t slot = -1;
+  if (a.num_seqs > 0 && t >= a.query_start_loc[0] && t < a.query_start_loc[a.num_seqs]) {
+    int lo = 0, hi = a.num_seqs;             // query_start_loc[lo] <= t, search (lo, hi)
+    while (hi - lo > 1) {
+      const int mid = lo + ((hi - lo) >> 1);
+      if (a.query_start_loc[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int q0 = a.query_start_loc[lo];
+    const int q = a.query_start_loc[lo + 1] - q0;
+    const int64_t pos = (int64_t)a.seq_lens[lo] - q + (t - q0);
+    const int64_t j = pos >> a.log2_block_size;
+    if (pos >= 0 && j < a.bt_stride) {
+      const int64_t blk = a.block_tables[(int64_t)lo * a.bt_stride + j];
+      slot = (blk << a.log2_block_size) + (pos & ((int64_t{1} << a.log2_block_size) - 1));
+    }
+  }
+  a.slot_mapping[t] = slot;
 }
 
 constexpr int kMaxCopyCaches = 64;
@@ -78,6 +108,12 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyBatch b) {
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
   const unsigned grid = (unsigned)((a.num_tokens + 3) / 4);
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_slot_mapping(const SlotArgs& a, void* stream) {
+  const unsigned grid = (unsigned)((a.num_tokens + 255) / 256);
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

@@ -164,6 +164,13 @@ def test_device_calls_validate_on_host():
     # zero tokens is a no-op that touches nothing
     assert L.pa_reshape_and_cache(None, 128, None, 128, _vp(fake), _vp(fake), 16 * 128, 4, None,
                                   0, 1, 128, 16, None) == B.PA_OK
+    # slot mapping: block size not a power of two, negative counts, NULL
+    # inputs, a table stride below 1; zero tokens is a no-op
+    assert L.pa_slot_mapping(_vp(fake), 4, _vp(fake), 8, _vp(fake), _vp(fake), 2, 12, None) == B.PA_ERR_INVALID
+    assert L.pa_slot_mapping(_vp(fake), -1, _vp(fake), 8, _vp(fake), _vp(fake), 2, 16, None) == B.PA_ERR_INVALID
+    assert L.pa_slot_mapping(_vp(fake), 4, None, 8, _vp(fake), _vp(fake), 2, 16, None) == B.PA_ERR_INVALID
+    assert L.pa_slot_mapping(_vp(fake), 4, _vp(fake), 0, _vp(fake), _vp(fake), 2, 16, None) == B.PA_ERR_INVALID
+    assert L.pa_slot_mapping(None, 0, None, 0, None, None, 0, 16, None) == B.PA_OK
     # copy pairs: duplicate destination, and a destination that is a source
     ptrs = (ctypes.c_void_p * 1)(fake)
     for pairs in ([0, 1, 2, 1], [0, 1, 1, 2], [0, 9]):

@@ -98,3 +98,42 @@ def test_copy_blocks_rejects_bad_pairs():
         B.pa_copy_blocks([t], [(0, 4)])
     B.pa_copy_blocks([t], np.zeros((0, 2)))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("block_size", [1, 16, 32])
+def test_slot_mapping_matches_the_pool(block_size):
+    """The mixed step at full size (16 chunks of 512 and 240 decode tokens,
+    2^20-slot pool): slots computed on the device from the block table equal,
+    bit for bit, the slots the host pool emitted when it appended the step's
+    tokens, and the oracle's formula."""
+    wl = workloads.mixed_step(block_size)
+    print(f"[slots] {wl.name}", flush=True)
+    h = HipStep(wl, gen="device")
+    qsl = np.concatenate([[0], np.cumsum(wl.new_lens)]).astype(np.int32)
+    T = int(qsl[-1])
+    got = B.pa_slot_mapping(h.table_dev, torch.from_numpy(qsl).cuda(), h.seq_lens_dev, block_size, T + 37)
+    got = got.cpu().numpy()
+    assert np.array_equal(got[:T], np.asarray(h.step_slots, dtype=np.int64))
+    assert (got[T:] == -1).all()
+    want = cache_ops.slot_mapping(h.table, qsl, h.seq_lens, block_size, T + 37)
+    assert np.array_equal(got, want)
+
+
+def test_slot_mapping_edge_cases_match_oracle():
+    """Empty requests, a first request offset into the token array, more new
+    tokens than a sequence holds (negative positions), table indexes past the
+    row, and padding rows; random tables, B = 4."""
+    rng = np.random.default_rng(5)
+    S, W, Bs = 11, 6, 4
+    bt = rng.integers(0, 500, size=(S, W)).astype(np.int32)
+    q = rng.integers(0, 9, size=S)
+    q[[2, 7]] = 0
+    qsl = np.concatenate([[3], 3 + np.cumsum(q)]).astype(np.int32)
+    lens = rng.integers(0, W * Bs + 6, size=S).astype(np.int32)
+    lens[4] = 1                                   # fewer positions than new tokens
+    T = int(qsl[-1]) + 5
+    got = B.pa_slot_mapping(torch.from_numpy(bt).cuda(), torch.from_numpy(qsl).cuda(),
+                            torch.from_numpy(lens).cuda(), Bs, T).cpu().numpy()
+    want = cache_ops.slot_mapping(bt, qsl, lens, Bs, T)
+    assert np.array_equal(got, want)
+    assert (got == -1).any() and (got >= 0).any()
