@@ -422,17 +422,35 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
         reshape()
         prefill()
         decode()
+
+    # the same step with the decode on a second stream (default priority):
+    # the HBM-bound decode can use compute units the MFMA-bound prefill leaves
+    # idle; both wait for the cache writes
+    side = torch.cuda.Stream()
+    written = torch.cuda.Event()
+
+    def step_two_streams():
+        slot_mapping()
+        reshape()
+        written.record()
+        side.wait_event(written)
+        with torch.cuda.stream(side):
+            decode()
+        prefill()
+        torch.cuda.current_stream().wait_stream(side)
     slot_mapping()
     t_m = time_launches(torch, slot_mapping, reps)
     t_r = time_launches(torch, reshape, reps)
     t_p = time_launches(torch, prefill, reps)
     t_d = time_launches(torch, decode, reps)
     t_s = time_launches(torch, step, reps)
+    t_s2 = time_launches(torch, step_two_streams, reps)
     flops = prefill_flops([wl.q_lens[s] for s in chunks], [wl.seq_lens[s] for s in chunks], wl.num_q_heads,
                           wl.head_dim)
     db = decode_bytes(dl, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, block_size)
     rb = 2 * T * wl.num_kv_heads * wl.head_dim * 2 * 2
-    res = {"block_size": block_size, "decode_partition_size": P, "step_ms": round(t_s * 1e3, 3), "tokens_written": T,
+    res = {"block_size": block_size, "decode_partition_size": P, "step_ms": round(t_s * 1e3, 3),
+           "step_two_streams_ms": round(t_s2 * 1e3, 3), "tokens_written": T,
            "slot_mapping_us": round(t_m * 1e6, 2),
            "reshape_us": round(t_r * 1e6, 2), "reshape_gbps": round(rb / t_r / 1e9, 1),
            "prefill_us": round(t_p * 1e6, 1), "prefill_gflop": round(flops / 1e9, 2),
