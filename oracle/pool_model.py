@@ -25,18 +25,65 @@ Sources
     reference count exceeds one; the capacity test covers both before any
     state changes; otherwise nothing is modified.
 
+Prefix caching and retention (same page unless noted)
+  * A full block carries a hash of its tokens and of the previous block's
+    hash, so the hash captures position ("The pantry of pigeonholes", the
+    prefix-sharing section); a global map from hash to block finds a cached
+    prefix.  Matching a prefix "touches" each hit block: its reference
+    count rises and, if it was waiting in the free queue as an eviction
+    candidate, it leaves the queue (1. The block pool; the copy-on-write
+    section on BlockPool.touch).
+  * free_blocks: a block whose references reach zero keeps its hash; a
+    hashed block goes to the tail of the queue (reused last, so it stays
+    matchable), an unhashed one to the head (reused first).  Popping a
+    hashed block for reuse evicts its hash entry (get_new_blocks).
+  * Transfer pins (the CPU reference allocator's two kinds of references):
+    a block is reusable only when it has neither owners nor pins; a pinned
+    partial tail is copied before a write, like a shared one.
+  * A copy-on-write keeps both endpoints retained until the copy has run
+    (_apply_cow: the source keeps its reference, the destination takes an
+    extra one); the caller reports the copies done.
+
 Readings where the pages leave a step open
   * No null block: every block id is allocatable (the CPU reference
     allocator returns all three of its pages to the free list).
   * Freed blocks are put at the head of the free queue in the order they
     are released (tail block first), so the tail block is the next one
-    handed out.
+    handed out.  Hashed blocks go to the tail in release order.
   * The copy block is taken from the queue before the appended blocks.
+  * The block hash is 64-bit FNV-1a over the previous block's hash (8 bytes,
+    little-endian; 0 for the first block) followed by the block's token ids
+    (4 bytes each, little-endian, two's complement).  The pages name no hash
+    function; any 64-bit hash of that input fits their description.
+  * Only full blocks are hashed and matched (prefix hits land on block
+    boundaries; no partial hits).  When a hash is already mapped, the new
+    block stays unhashed and the map keeps the first block.
+  * A request's pins cover the blocks its table names when it is pinned;
+    blocks released by an unpin, or by the completion of pending copies, are
+    freed in reverse order of the pinned list, and for each copy the source
+    before the destination.
 """
 
 from __future__ import annotations
 
 from collections import deque
+
+FNV_OFFSET = 14695981039346656037
+FNV_PRIME = 1099511628211
+MASK64 = (1 << 64) - 1
+
+
+def block_hash(parent: int, tokens) -> int:
+    """64-bit FNV-1a over the parent hash (8 bytes LE) and the token ids
+    (4 bytes LE each)."""
+    h = FNV_OFFSET
+    data = int(parent & MASK64).to_bytes(8, "little")
+    for t in tokens:
+        data += int(t & 0xFFFFFFFF).to_bytes(4, "little")
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
 
 
 class PoolError(Exception):
@@ -63,16 +110,119 @@ class PoolModel:
         self.num_blocks = num_blocks
         self.block_size = block_size
         self.free = deque(order)
-        self.ref = [0] * num_blocks
+        self.ref = [0] * num_blocks       # owners: tables that name the block
+        self.pins = [0] * num_blocks      # transfer pins
+        self.hold = [0] * num_blocks      # pending copy-on-write copies
+        self.hash_of = [None] * num_blocks
+        self.cached: dict[int, int] = {}  # block hash -> block
+        self.transfers: dict = {}         # transfer id -> pinned blocks
+        self.pending: list = []           # (src, dst) copies not yet run
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
 
+    # -- retention -----------------------------------------------------------
+    def _retained(self, b: int) -> bool:
+        return self.ref[b] + self.pins[b] + self.hold[b] > 0
+
+    def _release(self, blocks) -> None:
+        """blocks (in eviction-priority order) have just lost their last
+        reference: unhashed ones go to the head of the queue, hashed ones to
+        the tail, each group in the given order."""
+        first = [b for b in blocks if self.hash_of[b] is None]
+        last = [b for b in blocks if self.hash_of[b] is not None]
+        self.free.extendleft(reversed(first))
+        self.free.extend(last)
+
+    def _pop(self) -> int:
+        """Head of the free queue, its cached hash (if any) evicted."""
+        b = self.free.popleft()
+        if self.hash_of[b] is not None:
+            del self.cached[self.hash_of[b]]
+            self.hash_of[b] = None
+        return b
+
+    def _touch(self, b: int) -> None:
+        if not self._retained(b):
+            self.free.remove(b)
+        self.ref[b] += 1
+
     # -- sequences ---------------------------------------------------------
-    def add_seq(self, seq: int) -> None:
+    def add_seq(self, seq: int, tokens=None) -> int:
+        """New empty sequence; with ``tokens``, its longest prefix of cached
+        full blocks is shared (each hit block touched) and the number of
+        tokens covered is returned."""
         if seq in self.tables:
             raise InvalidArgument(f"sequence {seq} exists")
         self.tables[seq] = []
         self.lens[seq] = 0
+        if tokens is None:
+            return 0
+        B = self.block_size
+        h = 0
+        for j in range(len(tokens) // B):
+            h = block_hash(h, tokens[j * B:(j + 1) * B])
+            b = self.cached.get(h)
+            if b is None:
+                break
+            self._touch(b)
+            self.tables[seq].append(b)
+            self.lens[seq] += B
+        return self.lens[seq]
+
+    def cache_blocks(self, seq: int, tokens) -> None:
+        """Hash the full blocks of seq covered by ``tokens`` (its first
+        len(tokens) token ids) and enter the unhashed ones into the map."""
+        if seq not in self.tables:
+            raise InvalidArgument(f"unknown sequence {seq}")
+        if len(tokens) > self.lens[seq]:
+            raise InvalidArgument("more tokens than the sequence holds")
+        B = self.block_size
+        chain, h = [], 0
+        for j in range(len(tokens) // B):
+            h = block_hash(h, tokens[j * B:(j + 1) * B])
+            b = self.tables[seq][j]
+            if self.hash_of[b] is not None and self.hash_of[b] != h:
+                raise InvalidArgument(f"block {b} already holds other content")
+            chain.append((b, h))
+        for b, h in chain:                        # all checked: nothing changed on error
+            if self.hash_of[b] is None and h not in self.cached:
+                self.cached[h] = b
+                self.hash_of[b] = h
+
+    # -- transfer pins and pending copies -----------------------------------------
+    def pin(self, seq: int, transfer) -> list:
+        """Pin every block seq's table names under a new transfer id."""
+        if seq not in self.tables:
+            raise InvalidArgument(f"unknown sequence {seq}")
+        if transfer in self.transfers:
+            raise InvalidArgument(f"transfer {transfer} exists")
+        blocks = list(self.tables[seq])
+        for b in blocks:
+            self.pins[b] += 1
+        self.transfers[transfer] = blocks
+        return list(blocks)
+
+    def unpin(self, transfer) -> None:
+        if transfer not in self.transfers:
+            raise InvalidArgument(f"unknown transfer {transfer}")
+        released = []
+        for b in reversed(self.transfers.pop(transfer)):
+            self.pins[b] -= 1
+            if not self._retained(b):
+                released.append(b)
+        self._release(released)
+
+    def copies_done(self) -> None:
+        """The pending copy-on-write copies have run: their endpoints lose
+        the retention held for them."""
+        released = []
+        for src, dst in self.pending:
+            for b in (src, dst):
+                self.hold[b] -= 1
+                if not self._retained(b):
+                    released.append(b)
+        self.pending = []
+        self._release(released)
 
     def fork(self, src: int, dst: int) -> None:
         """dst shares every block of src; each shared block gains one ref."""
@@ -100,19 +250,22 @@ class PoolModel:
         table = self.tables[seq]
         cur = self.lens[seq]
         needed = -(-(cur + n) // B) - len(table)
-        cow = (cur % B != 0) and self.ref[table[-1]] > 1
+        cow = (cur % B != 0) and (self.ref[table[-1]] > 1 or self.pins[table[-1]] > 0)
         if needed + (1 if cow else 0) > len(self.free):
             raise NoSpace(f"need {needed + int(cow)} blocks, {len(self.free)} free")
         pair = None
         if cow:
             src = table[-1]
-            dst = self.free.popleft()
+            dst = self._pop()
             self.ref[dst] = 1
             self.ref[src] -= 1
+            self.hold[src] += 1
+            self.hold[dst] += 1
+            self.pending.append((src, dst))
             table[-1] = dst
             pair = (src, dst)
         for _ in range(needed):
-            b = self.free.popleft()
+            b = self._pop()
             self.ref[b] = 1
             table.append(b)
         slots = [table[p // B] * B + p % B for p in range(cur, cur + n)]
@@ -127,10 +280,10 @@ class PoolModel:
         released = []
         for b in reversed(self.tables[seq]):
             self.ref[b] -= 1
-            if self.ref[b] == 0:
+            if not self._retained(b):
                 released.append(b)
-        # released[0] (the sequence's tail block) becomes the new head
-        self.free.extendleft(reversed(released))
+        # unhashed: released[0] (the sequence's tail block) becomes the new head
+        self._release(released)
         del self.tables[seq]
         del self.lens[seq]
 
@@ -156,13 +309,18 @@ class PoolModel:
     def free_order(self) -> list[int]:
         return list(self.free)
 
+    def num_cached(self) -> int:
+        return len(self.cached)
+
     # -- invariants ----------------------------------------------------------
     def check(self) -> None:
         """Structural invariants of the CPU reference allocator section:
         free and allocated blocks are disjoint and cover every block once;
         every table entry exists and its count of owners is its refcount;
-        every allocated block has an owner; no table repeats a block;
-        every non-tail block is full and the tail holds 1..B tokens."""
+        every retained block has an owner, a pin or a pending copy, and the
+        pin and copy counts match their records; no table repeats a block;
+        every non-tail block is full and the tail holds 1..B tokens; the
+        hash map and the blocks' hashes agree one to one."""
         N, B = self.num_blocks, self.block_size
         free = list(self.free)
         if len(set(free)) != len(free):
@@ -178,11 +336,26 @@ class PoolModel:
                 if not 0 <= b < N:
                     raise AssertionError(f"table of {seq} names block {b}")
                 owners[b] += 1
+        pins = [0] * N
+        for blocks in self.transfers.values():
+            for b in blocks:
+                pins[b] += 1
+        hold = [0] * N
+        for src, dst in self.pending:
+            hold[src] += 1
+            hold[dst] += 1
         free_set = set(free)
         for b in range(N):
             if owners[b] != self.ref[b]:
                 raise AssertionError(f"block {b}: {owners[b]} owners, ref {self.ref[b]}")
-            if (b in free_set) != (self.ref[b] == 0):
-                raise AssertionError(f"block {b}: free={b in free_set} ref={self.ref[b]}")
-        if len(free) + sum(1 for r in self.ref if r > 0) != N:
+            if pins[b] != self.pins[b] or hold[b] != self.hold[b]:
+                raise AssertionError(f"block {b}: pin or copy counts do not match their records")
+            if (b in free_set) == self._retained(b):
+                raise AssertionError(f"block {b}: free={b in free_set} but retained={self._retained(b)}")
+        if len(free) + sum(1 for b in range(N) if self._retained(b)) != N:
             raise AssertionError("free and allocated blocks do not cover the pool")
+        for h, b in self.cached.items():
+            if self.hash_of[b] != h:
+                raise AssertionError(f"hash map entry of block {b} does not match its hash")
+        if sum(1 for h in self.hash_of if h is not None) != len(self.cached):
+            raise AssertionError("a block holds a hash the map does not know")

@@ -256,3 +256,60 @@ def device_query(seed: int, n_rows: int, num_q_heads: int, head_dim: int, layer:
     g.manual_seed((seed * 977 + layer * 31 + 5) % (2**63 - 1))
     return torch.randn((n_rows, num_q_heads, head_dim), generator=g, device=device,
                        dtype=torch.float32).to(torch.bfloat16)
+
+
+def pool_ops_cached(seed: int, n_ops: int = 200, max_seqs: int = 10, max_append: int = 24):
+    """Replayable pool operations with prefix caching, transfer pins and
+    step boundaries, for the randomized pool tests:
+      ("add", s), ("add_prefix", s, donor, n)  -- new sequence that asks for
+        the first n tokens of sequence donor (live or finished) as a prefix,
+      ("append", s, n), ("fork", src, dst), ("free", s),
+      ("cache", s)  -- hash the full blocks of s,
+      ("pin", s, t), ("unpin", t)  -- transfer pins,
+      ("done",)  -- end of a step: pending copies and writes land.
+    Only ids are tracked here; token contents are chosen by the runner."""
+    rng = np.random.default_rng([SEED_BASE, 8, seed])
+    live: list[int] = []
+    ever: list[int] = []
+    transfers: list[int] = []
+    next_id = next_t = 0
+    ops = []
+    for _ in range(n_ops):
+        r = rng.random()
+        if not live or (r < 0.10 and len(live) < max_seqs):
+            ops.append(("add", next_id))
+            live.append(next_id)
+            ever.append(next_id)
+            next_id += 1
+        elif r < 0.18 and len(live) < max_seqs and ever:
+            donor = ever[int(rng.integers(len(ever)))]
+            ops.append(("add_prefix", next_id, donor, int(rng.integers(0, 4 * max_append))))
+            live.append(next_id)
+            ever.append(next_id)
+            next_id += 1
+        elif r < 0.48:
+            s = live[int(rng.integers(len(live)))]
+            ops.append(("append", s, int(rng.integers(1, max_append + 1))))
+        elif r < 0.55 and len(live) < max_seqs:
+            s = live[int(rng.integers(len(live)))]
+            ops.append(("fork", s, next_id))
+            live.append(next_id)
+            ever.append(next_id)
+            next_id += 1
+        elif r < 0.65:
+            ops.append(("cache", live[int(rng.integers(len(live)))]))
+        elif r < 0.71:
+            ops.append(("pin", live[int(rng.integers(len(live)))], next_t))
+            transfers.append(next_t)
+            next_t += 1
+        elif r < 0.77 and transfers:
+            ops.append(("unpin", transfers.pop(int(rng.integers(len(transfers))))))
+        elif r < 0.90:
+            ops.append(("done",))
+        else:
+            s = live.pop(int(rng.integers(len(live))))
+            ops.append(("free", s))
+    ops.append(("done",))
+    for t in transfers:
+        ops.append(("unpin", t))
+    return ops

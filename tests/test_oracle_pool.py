@@ -27,8 +27,13 @@ class TokenStore:
         self.cells = np.full((pool.num_blocks, pool.block_size), -1, dtype=np.int64)
 
     def apply(self, slots, ids, pair):
+        """One append's copy (run at once, then reported done) and writes."""
         if pair is not None:
             cache_ops.copy_blocks([self.cells], [pair], self.pool.num_blocks)
+            self.pool.copies_done()
+        self.write(slots, ids)
+
+    def write(self, slots, ids):
         flat = self.cells.reshape(-1)
         for s, t in zip(slots, ids):
             flat[s] = t
@@ -40,7 +45,8 @@ class TokenStore:
 
 
 def snapshot(p: PoolModel):
-    return (list(p.free), list(p.ref), copy.deepcopy(p.tables), dict(p.lens))
+    return (list(p.free), list(p.ref), list(p.pins), list(p.hold), list(p.hash_of), dict(p.cached),
+            copy.deepcopy(p.tables), dict(p.lens), copy.deepcopy(p.transfers), list(p.pending))
 
 
 def test_initial_order_and_pop_from_head():
@@ -116,7 +122,8 @@ def test_full_tail_shares_without_copy():
 
 
 def test_pagedkv_scenario(golden):
-    """The CPU reference allocator example without its transfer pin."""
+    """The CPU reference allocator example, with its transfer pin: the
+    cancelled owner's page survives until the transfer is unpinned."""
     e = golden["pagedkv_scenario"]["printed"]
     p = PoolModel(e["capacity"], e["block_size"])
     st = TokenStore(p)
@@ -124,16 +131,150 @@ def test_pagedkv_scenario(golden):
     slots, pair = p.append("a", 1)
     st.apply(slots, [10], pair)
     p.fork("a", "b")
+    source, = p.pin("a", "transfer-1")
     slots, pair = p.append("b", 1)
-    assert pair is not None                      # partial shared tail: copy first
+    assert pair is not None and pair[0] == source    # partial shared tail: copy first
     st.apply(slots, [20], pair)
     assert st.read("a") == e["read_a"]
     assert st.read("b") == e["read_b"]
     p.check()
-    p.free_seq("a")
+    p.free_seq("a")                              # removes ownership, not the pin
+    assert source not in p.free_order() and p.pins[source] == 1
+    p.unpin("transfer-1")
+    assert source in p.free_order()
     p.check()
     p.free_seq("b")
     assert p.num_free() == e["free_after"]
+    p.check()
+
+
+def test_pinned_sole_owner_copies_its_partial_tail():
+    """A transfer's snapshot is immutable: even the only owner of a pinned
+    partial page copies it before writing."""
+    p = PoolModel(4, 4)
+    st = TokenStore(p)
+    p.add_seq(0)
+    slots, pair = p.append(0, 2)
+    st.apply(slots, [1, 2], pair)
+    tail, = p.pin(0, 7)
+    slots, pair = p.append(0, 1)
+    assert pair == (tail, p.block_table(0)[0])
+    st.apply(slots, [3], pair)
+    assert st.read(0) == [1, 2, 3]
+    assert list(st.cells[tail, :2]) == [1, 2] and st.cells[tail, 2] == -1
+    p.unpin(7)
+    assert tail in p.free_order()
+    p.check()
+    with pytest.raises(InvalidArgument):
+        p.unpin(7)                               # completed transfers are unknown
+    p.pin(0, 8)
+    with pytest.raises(InvalidArgument):
+        p.pin(0, 8)                              # handles are unique
+
+
+def test_copy_endpoints_retained_until_copies_done():
+    """A free in the same step cannot recycle a copy's source: both endpoints
+    stay retained until the copies are reported done."""
+    p = PoolModel(6, 4)
+    p.add_seq(0)
+    p.append(0, 2)
+    p.fork(0, 1)
+    _, (src, dst) = p.append(1, 1)
+    p.free_seq(0)                                # src's last owner leaves
+    assert p.refcount(src) == 0 and src not in p.free_order()
+    p.free_seq(1)                                # dst's owner leaves too
+    assert dst not in p.free_order()
+    p.check()
+    p.copies_done()
+    assert src in p.free_order() and dst in p.free_order() and p.num_free() == 6
+    p.check()
+
+
+def test_fnv1a_published_vectors():
+    """The block hash is FNV-1a 64; check the byte loop against the
+    published test vectors of the algorithm (empty input, "a", "foobar")
+    by feeding them through a parent-free helper with the same constants."""
+    from oracle import pool_model as pm
+
+    def fnv(data: bytes) -> int:
+        h = pm.FNV_OFFSET
+        for byte in data:
+            h ^= byte
+            h = (h * pm.FNV_PRIME) & pm.MASK64
+        return h
+    assert fnv(b"") == 0xCBF29CE484222325
+    assert fnv(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv(b"foobar") == 0x85944171F73967E8
+    # block_hash = FNV-1a over (parent LE 8 bytes, tokens LE 4 bytes each)
+    data = (5).to_bytes(8, "little") + (1).to_bytes(4, "little") + (0xFFFFFFFF).to_bytes(4, "little")
+    assert pm.block_hash(5, [1, -1]) == fnv(data)
+
+
+def test_block_hash_chain_captures_position():
+    from oracle.pool_model import block_hash
+    a = block_hash(0, [1, 2, 3, 4])
+    assert block_hash(0, [1, 2, 3, 4]) == a
+    assert block_hash(a, [1, 2, 3, 4]) != a        # same tokens, later position
+    assert block_hash(0, [1, 2, 3, 5]) != a
+
+
+def test_prefix_hit_after_free_and_eviction_on_reuse():
+    """A finished request's hashed blocks go to the tail of the queue and a
+    new request with the same prompt hits them (touch pulls them out of the
+    queue); unhashed blocks are reused first; popping a hashed block for a
+    new tenant evicts its hash."""
+    B = 4
+    p = PoolModel(8, B)
+    st = TokenStore(p)
+    prompt = list(range(100, 114))               # 3 full blocks + 2 tokens
+    p.add_seq(0)
+    slots, pair = p.append(0, len(prompt))
+    st.apply(slots, prompt, pair)
+    p.cache_blocks(0, prompt)
+    assert p.num_cached() == 3
+    full = p.block_table(0)[:3]
+    partial = p.block_table(0)[3]
+    p.free_seq(0)
+    order = p.free_order()
+    assert order[0] == partial                   # unhashed: head
+    assert order[-3:] == full[::-1]              # hashed: tail, tail block first
+    hit = p.add_seq(1, prompt)
+    assert hit == 12 and p.block_table(1) == full
+    assert all(p.refcount(b) == 1 for b in full) and all(b not in p.free_order() for b in full)
+    slots, pair = p.append(1, 2)
+    st.apply(slots, prompt[12:], pair)
+    assert st.read(1) == prompt
+    p.check()
+    # a hit on a block that is in use just adds a reference
+    assert p.add_seq(2, prompt[:8]) == 8 and p.refcount(full[0]) == 2
+    p.free_seq(1)
+    p.free_seq(2)
+    # now fill the pool: the hashed blocks are the last ones reused, and
+    # reusing one evicts its hash
+    p.add_seq(3)
+    p.append(3, 5 * B)
+    assert p.num_cached() == 3
+    p.append(3, B)
+    assert p.num_cached() == 2
+    # the prompt's last full block was freed first, so it was the first
+    # hashed block reused: the least valuable end of the prefix goes first
+    # and the chain now breaks at block 2
+    assert p.add_seq(4, prompt) == 8
+    p.check()
+
+
+def test_duplicate_content_keeps_first_block():
+    p = PoolModel(8, 2)
+    for s in (0, 1):
+        p.add_seq(s)
+        p.append(s, 4)
+        p.cache_blocks(s, [7, 8, 9, 10])
+    assert p.num_cached() == 2
+    assert p.hash_of[p.block_table(1)[0]] is None     # 0's blocks are the cached ones
+    with pytest.raises(InvalidArgument):
+        p.cache_blocks(0, [7, 8, 9, 11])          # block 1 of 0 already holds other content
+    with pytest.raises(InvalidArgument):
+        p.cache_blocks(0, [1] * 5)                # more tokens than the sequence holds
     p.check()
 
 
@@ -275,6 +416,117 @@ def test_randomized_against_list_model(seed):
     # a small pool so that exhaustion, reuse and copies all happen
     out = run_with_list_model(24, 4, seed)
     assert len(out) == 200
+
+
+def run_cached_with_list_model(num_blocks, block_size, seed, n_ops=200):
+    """Prefix caching, pins and step boundaries against the list model: a
+    step's copies and writes land at its end ("done"), copies first; every
+    sequence read back through its table must equal its token list, and the
+    contents of pinned blocks never change while pinned.  As in a serving
+    step, a sequence is appended to at most once per step, forks and block
+    caching read landed contents (the runner ends the step early otherwise)
+    and a sequence freed within a step is not run (its writes are dropped);
+    frees and unpins inside a step exercise the retention of pending
+    copies."""
+    p = PoolModel(num_blocks, block_size, np.random.default_rng([seed, 4]).permutation(num_blocks))
+    st = TokenStore(p)
+    lists, history = {}, {}
+    pending_pairs, pending_writes = [], []
+    frozen = {}                                   # transfer -> {block: contents}
+    next_tok = 0
+    stats = {"hits": 0, "copies": 0, "nospace": 0, "pins": 0}
+
+    stepped = set()                               # sequences with writes pending in this step
+
+    def end_step():
+        nonlocal pending_pairs, pending_writes
+        stepped.clear()
+        if pending_pairs:
+            cache_ops.copy_blocks([st.cells], pending_pairs, p.num_blocks)
+        for _, slots, ids in pending_writes:
+            st.write(slots, ids)
+        pending_pairs, pending_writes = [], []
+        p.copies_done()
+        for s, toks in lists.items():
+            assert st.read(s) == toks, (seed, op)
+        for t, blocks in frozen.items():
+            now = {b: st.cells[b].copy() for b in p.transfers[t]}
+            if blocks is None:
+                frozen[t] = now
+            else:
+                assert all(np.array_equal(blocks[b], now[b]) for b in blocks), (seed, t)
+
+    for op in workloads.pool_ops_cached(seed, n_ops):
+        kind = op[0]
+        if kind == "add":
+            p.add_seq(op[1])
+            lists[op[1]] = []
+        elif kind == "add_prefix":
+            s, donor, n = op[1], op[2], op[3]
+            toks = (lists.get(donor) or history.get(donor, []))[:n]
+            hit = p.add_seq(s, toks)
+            stats["hits"] += hit > 0
+            lists[s] = list(toks[:hit])
+        elif kind == "fork":
+            # a fork reads what its source has written: the step ends first
+            end_step()
+            p.fork(op[1], op[2])
+            lists[op[2]] = list(lists[op[1]])
+        elif kind == "free":
+            # a sequence freed within the step is not run: its writes are dropped
+            p.free_seq(op[1])
+            history[op[1]] = lists.pop(op[1])
+            pending_writes = [w for w in pending_writes if w[0] != op[1]]
+        elif kind == "cache":
+            # blocks are cached once their contents have landed
+            if op[1] in stepped:
+                end_step()
+            p.cache_blocks(op[1], lists[op[1]])
+        elif kind == "pin":
+            p.pin(op[1], op[2])
+            frozen[op[2]] = None                  # contents taken at the end of the step
+            stats["pins"] += 1
+        elif kind == "unpin":
+            p.unpin(op[1])
+            del frozen[op[1]]
+        elif kind == "append":
+            s, n = op[1], op[2]
+            if s in stepped:
+                # one append per sequence and step: a copy-on-write reads
+                # the source as the previous steps left it
+                end_step()
+            before = snapshot(p)
+            try:
+                slots, pair = p.append(s, n)
+            except NoSpace:
+                assert snapshot(p) == before
+                stats["nospace"] += 1
+            else:
+                ids = list(range(next_tok, next_tok + n))
+                next_tok += n
+                lists[s].extend(ids)
+                stepped.add(s)
+                pending_writes.append((s, slots, ids))
+                if pair is not None:
+                    pending_pairs.append(pair)
+                    stats["copies"] += 1
+        else:                                     # done: copies, then writes
+            end_step()
+        p.check()
+    return stats
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_randomized_prefix_cache_and_pins(seed):
+    run_cached_with_list_model(24, 4, seed)
+
+
+def test_randomized_cached_runs_exercise_every_branch():
+    tot = {"hits": 0, "copies": 0, "nospace": 0, "pins": 0}
+    for seed in range(25):
+        for k, v in run_cached_with_list_model(24, 4, seed).items():
+            tot[k] += v
+    assert all(v > 10 for v in tot.values()), tot
 
 
 def test_randomized_runs_exercise_every_branch():
