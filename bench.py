@@ -141,6 +141,7 @@ def run_step(inst, B, stream):
     cow = inst.pairs[inst.pairs[:, 0] >= 0]
     if len(cow):
         B.pa_copy_blocks([inst.state.kc, inst.state.vc], cow)
+        B.pa_pool_copies_done(inst.state.pool)
     rc = L.pa_reshape_and_cache(*inst.reshape_args, stream)
     if rc != 0:
         raise RuntimeError(L.pa_last_error().decode())

@@ -93,6 +93,35 @@ void pa_pool_destroy(pa_pool* pool);
  * seq_id already exists. */
 int pa_pool_add_seq(pa_pool* pool, int64_t seq_id);
 
+/* Register a sequence whose prompt is tokens[0..n_tokens) and give it the
+ * longest run of cached full blocks matching the prompt's leading blocks.
+ * Block j's hash is 64-bit FNV-1a over the previous block's hash (8 bytes
+ * little-endian; 0 before block 0) followed by the block's B token ids (4
+ * bytes little-endian each), so a hash names the block's content at its
+ * position.  Matching stops at the first full block whose hash is not cached;
+ * a partial last block never matches.  Each hit block gains one reference and,
+ * if it was free (cached but evictable), leaves the free queue.  The sequence
+ * then holds hit_tokens = hits * B tokens whose KV is already in the cache; the
+ * caller appends the rest of the prompt.
+ * ("PagedAttention: fragmentation, blocks, block tables", 1. The block pool:
+ * per-block hash and touch; copy-on-write section: a full-block prefix hit
+ * needs no copy.  "The pantry of pigeonholes", prefix sharing: a block's hash
+ * covers its tokens and its parent's hash.)
+ * tokens: host int32 [n_tokens] (NULL allowed when n_tokens is 0).
+ * Errors: PA_ERR_INVALID if seq_id exists or an argument is NULL/negative
+ * (pool unchanged, *hit_tokens = 0). */
+int pa_pool_add_seq_cached(pa_pool* pool, int64_t seq_id, const int32_t* tokens,
+                           int64_t n_tokens, int64_t* hit_tokens);
+
+/* Enter the full blocks of seq_id's first n_tokens tokens (whose KV the caller
+ * has written) into the prefix cache: block j gets the chained hash of
+ * tokens[0 .. (j+1)B).  A block that already holds that hash, or whose hash
+ * another block already holds (the first block entered keeps it), is left as it
+ * is.  All-or-nothing: if n_tokens exceeds the sequence's length or a block
+ * already holds a different hash, PA_ERR_INVALID and nothing changes.
+ * (Same passages as pa_pool_add_seq_cached.) */
+int pa_pool_cache_blocks(pa_pool* pool, int64_t seq_id, const int32_t* tokens, int64_t n_tokens);
+
 /* New sequence dst_seq shares every block of src_seq (same table, same
  * length); each shared block's reference count grows by one.  Full blocks are
  * then shared outright and a partial tail is copied on first write ("Memory
@@ -101,20 +130,24 @@ int pa_pool_add_seq(pa_pool* pool, int64_t seq_id);
 int pa_pool_fork(pa_pool* pool, int64_t src_seq, int64_t dst_seq);
 
 /* Append n_tokens >= 1 tokens to seq_id.
- *   needed = ceil((len + n) / B) - held;  copy = (len % B != 0) and
- *   refcount(tail) > 1.  If needed + copy exceeds the free blocks, return
- *   PA_ERR_NO_SPACE and change nothing.  Otherwise, if copy: pop dst from the
- *   head of the free queue (ref 1), drop one reference of the shared tail src,
- *   replace the tail entry in place and report (src, dst) in cow_pair_out; then
- *   pop `needed` blocks (ref 1) onto the table, and write the slot of every new
- *   position p in [len, len + n):  slot = table[p / B] * B + p % B.
+ *   needed = ceil((len + n) / B) - held;  copy = (len % B != 0) and the tail
+ *   is shared (refcount > 1) or pinned by a transfer.  If needed + copy
+ *   exceeds the free blocks, return PA_ERR_NO_SPACE and change nothing.
+ *   Otherwise, if copy: pop dst from the head of the free queue (ref 1), drop
+ *   one reference of the tail src, replace the tail entry in place, record
+ *   (src, dst) as a pending copy that keeps both blocks out of the free queue
+ *   until pa_pool_copies_done, and report it in cow_pair_out; then pop
+ *   `needed` blocks (ref 1) onto the table, and write the slot of every new
+ *   position p in [len, len + n):  slot = table[p / B] * B + p % B.  A block
+ *   popped from the free queue loses its cached hash.
  * ("Memory management", Code: append with copy-on-write; "PagedAttention:
  * fragmentation, blocks, block tables": get_new_blocks pops from the head,
  * the block table is append-only, 3. The slot mapping, and the copy-on-write
  * section's in-place redirect with a queued (src, dst) copy.)
  * slots_out: host int64 [n_tokens].  cow_pair_out: host int32 [2], set to
  * {-1, -1} when no copy is needed.  The caller must copy block src to dst
- * (pa_copy_blocks) before any write to dst and before src can be reused.
+ * (pa_copy_blocks) before any write to dst, then call pa_pool_copies_done
+ * once the copies are ordered before later work.
  * Errors: PA_ERR_INVALID (unknown seq, n_tokens < 1, NULL outputs),
  * PA_ERR_NO_SPACE (pool unchanged). */
 int pa_pool_append(pa_pool* pool, int64_t seq_id, int32_t n_tokens,
@@ -129,14 +162,42 @@ int pa_pool_append_batch(pa_pool* pool, const int64_t* seq_ids, const int32_t* n
                          int32_t n_seqs, int64_t* slots_out, int32_t* cow_pairs_out,
                          int32_t* n_done);
 
-/* Release seq_id: walk its blocks from the tail to the head, drop one
- * reference each, and put the blocks that reach zero at the head of the free
- * queue in that order, so the sequence's tail block is the next one reused.
+/* Release seq_id: walk its blocks from the tail to the head and drop one
+ * reference each.  Of the blocks that are left with no reference, no pin and
+ * no pending copy, taken in that tail-first order, the unhashed ones go to the
+ * head of the free queue (the sequence's tail block is the next one reused)
+ * and the hashed ones to its tail (reused last, still matchable by a prefix
+ * lookup until popped).
  * ("PagedAttention: fragmentation, blocks, block tables", 1. The block pool:
  * free_blocks takes blocks ordered by eviction priority, first evicted first;
- * non-cached blocks go to the front; a request frees its blocks in reverse.)
+ * non-cached blocks go to the front, cached ones to the back; a request frees
+ * its blocks in reverse.)
  * Errors: PA_ERR_INVALID if seq_id is unknown. */
 int pa_pool_free_seq(pa_pool* pool, int64_t seq_id);
+
+/* Pin every block of seq_id for an outgoing transfer transfer_id (a KV
+ * transfer to another engine reads them after the sequence may be gone).  A
+ * pinned block is not reused while pinned and a partial tail that is pinned is
+ * copied before the next write, as a shared one is.  blocks_out (host int32
+ * [cap]) receives the pinned ids in table order and *n_out their number.
+ * ("PagedAttention: fragmentation, blocks, block tables", CPU reference
+ * allocator: owner references and transfer pins both keep a block live.)
+ * Errors: PA_ERR_INVALID for an unknown sequence, an existing transfer_id or
+ * too small a cap (*n_out says how many are needed; nothing pinned). */
+int pa_pool_pin(pa_pool* pool, int64_t seq_id, int64_t transfer_id, int32_t* blocks_out,
+                int32_t cap, int32_t* n_out);
+
+/* End transfer transfer_id: drop its pins, releasing (as pa_pool_free_seq
+ * does, last pinned block first) the blocks left with no reference, pin or
+ * pending copy.  Errors: PA_ERR_INVALID if transfer_id is unknown. */
+int pa_pool_unpin(pa_pool* pool, int64_t transfer_id);
+
+/* The copies reported by pa_pool_append since the last call have been issued
+ * (on the stream that orders them before later kernels): release every copy's
+ * source and destination hold, freeing the blocks left with nothing else
+ * retaining them.  (Copy-on-write section: the scheduler issues the queued
+ * copies before the step's kernels.) */
+int pa_pool_copies_done(pa_pool* pool);
 
 /* Write the block tables of n_seqs sequences into table_out (host int32
  * [n_seqs][bt_stride]): row i gets ceil(len_i / B) block ids; the rest of the
@@ -148,6 +209,12 @@ int pa_pool_block_table(const pa_pool* pool, const int64_t* seq_ids, int32_t n_s
 
 /* Number of free blocks (the capacity test is a subtraction against it). */
 int pa_pool_num_free(const pa_pool* pool, int32_t* out);
+/* Number of cached block hashes (each names one block, free or in use). */
+int pa_pool_num_cached(const pa_pool* pool, int32_t* out);
+/* Pins, pending copies and cached hash of block_id (*hashed_out 0 or 1; the
+ * hash is 0 when not hashed).  Errors: PA_ERR_INVALID if out of range. */
+int pa_pool_block_state(const pa_pool* pool, int32_t block_id, int32_t* pins_out,
+                        int32_t* pending_out, uint64_t* hash_out, int32_t* hashed_out);
 /* Reference count of block_id.  Errors: PA_ERR_INVALID if out of range. */
 int pa_pool_refcount(const pa_pool* pool, int32_t block_id, int32_t* out);
 /* Token count of seq_id. */
@@ -155,10 +222,12 @@ int pa_pool_seq_len(const pa_pool* pool, int64_t seq_id, int64_t* out);
 /* The free queue from head to tail: writes min(cap, free) ids, *n_out = free. */
 int pa_pool_free_order(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n_out);
 
-/* Check the allocator invariants (CPU reference allocator section): free and
- * allocated blocks are disjoint and cover every block once; every table entry
- * is a valid id whose reference count equals its number of owners; no table
- * repeats a block; each table holds exactly ceil(len / B) blocks.
+/* Check the allocator invariants (CPU reference allocator section): a block is
+ * in the free queue exactly when it has no reference, pin or pending copy, and
+ * the queue's links are consistent; every table entry is a valid id whose
+ * reference count equals its number of owners; pin and pending-copy counts
+ * equal their records; no table repeats a block; each table holds exactly
+ * ceil(len / B) blocks; the hash map and the blocks' hashes name each other.
  * Returns PA_OK or PA_ERR_INVALID with the first violation in pa_last_error. */
 int pa_pool_check(const pa_pool* pool);
 

@@ -48,6 +48,13 @@ _SIGS = {
     "pa_pool_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
     "pa_pool_destroy": (None, [c_vp]),
     "pa_pool_add_seq": (c_i32, [c_vp, c_i64]),
+    "pa_pool_add_seq_cached": (c_i32, [c_vp, c_i64, P_i32, c_i64, P_i64]),
+    "pa_pool_cache_blocks": (c_i32, [c_vp, c_i64, P_i32, c_i64]),
+    "pa_pool_pin": (c_i32, [c_vp, c_i64, c_i64, P_i32, c_i32, P_i32]),
+    "pa_pool_unpin": (c_i32, [c_vp, c_i64]),
+    "pa_pool_copies_done": (c_i32, [c_vp]),
+    "pa_pool_num_cached": (c_i32, [c_vp, P_i32]),
+    "pa_pool_block_state": (c_i32, [c_vp, c_i32, P_i32, P_i32, ctypes.POINTER(ctypes.c_uint64), P_i32]),
     "pa_pool_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pa_pool_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32]),
     "pa_pool_append_batch": (c_i32, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, P_i32]),
@@ -147,6 +154,51 @@ def pa_pool_destroy(pool: Pool):
 
 def pa_pool_add_seq(pool, seq_id):
     _check(lib().pa_pool_add_seq(pool.handle, seq_id))
+
+
+def pa_pool_add_seq_cached(pool, seq_id, tokens):
+    """Registers seq_id with its cached prefix blocks; returns the hit tokens."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    hit = c_i64()
+    _check(lib().pa_pool_add_seq_cached(pool.handle, seq_id, _i32p(t), len(t), ctypes.byref(hit)))
+    return hit.value
+
+
+def pa_pool_cache_blocks(pool, seq_id, tokens):
+    t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    _check(lib().pa_pool_cache_blocks(pool.handle, seq_id, _i32p(t), len(t)))
+
+
+def pa_pool_pin(pool, seq_id, transfer_id):
+    """Pins seq_id's blocks for transfer_id; returns the pinned ids (list)."""
+    n = c_i32()
+    cap = -(-pa_pool_seq_len(pool, seq_id) // pool.block_size)
+    out = np.empty(max(cap, 1), dtype=np.int32)
+    _check(lib().pa_pool_pin(pool.handle, seq_id, transfer_id, _i32p(out), cap, ctypes.byref(n)))
+    return out[:n.value].tolist()
+
+
+def pa_pool_unpin(pool, transfer_id):
+    _check(lib().pa_pool_unpin(pool.handle, transfer_id))
+
+
+def pa_pool_copies_done(pool):
+    _check(lib().pa_pool_copies_done(pool.handle))
+
+
+def pa_pool_num_cached(pool):
+    out = c_i32()
+    _check(lib().pa_pool_num_cached(pool.handle, ctypes.byref(out)))
+    return out.value
+
+
+def pa_pool_block_state(pool, block_id):
+    """Returns (pins, pending copies, hash or None)."""
+    pins, pend, hashed = c_i32(), c_i32(), c_i32()
+    h = ctypes.c_uint64()
+    _check(lib().pa_pool_block_state(pool.handle, block_id, ctypes.byref(pins), ctypes.byref(pend),
+                                     ctypes.byref(h), ctypes.byref(hashed)))
+    return pins.value, pend.value, (h.value if hashed.value else None)
 
 
 def pa_pool_fork(pool, src_seq, dst_seq):

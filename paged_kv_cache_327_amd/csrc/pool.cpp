@@ -1,24 +1,37 @@
 // Host block pool: free queue, reference counts, append-only block tables,
-// ceil(n/B) allocation and copy-on-write of a shared partial tail.
+// ceil(n/B) allocation, copy-on-write of a shared partial tail, prefix
+// caching by block hash, and transfer pins.
 //
 // "PagedAttention: fragmentation, blocks, block tables":
-//   1. The block pool -- every physical block has metadata (id, refcount) and
-//      sits in one free queue at construction; allocation pops from the head;
-//      freeing drops a reference and returns non-cached blocks to the front,
-//      ordered by eviction priority (first evicted first), a request freeing its
-//      blocks tail first.
+//   1. The block pool -- every physical block has metadata (id, refcount, the
+//      hash of its contents once cached) and sits in one free queue at
+//      construction; allocation pops from the head and evicts the popped
+//      block's cached hash; freeing drops a reference and, at zero, returns an
+//      unhashed block to the front (reused first) and a hashed one to the back
+//      (reused last, still matchable), in eviction-priority order, a request
+//      freeing its blocks tail first.  The queue is intrusive, so a block that
+//      a prefix hit touches leaves the middle of the queue in O(1).
 //   2. The block table -- position p is in block table[p / B] at p % B.
 //   3. The slot mapping -- slot = table[p / B] * B + p % B.
 //   copy-on-write section -- the shared tail entry is replaced in place by a
-//      private block and the (src, dst) pair is handed to the caller.
+//      private block and the (src, dst) pair is handed to the caller; both
+//      endpoints stay retained until the copy has run (the caller reports it);
+//      a full-block prefix hit just touches the block.
+//   CPU reference allocator -- owner references and transfer pins: a block is
+//      reusable only when it has neither; a pinned partial tail is copied
+//      before a write, like a shared one.
+// "The pantry of pigeonholes", prefix sharing -- a block's hash covers its
+//   tokens and the previous block's hash, so it captures position.
 // "Memory management", Code -- append with copy-on-write: the capacity test
 //   covers the copy block and the new blocks before anything changes.
 //
-// The free queue is a ring buffer of capacity num_blocks: a block is queued at
-// most once, so it never overflows, and both ends are O(1).
+// Readings: the hash is 64-bit FNV-1a over the parent hash (8 bytes LE, 0 for
+// the first block) and the block's token ids (4 bytes LE each); only full
+// blocks are hashed and matched; the first block entered for a hash keeps it.
 #include <algorithm>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "internal.hpp"
@@ -27,31 +40,71 @@
 struct pa_pool {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> ring;  // free queue storage
-  int32_t head = 0;           // index of the queue head in `ring`
-  int32_t count = 0;          // number of free blocks
-  std::vector<int32_t> ref;   // reference count per block
+  // intrusive doubly linked free queue over block ids (-1 = none)
+  std::vector<int32_t> prev, next;
+  std::vector<uint8_t> queued;
+  int32_t head = -1, tail = -1, count = 0;
+  std::vector<int32_t> ref;   // owners: tables naming the block
+  std::vector<int32_t> pins;  // transfer pins
+  std::vector<int32_t> hold;  // pending copy-on-write copies
+  std::vector<uint8_t> hashed;
+  std::vector<uint64_t> hash;
+  std::unordered_map<uint64_t, int32_t> cached;                  // hash -> block
+  std::unordered_map<int64_t, std::vector<int32_t>> transfers;   // id -> pinned blocks
+  std::vector<std::pair<int32_t, int32_t>> pending;              // copies not yet run
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t len = 0;
   };
   std::unordered_map<int64_t, Seq> seqs;
 
-  int32_t pop_front() {
-    int32_t b = ring[head];
-    head = head + 1 == num_blocks ? 0 : head + 1;
-    --count;
-    return b;
-  }
+  bool retained(int32_t b) const { return ref[(size_t)b] + pins[(size_t)b] + hold[(size_t)b] > 0; }
+
   void push_front(int32_t b) {
-    head = head == 0 ? num_blocks - 1 : head - 1;
-    ring[head] = b;
+    prev[(size_t)b] = -1;
+    next[(size_t)b] = head;
+    if (head >= 0) prev[(size_t)head] = b; else tail = b;
+    head = b;
+    queued[(size_t)b] = 1;
     ++count;
   }
-  int32_t at(int32_t i) const {  // i-th block from the head
-    int64_t j = (int64_t)head + i;
-    if (j >= num_blocks) j -= num_blocks;
-    return ring[(size_t)j];
+  void push_back(int32_t b) {
+    next[(size_t)b] = -1;
+    prev[(size_t)b] = tail;
+    if (tail >= 0) next[(size_t)tail] = b; else head = b;
+    tail = b;
+    queued[(size_t)b] = 1;
+    ++count;
+  }
+  void remove(int32_t b) {  // O(1) removal from anywhere in the queue
+    const int32_t p = prev[(size_t)b], n = next[(size_t)b];
+    if (p >= 0) next[(size_t)p] = n; else head = n;
+    if (n >= 0) prev[(size_t)n] = p; else tail = p;
+    queued[(size_t)b] = 0;
+    --count;
+  }
+  // Head of the queue, its cached hash (if any) evicted.
+  int32_t pop() {
+    const int32_t b = head;
+    remove(b);
+    if (hashed[(size_t)b]) {
+      cached.erase(hash[(size_t)b]);
+      hashed[(size_t)b] = 0;
+    }
+    return b;
+  }
+  // A block gains an owner; a free (evictable) block leaves the queue.
+  void touch(int32_t b) {
+    if (!retained(b)) remove(b);
+    ref[(size_t)b] += 1;
+  }
+  // `blocks` (eviction-priority order) have just lost their last reference:
+  // unhashed ones to the head, hashed ones to the tail, each group in order.
+  void release(const std::vector<int32_t>& blocks) {
+    for (auto it = blocks.rbegin(); it != blocks.rend(); ++it)
+      if (!hashed[(size_t)*it]) push_front(*it);
+    for (int32_t b : blocks)
+      if (hashed[(size_t)b]) push_back(b);
   }
 };
 
@@ -59,8 +112,30 @@ namespace {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// All-or-nothing append of one sequence.  Host memory for the table grows
-// before any pool state changes, so an allocation failure leaves it intact.
+// 64-bit FNV-1a over the parent hash (8 bytes, little-endian) and the block's
+// token ids (4 bytes each, little-endian, two's complement).
+constexpr uint64_t kFnvOffset = 14695981039346656037ull;
+constexpr uint64_t kFnvPrime = 1099511628211ull;
+
+uint64_t block_hash(uint64_t parent, const int32_t* tokens, int32_t n) {
+  uint64_t h = kFnvOffset;
+  for (int i = 0; i < 8; ++i) {
+    h ^= (parent >> (8 * i)) & 0xff;
+    h *= kFnvPrime;
+  }
+  for (int32_t t = 0; t < n; ++t) {
+    const uint32_t v = (uint32_t)tokens[t];
+    for (int i = 0; i < 4; ++i) {
+      h ^= (v >> (8 * i)) & 0xff;
+      h *= kFnvPrime;
+    }
+  }
+  return h;
+}
+
+// All-or-nothing append of one sequence.  Host memory for the table and the
+// pending-copy record grows before any pool state changes, so an allocation
+// failure leaves it intact.
 int append_one(pa_pool* p, int64_t seq_id, int32_t n, int64_t* slots, int32_t* pair) {
   auto it = p->seqs.find(seq_id);
   if (it == p->seqs.end()) return pa::fail(PA_ERR_INVALID, "append: unknown sequence %lld", (long long)seq_id);
@@ -70,28 +145,33 @@ int append_one(pa_pool* p, int64_t seq_id, int32_t n, int64_t* slots, int32_t* p
   const int64_t L = s.len;
   if (L > INT64_MAX - n) return pa::fail(PA_ERR_INVALID, "append: length overflow");
   const int64_t needed = cdiv(L + n, B) - (int64_t)s.blocks.size();
-  const bool cow = (L % B != 0) && p->ref[(size_t)s.blocks.back()] > 1;
+  const int32_t last = s.blocks.empty() ? -1 : s.blocks.back();
+  const bool cow = (L % B != 0) && (p->ref[(size_t)last] > 1 || p->pins[(size_t)last] > 0);
   if (needed + (cow ? 1 : 0) > p->count)
     return pa::fail(PA_ERR_NO_SPACE, "append: need %lld blocks, %d free",
                     (long long)(needed + (cow ? 1 : 0)), p->count);
   try {
     s.blocks.reserve(s.blocks.size() + (size_t)needed);
+    if (cow) p->pending.reserve(p->pending.size() + 1);
   } catch (const std::bad_alloc&) {
     return pa::fail(PA_ERR_INVALID, "append: out of host memory");
   }
   pair[0] = -1;
   pair[1] = -1;
   if (cow) {
-    const int32_t src = s.blocks.back();
-    const int32_t dst = p->pop_front();
+    const int32_t src = last;
+    const int32_t dst = p->pop();
     p->ref[(size_t)dst] = 1;
     p->ref[(size_t)src] -= 1;
+    p->hold[(size_t)src] += 1;
+    p->hold[(size_t)dst] += 1;
+    p->pending.emplace_back(src, dst);
     s.blocks.back() = dst;
     pair[0] = src;
     pair[1] = dst;
   }
   for (int64_t i = 0; i < needed; ++i) {
-    const int32_t b = p->pop_front();
+    const int32_t b = p->pop();
     p->ref[(size_t)b] = 1;
     s.blocks.push_back(b);
   }
@@ -116,9 +196,16 @@ int pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
                     num_blocks, block_size);
   pa_pool* p = new (std::nothrow) pa_pool();
   if (!p) return pa::fail(PA_ERR_INVALID, "pool_create: out of host memory");
+  const size_t N = (size_t)num_blocks;
   try {
-    p->ring.resize((size_t)num_blocks);
-    p->ref.assign((size_t)num_blocks, 0);
+    p->prev.assign(N, -1);
+    p->next.assign(N, -1);
+    p->queued.assign(N, 0);
+    p->ref.assign(N, 0);
+    p->pins.assign(N, 0);
+    p->hold.assign(N, 0);
+    p->hashed.assign(N, 0);
+    p->hash.assign(N, 0);
   } catch (const std::bad_alloc&) {
     delete p;
     return pa::fail(PA_ERR_INVALID, "pool_create: out of host memory");
@@ -126,7 +213,7 @@ int pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   if (order) {
-    std::vector<char> seen((size_t)num_blocks, 0);
+    std::vector<char> seen(N, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
       const int32_t b = order[i];
       if (b < 0 || b >= num_blocks || seen[(size_t)b]) {
@@ -134,13 +221,11 @@ int pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
         return pa::fail(PA_ERR_INVALID, "pool_create: initial order is not a permutation (entry %d = %d)", i, b);
       }
       seen[(size_t)b] = 1;
-      p->ring[(size_t)i] = b;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) p->push_back(order[i]);
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) p->ring[(size_t)i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) p->push_back(i);
   }
-  p->head = 0;
-  p->count = num_blocks;
   *out = p;
   return PA_OK;
 }
@@ -155,6 +240,74 @@ int pa_pool_add_seq(pa_pool* p, int64_t seq_id) {
     p->seqs.emplace(seq_id, pa_pool::Seq());
   } catch (const std::bad_alloc&) {
     return pa::fail(PA_ERR_INVALID, "add_seq: out of host memory");
+  }
+  return PA_OK;
+}
+
+int pa_pool_add_seq_cached(pa_pool* p, int64_t seq_id, const int32_t* tokens, int64_t n_tokens,
+                           int64_t* hit_tokens) {
+  pa::clear_error();
+  if (!p || !hit_tokens || n_tokens < 0 || (n_tokens > 0 && !tokens))
+    return pa::fail(PA_ERR_INVALID, "add_seq_cached: bad argument");
+  *hit_tokens = 0;
+  if (p->seqs.count(seq_id))
+    return pa::fail(PA_ERR_INVALID, "add_seq_cached: sequence %lld exists", (long long)seq_id);
+  const int64_t B = p->block_size;
+  // the hit blocks first (nothing changes yet), then one insertion
+  std::vector<int32_t> hits;
+  try {
+    uint64_t h = 0;
+    for (int64_t j = 0; (j + 1) * B <= n_tokens; ++j) {
+      h = block_hash(h, tokens + j * B, (int32_t)B);
+      auto it = p->cached.find(h);
+      if (it == p->cached.end()) break;
+      hits.push_back(it->second);
+    }
+    pa_pool::Seq s;
+    s.blocks = hits;
+    s.len = (int64_t)hits.size() * B;
+    p->seqs.emplace(seq_id, std::move(s));
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_INVALID, "add_seq_cached: out of host memory");
+  }
+  for (int32_t b : hits) p->touch(b);
+  *hit_tokens = (int64_t)hits.size() * B;
+  return PA_OK;
+}
+
+int pa_pool_cache_blocks(pa_pool* p, int64_t seq_id, const int32_t* tokens, int64_t n_tokens) {
+  pa::clear_error();
+  if (!p || n_tokens < 0 || (n_tokens > 0 && !tokens)) return pa::fail(PA_ERR_INVALID, "cache_blocks: bad argument");
+  auto it = p->seqs.find(seq_id);
+  if (it == p->seqs.end())
+    return pa::fail(PA_ERR_INVALID, "cache_blocks: unknown sequence %lld", (long long)seq_id);
+  const pa_pool::Seq& s = it->second;
+  if (n_tokens > s.len)
+    return pa::fail(PA_ERR_INVALID, "cache_blocks: %lld tokens but the sequence holds %lld", (long long)n_tokens,
+                    (long long)s.len);
+  const int64_t B = p->block_size;
+  std::vector<std::pair<int32_t, uint64_t>> chain;
+  try {
+    chain.reserve((size_t)(n_tokens / B));
+    p->cached.reserve(p->cached.size() + (size_t)(n_tokens / B));
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_INVALID, "cache_blocks: out of host memory");
+  }
+  uint64_t h = 0;
+  for (int64_t j = 0; (j + 1) * B <= n_tokens; ++j) {
+    h = block_hash(h, tokens + j * B, (int32_t)B);
+    const int32_t b = s.blocks[(size_t)j];
+    if (p->hashed[(size_t)b] && p->hash[(size_t)b] != h)
+      return pa::fail(PA_ERR_INVALID, "cache_blocks: block %d already holds other content", b);
+    chain.emplace_back(b, h);
+  }
+  for (const auto& bh : chain) {  // all checked: nothing changed on error
+    const int32_t b = bh.first;
+    if (!p->hashed[(size_t)b] && !p->cached.count(bh.second)) {
+      p->cached.emplace(bh.second, b);
+      p->hashed[(size_t)b] = 1;
+      p->hash[(size_t)b] = bh.second;
+    }
   }
   return PA_OK;
 }
@@ -204,18 +357,82 @@ int pa_pool_free_seq(pa_pool* p, int64_t seq_id) {
   auto it = p->seqs.find(seq_id);
   if (it == p->seqs.end()) return pa::fail(PA_ERR_INVALID, "free_seq: unknown sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& blocks = it->second.blocks;
-  // Blocks reaching zero, in release order (tail first).  Pushing them to the
-  // front in reverse leaves the first released block at the head.
-  std::vector<int32_t> released;
+  std::vector<int32_t> released;  // blocks losing their last reference, tail first
   try {
     released.reserve(blocks.size());
   } catch (const std::bad_alloc&) {
     return pa::fail(PA_ERR_INVALID, "free_seq: out of host memory");
   }
-  for (auto b = blocks.rbegin(); b != blocks.rend(); ++b)
-    if (--p->ref[(size_t)*b] == 0) released.push_back(*b);
-  for (auto b = released.rbegin(); b != released.rend(); ++b) p->push_front(*b);
+  for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
+    p->ref[(size_t)*b] -= 1;
+    if (!p->retained(*b)) released.push_back(*b);
+  }
+  p->release(released);
   p->seqs.erase(it);
+  return PA_OK;
+}
+
+int pa_pool_pin(pa_pool* p, int64_t seq_id, int64_t transfer_id, int32_t* blocks_out, int32_t cap, int32_t* n_out) {
+  pa::clear_error();
+  if (!p || !n_out || cap < 0 || (cap > 0 && !blocks_out)) return pa::fail(PA_ERR_INVALID, "pin: bad argument");
+  *n_out = 0;
+  auto it = p->seqs.find(seq_id);
+  if (it == p->seqs.end()) return pa::fail(PA_ERR_INVALID, "pin: unknown sequence %lld", (long long)seq_id);
+  if (p->transfers.count(transfer_id))
+    return pa::fail(PA_ERR_INVALID, "pin: transfer %lld exists", (long long)transfer_id);
+  const std::vector<int32_t>& blocks = it->second.blocks;
+  *n_out = (int32_t)blocks.size();
+  if ((int64_t)blocks.size() > cap)
+    return pa::fail(PA_ERR_INVALID, "pin: %zu blocks but room for %d", blocks.size(), cap);
+  try {
+    p->transfers.emplace(transfer_id, blocks);
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_INVALID, "pin: out of host memory");
+  }
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    p->pins[(size_t)blocks[i]] += 1;
+    blocks_out[i] = blocks[i];
+  }
+  return PA_OK;
+}
+
+int pa_pool_unpin(pa_pool* p, int64_t transfer_id) {
+  pa::clear_error();
+  if (!p) return pa::fail(PA_ERR_INVALID, "unpin: pool is NULL");
+  auto it = p->transfers.find(transfer_id);
+  if (it == p->transfers.end())
+    return pa::fail(PA_ERR_INVALID, "unpin: unknown transfer %lld", (long long)transfer_id);
+  std::vector<int32_t> released;
+  try {
+    released.reserve(it->second.size());
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_INVALID, "unpin: out of host memory");
+  }
+  for (auto b = it->second.rbegin(); b != it->second.rend(); ++b) {
+    p->pins[(size_t)*b] -= 1;
+    if (!p->retained(*b)) released.push_back(*b);
+  }
+  p->release(released);
+  p->transfers.erase(it);
+  return PA_OK;
+}
+
+int pa_pool_copies_done(pa_pool* p) {
+  pa::clear_error();
+  if (!p) return pa::fail(PA_ERR_INVALID, "copies_done: pool is NULL");
+  std::vector<int32_t> released;
+  try {
+    released.reserve(2 * p->pending.size());
+  } catch (const std::bad_alloc&) {
+    return pa::fail(PA_ERR_INVALID, "copies_done: out of host memory");
+  }
+  for (const auto& sd : p->pending)
+    for (int32_t b : {sd.first, sd.second}) {
+      p->hold[(size_t)b] -= 1;
+      if (!p->retained(b)) released.push_back(b);
+    }
+  p->pending.clear();
+  p->release(released);
   return PA_OK;
 }
 
@@ -249,12 +466,33 @@ int pa_pool_num_free(const pa_pool* p, int32_t* out) {
   return PA_OK;
 }
 
+int pa_pool_num_cached(const pa_pool* p, int32_t* out) {
+  pa::clear_error();
+  if (!p || !out) return pa::fail(PA_ERR_INVALID, "num_cached: NULL argument");
+  *out = (int32_t)p->cached.size();
+  return PA_OK;
+}
+
 int pa_pool_refcount(const pa_pool* p, int32_t block_id, int32_t* out) {
   pa::clear_error();
   if (!p || !out) return pa::fail(PA_ERR_INVALID, "refcount: NULL argument");
   if (block_id < 0 || block_id >= p->num_blocks)
     return pa::fail(PA_ERR_INVALID, "refcount: block %d out of range", block_id);
   *out = p->ref[(size_t)block_id];
+  return PA_OK;
+}
+
+int pa_pool_block_state(const pa_pool* p, int32_t block_id, int32_t* pins_out, int32_t* pending_out,
+                        uint64_t* hash_out, int32_t* hashed_out) {
+  pa::clear_error();
+  if (!p || !pins_out || !pending_out || !hash_out || !hashed_out)
+    return pa::fail(PA_ERR_INVALID, "block_state: NULL argument");
+  if (block_id < 0 || block_id >= p->num_blocks)
+    return pa::fail(PA_ERR_INVALID, "block_state: block %d out of range", block_id);
+  *pins_out = p->pins[(size_t)block_id];
+  *pending_out = p->hold[(size_t)block_id];
+  *hashed_out = p->hashed[(size_t)block_id];
+  *hash_out = p->hashed[(size_t)block_id] ? p->hash[(size_t)block_id] : 0;
   return PA_OK;
 }
 
@@ -270,8 +508,8 @@ int pa_pool_seq_len(const pa_pool* p, int64_t seq_id, int64_t* out) {
 int pa_pool_free_order(const pa_pool* p, int32_t* out, int32_t cap, int32_t* n_out) {
   pa::clear_error();
   if (!p || !n_out || cap < 0 || (cap > 0 && !out)) return pa::fail(PA_ERR_INVALID, "free_order: bad argument");
-  const int32_t n = std::min(cap, p->count);
-  for (int32_t i = 0; i < n; ++i) out[i] = p->at(i);
+  int32_t i = 0;
+  for (int32_t b = p->head; b >= 0 && i < cap; b = p->next[(size_t)b]) out[i++] = b;
   *n_out = p->count;
   return PA_OK;
 }
@@ -282,14 +520,18 @@ int pa_pool_check(const pa_pool* p) {
   const int32_t N = p->num_blocks;
   const int64_t B = p->block_size;
   if (p->count < 0 || p->count > N) return pa::fail(PA_ERR_INVALID, "check: free count %d", p->count);
-  std::vector<int32_t> owners((size_t)N, 0);
+  std::vector<int32_t> owners((size_t)N, 0), pins((size_t)N, 0), hold((size_t)N, 0);
   std::vector<char> in_free((size_t)N, 0);
-  for (int32_t i = 0; i < p->count; ++i) {
-    const int32_t b = p->at(i);
-    if (b < 0 || b >= N) return pa::fail(PA_ERR_INVALID, "check: free queue holds id %d", b);
+  int32_t walked = 0, last = -1;
+  for (int32_t b = p->head; b >= 0; b = p->next[(size_t)b]) {
+    if (b >= N) return pa::fail(PA_ERR_INVALID, "check: free queue holds id %d", b);
     if (in_free[(size_t)b]) return pa::fail(PA_ERR_INVALID, "check: block %d queued twice", b);
+    if (p->prev[(size_t)b] != last) return pa::fail(PA_ERR_INVALID, "check: queue links broken at block %d", b);
     in_free[(size_t)b] = 1;
+    last = b;
+    if (++walked > N) return pa::fail(PA_ERR_INVALID, "check: free queue has a cycle");
   }
+  if (walked != p->count || last != p->tail) return pa::fail(PA_ERR_INVALID, "check: free queue count or tail");
   std::vector<char> mark((size_t)N, 0);
   for (const auto& kv : p->seqs) {
     const auto& s = kv.second;
@@ -304,17 +546,33 @@ int pa_pool_check(const pa_pool* p) {
     }
     for (int32_t b : s.blocks) mark[(size_t)b] = 0;
   }
-  int32_t allocated = 0;
+  for (const auto& kv : p->transfers)
+    for (int32_t b : kv.second) pins[(size_t)b] += 1;
+  for (const auto& sd : p->pending) {
+    hold[(size_t)sd.first] += 1;
+    hold[(size_t)sd.second] += 1;
+  }
+  int32_t retained = 0, hashed = 0;
   for (int32_t b = 0; b < N; ++b) {
     if (owners[(size_t)b] != p->ref[(size_t)b])
       return pa::fail(PA_ERR_INVALID, "check: block %d has %d owners but refcount %d", b, owners[(size_t)b],
                       p->ref[(size_t)b]);
-    if ((bool)in_free[(size_t)b] == (p->ref[(size_t)b] > 0))
-      return pa::fail(PA_ERR_INVALID, "check: block %d free=%d refcount %d", b, (int)in_free[(size_t)b],
-                      p->ref[(size_t)b]);
-    if (p->ref[(size_t)b] > 0) ++allocated;
+    if (pins[(size_t)b] != p->pins[(size_t)b] || hold[(size_t)b] != p->hold[(size_t)b])
+      return pa::fail(PA_ERR_INVALID, "check: block %d pin or copy counts do not match their records", b);
+    const bool r = p->retained(b);
+    if ((bool)in_free[(size_t)b] == r || (bool)p->queued[(size_t)b] != (bool)in_free[(size_t)b])
+      return pa::fail(PA_ERR_INVALID, "check: block %d free=%d retained=%d", b, (int)in_free[(size_t)b], (int)r);
+    retained += r;
+    if (p->hashed[(size_t)b]) {
+      ++hashed;
+      auto it = p->cached.find(p->hash[(size_t)b]);
+      if (it == p->cached.end() || it->second != b)
+        return pa::fail(PA_ERR_INVALID, "check: block %d holds a hash the map does not point back to", b);
+    }
   }
-  if (allocated + p->count != N) return pa::fail(PA_ERR_INVALID, "check: free and allocated do not cover the pool");
+  if (retained + p->count != N) return pa::fail(PA_ERR_INVALID, "check: free and retained do not cover the pool");
+  if (hashed != (int32_t)p->cached.size()) return pa::fail(PA_ERR_INVALID, "check: hash map size %zu, %d hashed blocks",
+                                                          p->cached.size(), hashed);
   return PA_OK;
 }
 

@@ -67,6 +67,7 @@ class HipStep:
             if seqs:
                 n0 = np.concatenate([[0], np.cumsum([wl.new_lens[s] for s in seqs])])
                 self.write_part(lyr, kc, vc, seqs, [slots[n0[i]:n0[i + 1]] for i in range(len(seqs))], part=1)
+        B.pa_pool_copies_done(self.pool)
         width = bt_width or max(1, -(-max(wl.seq_lens + [1]) // wl.block_size))
         self.table, self.seq_lens = B.pa_pool_block_table(self.pool, list(range(S)), width, fill=0)
         self.table_dev = torch.from_numpy(self.table).to(device)

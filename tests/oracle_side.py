@@ -102,6 +102,7 @@ class OracleStep:
                 if pair is not None:
                     self.pairs.append(pair)
         cache_ops.copy_blocks([self.kc, self.vc], self.pairs, wl.num_blocks)
+        self.pool.copies_done()
         for s in range(S):
             if wl.new_lens[s]:
                 k, v = wl.step_kv(s, layer)

@@ -43,7 +43,10 @@ def test_pool_matches_oracle_model(seed):
     m = PoolModel(nb, bs, order)
     p = B.pa_pool_create(nb, bs, order)
     live = []
-    for op in workloads.pool_ops(seed, 200):
+    for i, op in enumerate(workloads.pool_ops(seed, 200)):
+        if i % 3 == 2:                            # the step's copies have been issued
+            m.copies_done()
+            B.pa_pool_copies_done(p)
         if op[0] == "add":
             m.add_seq(op[1])
             B.pa_pool_add_seq(p, op[1])
@@ -72,6 +75,128 @@ def test_pool_matches_oracle_model(seed):
         B.pa_pool_check(p)
         assert state(p, live) == model_state(m, live), (seed, op)
         assert B.pa_pool_num_free(p) == m.num_free()
+
+
+def full_state(pool, m, seqs):
+    """Native and model views of everything the pool holds per block."""
+    native = [B.pa_pool_block_state(pool, b) for b in range(pool.num_blocks)]
+    model = [(m.pins[b], m.hold[b], m.hash_of[b]) for b in range(m.num_blocks)]
+    return (state(pool, seqs), B.pa_pool_num_cached(pool), native), \
+        (model_state(m, seqs), m.num_cached(), model)
+
+
+def run_cached(seed):
+    """Drive the native pool and the model through pool_ops_cached(seed, 240)
+    and compare them after every operation; returns the number of prefix
+    lookups that hit."""
+    nb, bs = 40, 4
+    order = np.random.default_rng([seed, 5]).permutation(nb)
+    m = PoolModel(nb, bs, order)
+    p = B.pa_pool_create(nb, bs, order)
+    lists, history, live = {}, {}, []
+    next_tok = 0
+    hits = 0
+    for op in workloads.pool_ops_cached(seed, 240):
+        kind = op[0]
+        if kind == "add":
+            m.add_seq(op[1])
+            B.pa_pool_add_seq(p, op[1])
+            lists[op[1]] = []
+            live.append(op[1])
+        elif kind == "add_prefix":
+            s, donor, n = op[1], op[2], op[3]
+            toks = (lists.get(donor) or history.get(donor, []))[:n]
+            want = m.add_seq(s, toks)
+            got = B.pa_pool_add_seq_cached(p, s, np.array(toks, dtype=np.int32))
+            assert got == want, (seed, op)
+            hits += got > 0
+            lists[s] = list(toks[:got])
+            live.append(s)
+        elif kind == "fork":
+            m.fork(op[1], op[2])
+            B.pa_pool_fork(p, op[1], op[2])
+            lists[op[2]] = list(lists[op[1]])
+            live.append(op[2])
+        elif kind == "free":
+            m.free_seq(op[1])
+            B.pa_pool_free_seq(p, op[1])
+            history[op[1]] = lists.pop(op[1])
+            live.remove(op[1])
+        elif kind == "cache":
+            toks = lists[op[1]]
+            m.cache_blocks(op[1], toks)
+            B.pa_pool_cache_blocks(p, op[1], np.array(toks, dtype=np.int32))
+        elif kind == "pin":
+            assert B.pa_pool_pin(p, op[1], op[2]) == m.pin(op[1], op[2])
+        elif kind == "unpin":
+            m.unpin(op[1])
+            B.pa_pool_unpin(p, op[1])
+        elif kind == "done":
+            m.copies_done()
+            B.pa_pool_copies_done(p)
+        else:
+            s, n = op[1], op[2]
+            try:
+                want = m.append(s, n)
+            except ModelNoSpace:
+                want = "nospace"
+            try:
+                got = B.pa_pool_append(p, s, n)
+            except B.NoSpace:
+                got = "nospace"
+            assert (got if got == "nospace" else (got[0].tolist(), got[1])) == \
+                (want if want == "nospace" else (want[0], want[1])), (seed, op)
+            if want != "nospace":
+                lists[s].extend(range(next_tok, next_tok + n))
+                next_tok += n
+        B.pa_pool_check(p)
+        native, model = full_state(p, m, live)
+        assert native == model, (seed, op)
+    return hits
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_cached_pool_matches_oracle_model(seed):
+    """Prefix caching, block hashes, transfer pins and pending copies: 12
+    seeded runs of 240 operations agree with the model after every step
+    (tables, lengths, refcounts, free-queue order, hit lengths, pins, pending
+    holds and every block's hash)."""
+    run_cached(seed)
+
+
+def test_cached_pool_runs_exercise_prefix_hits():
+    assert sum(run_cached(seed) > 0 for seed in range(12)) >= 6
+
+
+def test_cached_pool_rejects_bad_calls():
+    p = B.pa_pool_create(8, 4)
+    B.pa_pool_add_seq(p, 0)
+    B.pa_pool_append(p, 0, 6)
+    toks = np.arange(6, dtype=np.int32)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_cache_blocks(p, 0, np.arange(7, dtype=np.int32))    # more tokens than held
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_cache_blocks(p, 9, toks)                             # unknown sequence
+    B.pa_pool_cache_blocks(p, 0, toks)
+    assert B.pa_pool_num_cached(p) == 1                                # one full block
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_cache_blocks(p, 0, toks[::-1].copy())               # other content, nothing changes
+    assert B.pa_pool_num_cached(p) == 1
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_add_seq_cached(p, 0, toks)                           # existing sequence
+    assert B.pa_pool_add_seq_cached(p, 1, toks) == 4
+    assert B.pa_pool_refcount(p, B.pa_pool_block_table(p, [1], 2)[0][0, 0]) == 2
+    B.pa_pool_pin(p, 0, 77)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_pin(p, 0, 77)                                        # existing transfer
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_unpin(p, 78)
+    n = B.c_i32()
+    out = np.empty(1, dtype=np.int32)
+    assert B.lib().pa_pool_pin(p.handle, 0, 79, B._i32p(out), 1, B.ctypes.byref(n)) == B.PA_ERR_INVALID
+    assert n.value == 2                                                # the room needed
+    B.pa_pool_unpin(p, 77)
+    B.pa_pool_check(p)
 
 
 def test_r7_walk_native(golden):
