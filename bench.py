@@ -464,6 +464,59 @@ def measure_mixed(torch, B, hip_side, workloads, block_size, reps=10):
     return res
 
 
+def measure_host_pool(B, num_blocks=26_785, block_size=16, prompt=8192, batch=64, reps=200):
+    """Host cost of the pool calls a serving step makes, on a pool the size of
+    the 52.32 GiB Llama-3-8B budget: one decode step's append for `batch`
+    sequences, hashing a prompt's full blocks into the prefix cache, a fully
+    hitting prefix lookup of the same prompt, and freeing it again."""
+    L = B.lib()
+    pool = B.pa_pool_create(num_blocks, block_size)
+    h = pool.handle
+    toks = np.arange(prompt, dtype=np.int32)
+    tp = toks.ctypes.data_as(B.P_i32)
+    hit = B.c_i64()
+    B.pa_pool_add_seq(pool, 0)
+    B.pa_pool_append(pool, 0, prompt)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        if L.pa_pool_cache_blocks(h, 0, tp, prompt) != 0:
+            raise RuntimeError(L.pa_last_error().decode())
+    t_cache = (time.perf_counter() - t0) / reps
+    t_hit = t_free = 0.0
+    for r in range(reps):
+        t0 = time.perf_counter()
+        rc = L.pa_pool_add_seq_cached(h, 1 + r, tp, prompt, B.ctypes.byref(hit))
+        t1 = time.perf_counter()
+        rc |= L.pa_pool_free_seq(h, 1 + r)
+        t2 = time.perf_counter()
+        if rc != 0 or hit.value != prompt:
+            raise RuntimeError("prefix lookup did not hit the whole prompt")
+        t_hit += t1 - t0
+        t_free += t2 - t1
+    ids = np.arange(1000, 1000 + batch, dtype=np.int64)
+    ones = np.full(batch, 1, dtype=np.int32)
+    slots = np.empty(batch, dtype=np.int64)
+    pairs = np.empty((batch, 2), dtype=np.int32)
+    done = B.c_i32()
+    for i in ids:
+        B.pa_pool_add_seq(pool, int(i))
+        B.pa_pool_append(pool, int(i), 600)
+    args = (h, ids.ctypes.data_as(B.P_i64), ones.ctypes.data_as(B.P_i32), batch,
+            slots.ctypes.data_as(B.P_i64), pairs.ctypes.data_as(B.P_i32), B.ctypes.byref(done))
+    n = 1000
+    t0 = time.perf_counter()
+    for _ in range(n):
+        if L.pa_pool_append_batch(*args) != 0:
+            raise RuntimeError(L.pa_last_error().decode())
+    t_app = (time.perf_counter() - t0) / n
+    B.pa_pool_check(pool)
+    return {"num_blocks": num_blocks, "block_size": block_size, "prompt_tokens": prompt,
+            "cache_blocks_us": round(t_cache * 1e6, 1),
+            "hash_mtok_per_s": round(prompt / t_cache / 1e6, 1),
+            "prefix_hit_us": round(t_hit / reps * 1e6, 1), "free_seq_us": round(t_free / reps * 1e6, 1),
+            f"append_batch_{batch}x1_us": round(t_app * 1e6, 2)}
+
+
 def counter_run(kind, reps):
     """Launch only one kernel kind, for rocprofv3 --pmc passes:
     'decode' = the decode call of this workload on rotating pools,
@@ -626,6 +679,7 @@ def main():
             print(f"[bench] mixed step, block size {bs}", file=sys.stderr, flush=True)
             cfg[f"mixed_step_b{bs}"] = measure_mixed(torch, B, hip_side, workloads, bs)
         line["configs"] = cfg
+    line["host_pool"] = measure_host_pool(B)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -77,9 +77,9 @@ def block_hash(parent: int, tokens) -> int:
     """64-bit FNV-1a over the parent hash (8 bytes LE) and the token ids
     (4 bytes LE each)."""
     h = FNV_OFFSET
-    data = int(parent & MASK64).to_bytes(8, "little")
+    data = (int(parent) & MASK64).to_bytes(8, "little")
     for t in tokens:
-        data += int(t & 0xFFFFFFFF).to_bytes(4, "little")
+        data += (int(t) & 0xFFFFFFFF).to_bytes(4, "little")
     for byte in data:
         h ^= byte
         h = (h * FNV_PRIME) & MASK64
