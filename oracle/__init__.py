@@ -12,6 +12,7 @@ Sources (the three web pages on PagedAttention):
     attention metadata and the CPU reference allocator sections.
   * "The pantry of pigeonholes" (blog.lo0.es): "The maths that matter".
   * "Memory management" (llm-inference-explained): "Maths" and "Code".
+    Its knobs table and "With KV quantisation" name the FP8 KV cache.
 
 Modules
   sizing      closed forms of the pages' capacity arithmetic
@@ -19,6 +20,8 @@ Modules
   cache_ops   the slot mapping from the block table, the slot scatter and the
               whole-block copy
   attention   fp64 decode and chunked-prefill attention by table gather
+  fp8         E4M3 encoding, decoding and per-cache-scale quantisation of
+              K/V elements (the FP8 KV cache)
 
 Every floating-point result is computed in fp64 from exact bf16 inputs.
 bf16 values travel as uint16 bit patterns (numpy has no bf16 type).

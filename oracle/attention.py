@@ -30,6 +30,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import fp8
+
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact bf16 -> fp64: a bf16 pattern is the upper half of an fp32."""
@@ -37,9 +39,13 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def gather_sequence(cache: np.ndarray, table_row, seq_len: int, kv_head: int) -> np.ndarray:
+def gather_sequence(cache: np.ndarray, table_row, seq_len: int, kv_head: int,
+                    scale: float = 1.0) -> np.ndarray:
     """Contiguous [seq_len, D] fp64 rows of one KV head, gathered through the
-    table: logical position p is row p % B of physical block table_row[p // B]."""
+    table: logical position p is row p % B of physical block table_row[p // B].
+
+    A uint16 cache holds bf16 bits (scale must be 1); a uint8 cache holds
+    E4M3 codes whose values are decode(code) * scale (oracle.fp8)."""
     B = cache.shape[1]
     nblk = -(-seq_len // B)
     pieces = []
@@ -49,7 +55,11 @@ def gather_sequence(cache: np.ndarray, table_row, seq_len: int, kv_head: int) ->
         pieces.append(cache[blk, :valid, kv_head, :])
     if not pieces:
         return np.zeros((0, cache.shape[3]), dtype=np.float64)
-    return bf16_to_f64(np.concatenate(pieces, axis=0))
+    rows = np.concatenate(pieces, axis=0)
+    if cache.dtype == np.uint8:
+        return fp8.dequantize(rows, scale)
+    assert scale == 1.0, "a bf16 cache has no scale"
+    return bf16_to_f64(rows)
 
 
 def softmax_attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
@@ -76,10 +86,12 @@ def softmax_attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def paged_decode(q_bits: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
-                 block_tables: np.ndarray, seq_lens, scale: float):
+                 block_tables: np.ndarray, seq_lens, scale: float,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
     """Single-query attention per sequence over its paged K/V.
 
-    q_bits [S, Hq, D] bf16 bits; caches [NB, B, Hkv, D] bf16 bits;
+    q_bits [S, Hq, D] bf16 bits; caches [NB, B, Hkv, D] bf16 bits, or E4M3
+    codes (uint8) with per-cache scales k_scale / v_scale;
     block_tables [S, W] int32; seq_lens [S].
     Returns out [S, Hq, D] fp64 and lse [S, Hq] fp64.
     """
@@ -92,8 +104,8 @@ def paged_decode(q_bits: np.ndarray, key_cache: np.ndarray, value_cache: np.ndar
     for s in range(S):
         n = int(seq_lens[s])
         for g in range(Hkv):
-            k = gather_sequence(key_cache, block_tables[s], n, g)
-            v = gather_sequence(value_cache, block_tables[s], n, g)
+            k = gather_sequence(key_cache, block_tables[s], n, g, k_scale)
+            v = gather_sequence(value_cache, block_tables[s], n, g, v_scale)
             heads = slice(g * G, (g + 1) * G)
             o, l = softmax_attend(q[s, heads], k, v, scale)
             out[s, heads] = o

@@ -8,6 +8,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import fp8
+
 
 PAD_SLOT = -1
 
@@ -100,3 +102,14 @@ def copy_blocks(caches, pairs, num_blocks: int) -> None:
             raise ValueError("axis 0 of every cache must index the blocks")
         rows = cache[srcs].copy()
         cache[dsts] = rows
+
+
+def reshape_and_cache_fp8(key_cache: np.ndarray, value_cache: np.ndarray,
+                          key: np.ndarray, value: np.ndarray, slot_mapping: np.ndarray,
+                          k_scale: float, v_scale: float) -> None:
+    """The slot write of reshape_and_cache into E4M3 caches (uint8): each
+    bf16 element is stored as its E4M3 code at the cache's scale
+    (oracle.fp8.quantize_bf16), then written at its slot exactly as above."""
+    assert key_cache.dtype == np.uint8 and value_cache.dtype == np.uint8
+    reshape_and_cache(key_cache, value_cache, fp8.quantize_bf16(key, k_scale),
+                      fp8.quantize_bf16(value, v_scale), slot_mapping)
