@@ -51,18 +51,18 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def kv_bytes(seq_lens, num_kv_heads, head_dim):
-    """K and V rows of every attended token (bf16)."""
-    return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * 2 * num_kv_heads * head_dim * 2
+def kv_bytes(seq_lens, num_kv_heads, head_dim, elem_bytes=2):
+    """K and V rows of every attended token (bf16, or 1-byte E4M3)."""
+    return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * 2 * num_kv_heads * head_dim * elem_bytes
 
 
-def decode_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, block_size):
-    """Algorithmic bytes of one decode call: K/V rows, q in and out (bf16)
-    and the block-table entries walked."""
+def decode_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, elem_bytes=2):
+    """Algorithmic bytes of one decode call: K/V rows (elem_bytes per
+    element), q in and out (bf16) and the block-table entries walked."""
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     qo = len(seq_lens) * num_q_heads * head_dim * 2 * 2
     table = int(np.sum(-(-seq_lens // block_size))) * 4
-    return kv_bytes(seq_lens, num_kv_heads, head_dim) + qo + table
+    return kv_bytes(seq_lens, num_kv_heads, head_dim, elem_bytes) + qo + table
 
 
 class Instance:
@@ -517,6 +517,69 @@ def measure_host_pool(B, num_blocks=26_785, block_size=16, prompt=8192, batch=64
             f"append_batch_{batch}x1_us": round(t_app * 1e6, 2)}
 
 
+def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), instances=8, reps=48):
+    """Decode over E4M3 caches: the 64-sequence Llama-3-8B decode batch
+    (8 pools rotated, about 590 MB of K/V codes, so that no pool stays in the
+    last-level cache between its calls) and the 32-layer long-context pool;
+    plus the quantising cache write of one decode step's 64 tokens."""
+    wls = [workloads.llama_decode(seed_offset=i) for i in range(instances)]
+    hs = [hip_side.HipStep(w, gen="device", fp8=scales) for w in wls]
+    wl = wls[0]
+    S = wl.num_seqs
+    qs = [workloads.device_query(w.seed, S, w.num_q_heads, w.head_dim) for w in wls]
+    msl = max(max(w.seq_lens) for w in wls)
+    out = torch.empty_like(qs[0])
+    rot = [0]
+
+    def nxt():
+        i = rot[0] % instances
+        B.pa_paged_decode_fp8(out, qs[i], hs[i].kc, hs[i].vc, hs[i].table_dev, hs[i].seq_lens_dev, msl,
+                              wl.scale, *scales, partition_size=0)
+        rot[0] += 1
+    sec = time_launches(torch, nxt, reps)
+    alg = np.mean([decode_bytes(w.seq_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, 1)
+                   for w in wls])
+    gbps = alg / sec / 1e9
+    # one step's write: 64 new tokens quantised into their slots
+    k = hip_side.to_device(workloads.normal_bf16(np.random.default_rng(1), (S, wl.num_kv_heads, wl.head_dim)))
+    slots = torch.from_numpy(hs[0].step_slots.astype(np.int64)).cuda()
+    t_w = time_launches(torch, lambda: B.pa_reshape_and_cache_fp8(k, k, hs[0].kc, hs[0].vc, slots, *scales), 200)
+    res = {"workload": f"{wl.name}, E4M3 K/V with per-cache scales", "scales": list(scales),
+           "kernel": DECODE_KERNEL.replace(">", ", fp8>"), "decode_us": round(sec * 1e6, 2),
+           "bytes_per_launch": int(alg), "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
+           "seqs_per_s": round(S / sec, 1), "write_64_tokens_us": round(t_w * 1e6, 2)}
+    del hs, qs
+    torch.cuda.empty_cache()
+
+    # the 32-layer long-context pool in E4M3 (half the bytes of the bf16 pool)
+    wl = workloads.long_context()
+    L, S, P = wl.num_layers, wl.num_seqs, 2048
+    kv = torch.full((L, 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), 0x7F,
+                    dtype=torch.uint8, device="cuda")
+    h = hip_side.HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]),
+                         layers=[(l, kv[l, 0], kv[l, 1]) for l in range(L)], fp8=scales)
+    msl = max(wl.seq_lens)
+    qs = [workloads.device_query(wl.seed, S, wl.num_q_heads, wl.head_dim, layer=l) for l in range(L)]
+    out = torch.empty_like(qs[0])
+    ws = torch.empty(B.pa_paged_decode_workspace_size(S, wl.num_q_heads, wl.head_dim, msl, P),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        for l in range(L):
+            B.pa_paged_decode_fp8(out, qs[l], kv[l, 0], kv[l, 1], h.table_dev, h.seq_lens_dev, msl, wl.scale,
+                                  *scales, partition_size=P, workspace=ws)
+    sec = time_launches(torch, step, 3)
+    per_layer = decode_bytes(wl.seq_lens, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, 1)
+    gbps = per_layer * L / sec / 1e9
+    res["long_context"] = {"pool_gib": round(kv.numel() / 2**30, 2), "partition_size": P,
+                           "step_ms": round(sec * 1e3, 3), "layer_us": round(sec / L * 1e6, 1),
+                           "bytes_per_layer": per_layer, "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
+                           "seqs_per_s": round(S / sec, 1)}
+    del kv, h, qs
+    torch.cuda.empty_cache()
+    return res
+
+
 def counter_run(kind, reps):
     """Launch only one kernel kind, for rocprofv3 --pmc passes:
     'decode' = the decode call of this workload on rotating pools,
@@ -678,6 +741,8 @@ def main():
         for bs in (1, 16, 32):
             print(f"[bench] mixed step, block size {bs}", file=sys.stderr, flush=True)
             cfg[f"mixed_step_b{bs}"] = measure_mixed(torch, B, hip_side, workloads, bs)
+        print("[bench] E4M3 KV cache decode", file=sys.stderr, flush=True)
+        cfg["fp8_decode"] = measure_fp8_decode(torch, B, hip_side, workloads)
         line["configs"] = cfg
     line["host_pool"] = measure_host_pool(B)
     if not args.no_cpu_baseline:

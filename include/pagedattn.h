@@ -282,6 +282,26 @@ int pa_reshape_and_cache(const void* key, int64_t key_row_stride,
                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, void* stream);
 
+/* pa_reshape_and_cache into E4M3 caches (one byte per element): each bf16
+ * element x is stored as the E4M3 code of the fp32 product x * r, where
+ * r = fp32(1 / k_scale) for K and fp32(1 / v_scale) for V; the code's value
+ * times the scale stands for x.  E4M3 here is the finite-only form (bias 7,
+ * subnormals m * 2^-9, largest finite 448, S.1111.111 = NaN); rounding is to
+ * nearest, ties to even; magnitudes above 448 saturate to +-448; NaN stays NaN.
+ * ("The pantry of pigeonholes", knobs table and "With KV quantisation": an
+ * FP8 KV cache halves the bytes per token.  Format, scaling and rounding are
+ * not given there; the ones above are this library's.)
+ * key_cache / value_cache: device uint8 [num_blocks][block_size][num_kv_heads]
+ * [head_dim] codes, block b at b * cache_block_stride bytes (a multiple of 16).
+ * Errors as pa_reshape_and_cache, plus PA_ERR_INVALID for a scale that is not
+ * positive and finite. */
+int pa_reshape_and_cache_fp8(const void* key, int64_t key_row_stride,
+                             const void* value, int64_t value_row_stride,
+                             void* key_cache, void* value_cache, int64_t cache_block_stride,
+                             int32_t num_blocks, const int64_t* slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, float k_scale, float v_scale, void* stream);
+
 /* Copy whole blocks: for every cache c and pair (src, dst),
  * bytes [0, block_bytes) of block dst <- the same bytes of block src, where
  * block b of cache c starts at caches[c] + b * cache_block_stride_bytes.
@@ -335,6 +355,23 @@ int pa_paged_decode(void* out, float* lse, const void* q,
                     int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                     int32_t partition_size, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_paged_decode over E4M3 caches written by pa_reshape_and_cache_fp8: K_t
+ * and V_t above are the codes' values times k_scale and v_scale.  Codes are
+ * converted to bf16 exactly; the logits use scale * k_scale (rounded to fp32)
+ * and the output is multiplied by v_scale.  cache_block_stride is in bytes
+ * and must be a multiple of 16.  Same workspace as pa_paged_decode.
+ * ("The pantry of pigeonholes", knobs table and "With KV quantisation".)
+ * Errors as pa_paged_decode, plus PA_ERR_INVALID for a scale that is not
+ * positive and finite. */
+int pa_paged_decode_fp8(void* out, float* lse, const void* q,
+                        const void* key_cache, const void* value_cache,
+                        int64_t cache_block_stride, int32_t num_blocks,
+                        const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                        int32_t partition_size, float scale, float k_scale, float v_scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Chunked-prefill attention of query chunks over their paged context.
  * Request i's queries are rows query_start_loc[i] .. query_start_loc[i+1]-1 of

@@ -69,10 +69,15 @@ _SIGS = {
     "pa_slot_mapping": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]),
     "pa_reshape_and_cache": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp,
                                      c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_reshape_and_cache_fp8": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp,
+                                         c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_vp]),
     "pa_copy_blocks": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_i32, P_i32, c_i32, c_vp]),
     "pa_paged_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_paged_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "pa_paged_decode_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
+                                    c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
+                                    c_vp, c_sz, c_vp]),
     "pa_paged_prefill": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
 }
@@ -296,11 +301,18 @@ def _bf16(t, name):
         raise InvalidArgument(PA_ERR_INVALID, f"{name} must be a bf16 device tensor")
 
 
-def _cache_geometry(kc, vc):
-    """[NB, B, Hkv, D] views whose inner three dims are contiguous; returns
+def _cache_geometry(kc, vc, fp8=False):
+    """[NB, B, Hkv, D] views whose inner three dims are contiguous (bf16, or
+    one-byte E4M3 codes as uint8 / float8_e4m3fn with fp8); returns
     (num_blocks, block_size, num_kv_heads, head_dim, block_stride)."""
-    _bf16(kc, "key_cache")
-    _bf16(vc, "value_cache")
+    import torch
+    if fp8:
+        for t, name in ((kc, "key_cache"), (vc, "value_cache")):
+            if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_cuda:
+                raise InvalidArgument(PA_ERR_INVALID, f"{name} must be a uint8 or float8_e4m3fn device tensor")
+    else:
+        _bf16(kc, "key_cache")
+        _bf16(vc, "value_cache")
     if kc.dim() != 4 or kc.shape != vc.shape or kc.stride() != vc.stride():
         raise InvalidArgument(PA_ERR_INVALID, "caches must be matching [NB, B, Hkv, D] views")
     nb, bs, hkv, d = kc.shape
@@ -336,8 +348,19 @@ def pa_slot_mapping(block_tables, query_start_loc, seq_lens, block_size, num_tok
 def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
     """key/value [T, Hkv, D] bf16 (heads and dims contiguous); slot_mapping
     int64 [T] device tensor."""
+    _reshape(key, value, key_cache, value_cache, slot_mapping, stream, False, 1.0, 1.0)
+
+
+def pa_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale=1.0, v_scale=1.0,
+                             stream=None):
+    """As pa_reshape_and_cache into E4M3 caches (uint8 or float8_e4m3fn
+    [NB, B, Hkv, D]) with per-cache scales."""
+    _reshape(key, value, key_cache, value_cache, slot_mapping, stream, True, k_scale, v_scale)
+
+
+def _reshape(key, value, key_cache, value_cache, slot_mapping, stream, fp8, k_scale, v_scale):
     import torch
-    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache, fp8)
     _bf16(key, "key")
     _bf16(value, "value")
     T = key.shape[0]
@@ -347,9 +370,12 @@ def pa_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, strea
     if slot_mapping.dtype != torch.int64 or not slot_mapping.is_cuda or slot_mapping.shape != (T,) \
             or not slot_mapping.is_contiguous():
         raise InvalidArgument(PA_ERR_INVALID, "slot_mapping must be a contiguous int64 device tensor [T]")
-    _check(lib().pa_reshape_and_cache(key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
-                                      key_cache.data_ptr(), value_cache.data_ptr(), bstride, nb,
-                                      slot_mapping.data_ptr(), T, hkv, d, bs, _stream(key_cache, stream)))
+    args = (key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0), key_cache.data_ptr(),
+            value_cache.data_ptr(), bstride, nb, slot_mapping.data_ptr(), T, hkv, d, bs)
+    if fp8:
+        _check(lib().pa_reshape_and_cache_fp8(*args, k_scale, v_scale, _stream(key_cache, stream)))
+    else:
+        _check(lib().pa_reshape_and_cache(*args, _stream(key_cache, stream)))
 
 
 def pa_copy_blocks(caches, pairs, stream=None):
@@ -381,8 +407,22 @@ def pa_paged_decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_
     """out/q [S, Hq, D] bf16 contiguous; block_tables int32 [S, W] (row
     stride bt_stride = its stride(0)); seq_lens int32 [S]; lse fp32 [S, Hq]
     or None; workspace a uint8 device tensor (allocated here if None)."""
+    _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
+            workspace, stream, False, 1.0, 1.0)
+
+
+def pa_paged_decode_fp8(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale,
+                        k_scale=1.0, v_scale=1.0, partition_size=512, lse=None, workspace=None, stream=None):
+    """pa_paged_decode over E4M3 caches (uint8 or float8_e4m3fn) with
+    per-cache scales."""
+    _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
+            workspace, stream, True, k_scale, v_scale)
+
+
+def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
+            workspace, stream, fp8, k_scale, v_scale):
     import torch
-    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache, fp8)
     _bf16(q, "q")
     _bf16(out, "out")
     S, hq = q.shape[0], q.shape[1]
@@ -400,11 +440,13 @@ def pa_paged_decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().pa_paged_decode(out.data_ptr(), lse.data_ptr() if lse is not None else None, q.data_ptr(),
-                                 key_cache.data_ptr(), value_cache.data_ptr(), bstride, nb,
-                                 block_tables.data_ptr(), block_tables.stride(0), seq_lens.data_ptr(),
-                                 S, hq, hkv, d, bs, max_seq_len, partition_size, scale, ws_ptr, ws_bytes,
-                                 _stream(q, stream)))
+    args = (out.data_ptr(), lse.data_ptr() if lse is not None else None, q.data_ptr(), key_cache.data_ptr(),
+            value_cache.data_ptr(), bstride, nb, block_tables.data_ptr(), block_tables.stride(0),
+            seq_lens.data_ptr(), S, hq, hkv, d, bs, max_seq_len, partition_size, scale)
+    if fp8:
+        _check(lib().pa_paged_decode_fp8(*args, k_scale, v_scale, ws_ptr, ws_bytes, _stream(q, stream)))
+    else:
+        _check(lib().pa_paged_decode(*args, ws_ptr, ws_bytes, _stream(q, stream)))
 
 
 def pa_paged_prefill(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,

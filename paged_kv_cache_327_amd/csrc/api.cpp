@@ -88,15 +88,23 @@ int pa_slot_mapping(int64_t* slot_mapping, int32_t num_tokens, const int32_t* bl
   return hip_status(fn, pa::launch_slot_mapping(a, stream));
 }
 
-int pa_reshape_and_cache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
-                         void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
-                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int reshape_impl(const char* fn, const void* key, int64_t key_row_stride, const void* value,
+                 int64_t value_row_stride, void* key_cache, void* value_cache, int64_t cache_block_stride,
+                 int32_t num_blocks, const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, bool fp8, float k_scale, float v_scale, void* stream) {
   pa::clear_error();
-  const char* fn = "reshape_and_cache";
   if (int rc = check_heads(fn, num_kv_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (fp8 && cache_block_stride % 16)
+    return pa::fail(PA_ERR_INVALID, "%s: cache_block_stride %lld must be a multiple of 16 for E4M3 caches", fn,
+                    (long long)cache_block_stride);
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f && k_scale < __builtin_huge_valf() && v_scale < __builtin_huge_valf()))
+    return pa::fail(PA_ERR_INVALID, "%s: k_scale and v_scale must be positive and finite", fn);
   if (num_tokens < 0) return pa::fail(PA_ERR_INVALID, "%s: num_tokens %d < 0", fn, num_tokens);
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !slot_mapping) return pa::fail(PA_ERR_INVALID, "%s: NULL input", fn);
@@ -105,8 +113,31 @@ int pa_reshape_and_cache(const void* key, int64_t key_row_stride, const void* va
   if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 || value_row_stride % 8)
     return pa::fail(PA_ERR_INVALID, "%s: row strides must be multiples of 8 and >= Hkv*D", fn);
   pa::ReshapeArgs a{key, key_row_stride, value, value_row_stride, key_cache, value_cache, cache_block_stride,
-                    (int64_t)num_blocks * block_size, slot_mapping, num_tokens, (int32_t)row, ilog2(block_size)};
+                    (int64_t)num_blocks * block_size, slot_mapping, num_tokens, (int32_t)row, ilog2(block_size),
+                    fp8 ? 1 : 0, fp8 ? 1.0f / k_scale : 1.f, fp8 ? 1.0f / v_scale : 1.f};
   return hip_status(fn, pa::launch_reshape_and_cache(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_reshape_and_cache(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                         void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, void* stream) {
+  return reshape_impl("reshape_and_cache", key, key_row_stride, value, value_row_stride, key_cache, value_cache,
+                      cache_block_stride, num_blocks, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+                      false, 1.f, 1.f, stream);
+}
+
+int pa_reshape_and_cache_fp8(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                             void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                             const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, float k_scale, float v_scale, void* stream) {
+  return reshape_impl("reshape_and_cache_fp8", key, key_row_stride, value, value_row_stride, key_cache,
+                      value_cache, cache_block_stride, num_blocks, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                      block_size, true, k_scale, v_scale, stream);
 }
 
 int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
@@ -145,16 +176,25 @@ size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
   return (size_t)(out_bytes + rows * 4);
 }
 
-int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,
-                    int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
-                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t block_size, int32_t max_seq_len, int32_t partition_size, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* key_cache,
+                const void* value_cache, int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
+                int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                int32_t partition_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
   pa::clear_error();
-  const char* fn = "paged_decode";
   if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (fp8 && cache_block_stride % 16)
+    return pa::fail(PA_ERR_INVALID, "%s: cache_block_stride %lld must be a multiple of 16 for E4M3 caches", fn,
+                    (long long)cache_block_stride);
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f && k_scale < __builtin_huge_valf() && v_scale < __builtin_huge_valf()))
+    return pa::fail(PA_ERR_INVALID, "%s: k_scale and v_scale must be positive and finite", fn);
   if (num_seqs < 0) return pa::fail(PA_ERR_INVALID, "%s: num_seqs < 0", fn);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !block_tables || !seq_lens) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
@@ -194,13 +234,40 @@ int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache,
   a.max_seq_len = max_seq_len;
   a.partition_size = P;
   a.max_parts = (int32_t)parts;
-  a.scale = scale;
+  a.scale = fp8 ? scale * k_scale : scale;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  a.fp8 = fp8 ? 1 : 0;
   if (parts > 1) {
     const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
     a.ws_out = static_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((rows * head_dim * 4) + 255) / 256 * 256);
   }
   return hip_status(fn, pa::launch_paged_decode(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,
+                    int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_seq_len, int32_t partition_size, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("paged_decode", out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                     block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_seq_len, partition_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_fp8(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,
+                        int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
+                        int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                        int32_t partition_size, float scale, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode_impl("paged_decode_fp8", out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                     block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_seq_len, partition_size, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 int pa_paged_prefill(void* out, const void* q, const void* key_cache, const void* value_cache,

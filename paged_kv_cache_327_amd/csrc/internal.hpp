@@ -26,6 +26,9 @@ struct ReshapeArgs {
   int32_t num_tokens;
   int32_t row_elems;  // num_kv_heads * head_dim
   int32_t log2_block_size;
+  int32_t fp8;        // caches hold E4M3 codes (1 byte per element)
+  float k_recip;      // fp32(1 / k_scale), fp32(1 / v_scale) (fp8 only)
+  float v_recip;
 };
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream);
 
@@ -61,7 +64,9 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t partition_size;  // > 0, multiple of 64 and of the block size
   int32_t max_parts;
-  float scale;
+  float scale;     // softmax scale (times k_scale for E4M3 caches)
+  float v_scale;   // 1 for bf16 caches
+  int32_t fp8;     // caches hold E4M3 codes (1 byte per element)
   float* ws_out;  // [S][Hq][max_parts][D]   (max_parts > 1 only)
   float* ws_lse;  // [S][Hq][max_parts]
 };

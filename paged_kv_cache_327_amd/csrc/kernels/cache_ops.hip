@@ -1,5 +1,5 @@
-// Slot mapping, KV-cache write by slot mapping and whole-block copy-on-write
-// copies.
+// Slot mapping, KV-cache write by slot mapping (bf16, or E4M3 with a
+// per-cache scale) and whole-block copy-on-write copies.
 //
 // The write and the copy move bits with 16-byte vector loads and stores and
 // are bound by HBM bandwidth; the slot mapping is integer work on a few
@@ -15,6 +15,23 @@ namespace {
 // 16-byte pieces.  "PagedAttention: fragmentation, blocks, block tables",
 // 3. The slot mapping: the write goes to flat row slot of block-major storage,
 // block slot / B at offset slot % B; the padding id (-1) writes nothing.
+//
+// E4M3 caches (F8): each bf16 element x is stored as the E4M3 code of the
+// fp32 product x * r, r = fp32(1 / scale) of its cache ("The pantry of
+// pigeonholes", knobs table: the KV cache dtype sets the bytes per element).
+// A lane turns 8 bf16 (16 bytes) into 8 codes (8 bytes).
+__device__ __forceinline__ uint2 quantize8(const uint4 x, float r) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = e4m3_code(__uint_as_float(w[i] << 16) * r);
+    c[2 * i + 1] = e4m3_code(__uint_as_float(w[i] & 0xffff0000u) * r);
+  }
+  return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+}
+
+template <bool F8>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
@@ -26,14 +43,25 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
   const int64_t dst = blk * a.cache_block_stride + off * a.row_elems;
   const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + t * a.key_row_stride);
   const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.value) + t * a.value_row_stride);
-  uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
-  uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
   const int nvec = a.row_elems >> 3;
-  for (int c = lane; c < nvec; c += 64) {
-    const uint4 k = ks[c];
-    const uint4 v = vs[c];
-    kd[c] = k;
-    vd[c] = v;
+  if constexpr (F8) {
+    uint2* kd = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.key_cache) + dst);
+    uint2* vd = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.value_cache) + dst);
+    for (int c = lane; c < nvec; c += 64) {
+      const uint4 k = ks[c];
+      const uint4 v = vs[c];
+      kd[c] = quantize8(k, a.k_recip);
+      vd[c] = quantize8(v, a.v_recip);
+    }
+  } else {
+    uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
+    uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
+    for (int c = lane; c < nvec; c += 64) {
+      const uint4 k = ks[c];
+      const uint4 v = vs[c];
+      kd[c] = k;
+      vd[c] = v;
+    }
   }
 }
 
@@ -107,7 +135,10 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyBatch b) {
 
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
   const unsigned grid = (unsigned)((a.num_tokens + 3) / 4);
-  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+  if (a.fp8)
+    hipLaunchKernelGGL(reshape_and_cache_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

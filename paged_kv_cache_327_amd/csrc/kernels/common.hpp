@@ -57,6 +57,42 @@ __device__ __forceinline__ uint32_t dpp(uint32_t x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// E4M3 (finite-only form: bias 7, subnormals m * 2^-9, largest finite 448,
+// S.1111.111 = NaN) code of an fp32 value: round to nearest, ties to even;
+// magnitudes above 448 and infinities saturate to 448; NaN gives the NaN code.
+// Written from the format's definition with integer operations, so the result
+// does not depend on a conversion instruction's rounding or clamping mode.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t bits = __float_as_uint(x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t mag = bits & 0x7fffffffu;
+  uint32_t code;
+  if (mag > 0x7f800000u) {
+    code = 0x7fu;                                   // NaN
+  } else if (mag >= 0x43e00000u) {
+    code = 0x7eu;                                   // >= 448: saturate
+  } else if (mag < 0x3c800000u) {
+    // below 2^-6: a multiple of 2^-9 (code 8, the smallest normal, on carry);
+    // scaling by 2^9 is exact and rint rounds half to even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  } else {
+    // keep 3 of the 23 mantissa bits, round to nearest even on the other 20;
+    // a carry moves into the exponent; rebias 127 -> 7
+    const uint32_t r = mag + 0x7ffffu + ((mag >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+    code = code > 0x7eu ? 0x7eu : code;
+  }
+  return code | sign;
+}
+
+// Two E4M3 codes (bytes 0-1 of w, or bytes 2-3 with HI) as a packed bf16 pair
+// (lo = the lower byte).  Exact: every E4M3 value is a bf16 value, and the
+// scale operand is 1.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -36,6 +36,8 @@
 //    sequence with one partition writes its bf16 output directly; otherwise
 //    partials (normalised output, log2 lse) go to the workspace for the merge
 //    pass.
+#include <type_traits>
+
 #include "../internal.hpp"
 #include "common.hpp"
 
@@ -49,12 +51,45 @@ constexpr int kChunk = 512;   // tokens whose table entries are staged at once (
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-template <int D>
+// A lane's share of the K and V rows of its group's two tokens: D / 8
+// elements each, bf16 in 16-byte pieces (element e is d = 64 (e / 8) + 8 li +
+// e % 8), or E4M3 codes in one 16- or 8-byte piece (element e is d =
+// (D / 8) li + e).  Either way a group's 8 lanes read a row's contiguous bytes.
+template <int D, bool F8>
 struct KV {
-  static constexpr int kPieces = D / 64;  // 16-byte pieces per lane per token
+  static constexpr int kPieces = D / 64;  // 16-byte bf16 pieces per lane per token
   uint4 k[2][kPieces];
   uint4 v[2][kPieces];
 };
+template <int D>
+struct KV<D, true> {
+  using Piece = typename std::conditional<D == 128, uint4, uint2>::type;
+  Piece k[2];
+  Piece v[2];
+};
+
+// Element index e = 8 k + i of a lane -> dimension d.
+template <int D, bool F8>
+__device__ __forceinline__ int lane_dim(int k, int i, int li) {
+  return F8 ? (D / 8) * li + 8 * k + i : 64 * k + 8 * li + i;
+}
+
+// The lane's D / 8 elements of one token as D / 16 packed bf16 pairs, in
+// element order (E4M3 codes are converted exactly).
+template <int D, bool F8, typename P>
+__device__ __forceinline__ void bf16_words(const P& piece, uint32_t (&w)[D / 16]) {
+  const uint32_t* raw = reinterpret_cast<const uint32_t*>(&piece);
+  if constexpr (F8) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      w[2 * j] = e4m3x2_to_bf16x2<false>(raw[j]);
+      w[2 * j + 1] = e4m3x2_to_bf16x2<true>(raw[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) w[j] = raw[j];
+  }
+}
 
 // Sum of 8 per-lane values over the 8 lanes of a group, scattered: lane i
 // of the group ends with the total of value i.  Pairs are (i, 7 - i), then
@@ -88,9 +123,11 @@ __device__ __forceinline__ void broadcast4(uint32_t x, bool up4, uint32_t (&out)
   out[3] = up4 ? b : b2;
 }
 
-template <int D, int G, bool BIG>
+template <int D, int G, bool BIG, bool F8>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
-  constexpr int PPL = D / 64;
+  using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
+  constexpr int PPL = D / 64;   // groups of 8 elements per lane per token
+  constexpr int NW = D / 16;    // packed bf16 pairs per lane per token
   constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score slot per lane per set
   __shared__ int32_t s_bt[BIG ? 1 : kChunk];
   __shared__ float s_acc[kWaves][4][G][D];
@@ -110,8 +147,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const int Bmask = (1 << lgB) - 1;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
   const int64_t bstride = a.cache_block_stride;
-  const uint16_t* kcache = static_cast<const uint16_t*>(a.key_cache);
-  const uint16_t* vcache = static_cast<const uint16_t*>(a.value_cache);
+  const T* kcache = static_cast<const T*>(a.key_cache);
+  const T* vcache = static_cast<const T*>(a.value_cache);
   const int32_t* bt_row = a.block_tables + (int64_t)s * a.bt_stride;
   const int width = (a.max_seq_len + Bmask) >> lgB;   // table entries that may be read
   const float scale = a.scale * kLog2e;
@@ -125,7 +162,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < PPL; ++k)
       qr[h][k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                                 ((int64_t)s * a.num_q_heads + g * G + h) * D + 64 * k + 8 * li);
+                                                 ((int64_t)s * a.num_q_heads + g * G + h) * D +
+                                                 lane_dim<D, F8>(k, 0, li));
   auto stage_table = [&](int c0) {
     const int j0 = c0 >> lgB;
     int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
@@ -160,7 +198,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 
   // per-lane constant part of a K/V element offset (BIG: tokens grp, grp + 8
   // of the tile relative to its first token)
-  const int lane_off = g * D + 8 * li;
+  const int lane_off = g * D + lane_dim<D, F8>(0, 0, li);
 
   float m_own[NSET], l_own[NSET], acc[G][PPL][8];
 #pragma unroll
@@ -185,27 +223,35 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     // issued before the V loads so q.k can start first.
     // (with `fetched`, the block id is `pre`, fetched early for tile t0, or
     // pre_start for a tile past c1)
-    auto load = [&](int t0, KV<D>& r, bool fetched = false, int pre = 0) __attribute__((always_inline)) {
+    auto load = [&](int t0, KV<D, F8>& r, bool fetched = false, int pre = 0) __attribute__((always_inline)) {
       if (BIG) {
         const int tc = t0 < c1 ? t0 : c0;          // wave-uniform
         int blk = __builtin_amdgcn_readfirstlane(fetched ? (t0 < c1 ? pre : pre_start) : bt_row[tc >> lgB]);
         blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
         const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
-        const uint16_t* kb = kcache + base;
-        const uint16_t* vb = vcache + base;
+        const T* kb = kcache + base;
+        const T* vb = vcache + base;
         // tokens past c1 read the tile's first token (valid): their slots may
         // hold anything, and a zero weight times a NaN is NaN
         int64_t roff[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) roff[u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
+        if constexpr (F8) {
+          using P = typename KV<D, F8>::Piece;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2; ++u) r.k[u] = *reinterpret_cast<const P*>(kb + roff[u]);
 #pragma unroll
-          for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kb + roff[u] + 64 * k);
+          for (int u = 0; u < 2; ++u) r.v[u] = *reinterpret_cast<const P*>(vb + roff[u]);
+        } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vb + roff[u] + 64 * k);
+            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kb + roff[u] + 64 * k);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vb + roff[u] + 64 * k);
+        }
       } else {
         int64_t off[2];
 #pragma unroll
@@ -215,20 +261,31 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
           const int64_t blk = s_bt[(t >> lgB) - j0];
           off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
         }
+        if constexpr (F8) {
+          using P = typename KV<D, F8>::Piece;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2; ++u) r.k[u] = *reinterpret_cast<const P*>(kcache + off[u]);
 #pragma unroll
-          for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kcache + off[u] + 64 * k);
+          for (int u = 0; u < 2; ++u) r.v[u] = *reinterpret_cast<const P*>(vcache + off[u]);
+        } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vcache + off[u] + 64 * k);
+            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kcache + off[u] + 64 * k);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vcache + off[u] + 64 * k);
+        }
       }
     };
 
-    auto compute = [&](int t0, const KV<D>& r) __attribute__((always_inline)) {
+    auto compute = [&](int t0, const KV<D, F8>& r) __attribute__((always_inline)) {
       const bool valid0 = t0 + grp < c1;
       const bool valid1 = t0 + grp + 8 < c1;
+      uint32_t kw[2][NW];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) bf16_words<D, F8>(r.k[u], kw[u]);
       // partial dots: slot v of set j is head 4 j + v / 2, token v % 2
       float x[NSET];
 #pragma unroll
@@ -239,13 +296,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
           const int h = 4 * j + (v >> 1), u = v & 1;
           float d = 0.f;
           if (h < G) {
+            const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h][0]);
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-              const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h][k]);
-              const uint32_t* kk = reinterpret_cast<const uint32_t*>(&r.k[u][k]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) d = dot2_bf16(qq[i], kk[i], d);
-            }
+            for (int jw = 0; jw < NW; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
           }
           w[v] = d;
         }
@@ -294,20 +347,19 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
         broadcast4(pk, up4, pp[j]);
       }
       // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
+      uint32_t v0[NW], v1[NW];
+      bf16_words<D, F8>(r.v[0], v0);
+      bf16_words<D, F8>(r.v[1], v1);
 #pragma unroll
-      for (int k = 0; k < PPL; ++k) {
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&r.v[0][k]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&r.v[1][k]);
+      for (int jw = 0; jw < NW; ++jw) {
+        const int k = jw >> 2, i = jw & 3;
+        const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = __builtin_amdgcn_perm(v1[i], v0[i], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(v1[i], v0[i], 0x07060302u);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t w = pp[h >> 2][h & 3];
-            acc[h][k][2 * i] = dot2_bf16(w, lo, acc[h][k][2 * i]);
-            acc[h][k][2 * i + 1] = dot2_bf16(w, hi, acc[h][k][2 * i + 1]);
-          }
+        for (int h = 0; h < G; ++h) {
+          const uint32_t w = pp[h >> 2][h & 3];
+          acc[h][k][2 * i] = dot2_bf16(w, lo, acc[h][k][2 * i]);
+          acc[h][k][2 * i + 1] = dot2_bf16(w, hi, acc[h][k][2 * i + 1]);
         }
       }
     };
@@ -323,7 +375,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     constexpr int kStep = kWaves * kTile;
     int t = c0 + wave * kTile;
     const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
-    KV<D> r[kBuffers];
+    KV<D, F8> r[kBuffers];
 #pragma unroll
     for (int k = 0; k + 1 < kBuffers; ++k) load(t + k * kStep, r[k], BIG && k < 2, k == 0 ? pre0 : pre1);
     int i = 0;
@@ -378,7 +430,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < PPL; ++k)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s_acc[wave][row][h][64 * k + 8 * li + i] = acc[h][k][i];
+        for (int i = 0; i < 8; ++i) s_acc[wave][row][h][lane_dim<D, F8>(k, i, li)] = acc[h][k][i];
     if (!b0) {
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
@@ -416,7 +468,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
     const int hq = g * G + h;
     const int64_t orow = (int64_t)s * a.num_q_heads + hq;
-    const float val = L > 0.f ? A / L : 0.f;
+    const float val = L > 0.f ? A / L * a.v_scale : 0.f;
     const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;
     if (nparts == 1) {
       static_cast<uint16_t*>(a.out)[orow * D + d] = to_bf16(val);
@@ -459,10 +511,17 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
 template <int D, int G>
 int launch_g(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  if (a.log2_block_size >= 4)
-    hipLaunchKernelGGL((decode_partition_kernel<D, G, true>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_partition_kernel<D, G, false>), grid, dim3(256), 0, st, a);
+  if (a.fp8) {
+    if (a.log2_block_size >= 4)
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.log2_block_size >= 4)
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false>), grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, st, a);

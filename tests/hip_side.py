@@ -19,8 +19,12 @@ def to_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def nan_cache(wl, device="cuda"):
+def nan_cache(wl, device="cuda", fp8=False):
+    """Caches filled with NaN: bf16 NaN, or the E4M3 NaN code 0x7F."""
     shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    if fp8:
+        return (torch.full(shape, 0x7F, dtype=torch.uint8, device=device),
+                torch.full(shape, 0x7F, dtype=torch.uint8, device=device))
     return (torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device),
             torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device))
 
@@ -30,16 +34,19 @@ class HipStep:
     pa_copy_blocks for the step's copy-on-write pairs and
     pa_reshape_and_cache for every write."""
 
-    def __init__(self, wl, layer=0, bt_width=None, device="cuda", caches=None, gen="host", layers=None):
+    def __init__(self, wl, layer=0, bt_width=None, device="cuda", caches=None, gen="host", layers=None,
+                 fp8=None):
         """gen="host": numpy draws (workloads.seq_kv_bits); gen="device":
         torch-generator draws on the GPU (workloads.device_seq_kv).  With
         ``layers`` = [(layer, kc, vc), ...] every layer's caches receive that
-        layer's tokens at the same slots (one pool shared by all layers)."""
+        layer's tokens at the same slots (one pool shared by all layers).
+        fp8 = (k_scale, v_scale) makes the caches E4M3."""
         S = wl.num_seqs
         self.wl = wl
         self.gen = gen
+        self.fp8 = fp8
         self.pool = B.pa_pool_create(wl.num_blocks, wl.block_size, wl.free_order)
-        self.kc, self.vc = caches if caches is not None else nan_cache(wl, device)
+        self.kc, self.vc = caches if caches is not None else nan_cache(wl, device, fp8 is not None)
         targets = layers if layers is not None else [(layer, self.kc, self.vc)]
         forked = {b for _, b in wl.forks}
         ctx_seqs, ctx_slots = [], []
@@ -100,7 +107,13 @@ class HipStep:
         k = torch.cat(ks)
         v = torch.cat(vs)
         sl = torch.from_numpy(np.concatenate(ss)).to(kc.device)
-        B.pa_reshape_and_cache(k, v, kc, vc, sl)
+        self._store(k, v, kc, vc, sl)
+
+    def _store(self, k, v, kc, vc, sl):
+        if self.fp8 is None:
+            B.pa_reshape_and_cache(k, v, kc, vc, sl)
+        else:
+            B.pa_reshape_and_cache_fp8(k, v, kc, vc, sl, *self.fp8)
 
     def logical_kv_bits(self, seq, layer=0):
         """Host copies (bf16 bits) of the logical K/V of ``seq`` exactly as
@@ -123,7 +136,7 @@ class HipStep:
         k = to_device(k_bits, self.kc.device)
         v = to_device(v_bits, self.kc.device)
         sl = torch.from_numpy(np.asarray(slots, dtype=np.int64)).to(self.kc.device)
-        B.pa_reshape_and_cache(k, v, self.kc, self.vc, sl)
+        self._store(k, v, self.kc, self.vc, sl)
 
     def decode(self, q_bits, partition_size=512, rows=None, max_seq_len=None, caches=None):
         rows = list(range(self.wl.num_seqs)) if rows is None else list(rows)
@@ -135,8 +148,12 @@ class HipStep:
         bt = self.table_dev[rows].contiguous()
         sl = self.seq_lens_dev[rows].contiguous()
         msl = max_seq_len or max(1, int(self.seq_lens[rows].max()))
-        B.pa_paged_decode(out, q, kc, vc, bt, sl, msl, self.wl.scale,
-                          partition_size=partition_size, lse=lse)
+        if self.fp8 is None:
+            B.pa_paged_decode(out, q, kc, vc, bt, sl, msl, self.wl.scale,
+                              partition_size=partition_size, lse=lse)
+        else:
+            B.pa_paged_decode_fp8(out, q, kc, vc, bt, sl, msl, self.wl.scale, *self.fp8,
+                                  partition_size=partition_size, lse=lse)
         return out, lse
 
     def prefill(self, q_bits, seqs, causal=True, max_seq_len=None):

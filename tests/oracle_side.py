@@ -74,12 +74,18 @@ class OracleStep:
     numpy caches: context appends, forks, step appends with their
     copy-on-write copies, then the step's cache writes."""
 
-    def __init__(self, wl, layer=0, bt_width=None):
+    def __init__(self, wl, layer=0, bt_width=None, fp8=None):
+        """fp8 = (k_scale, v_scale): E4M3 caches (oracle.fp8), NaN code 0x7F
+        where nothing was written."""
         S = wl.num_seqs
         self.wl = wl
+        self.fp8 = fp8
         self.pool = PoolModel(wl.num_blocks, wl.block_size, wl.free_order)
         shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
-        self.kc = np.full(shape, NAN_BF16, dtype=np.uint16)
+        if fp8 is None:
+            self.kc = np.full(shape, NAN_BF16, dtype=np.uint16)
+        else:
+            self.kc = np.full(shape, 0x7F, dtype=np.uint8)
         self.vc = self.kc.copy()
         forked = {b for _, b in wl.forks}
         for s in range(S):
@@ -90,7 +96,7 @@ class OracleStep:
                 slots, pair = self.pool.append(s, wl.ctx_lens[s])
                 assert pair is None
                 k, v = wl.ctx_kv(s, layer)
-                cache_ops.reshape_and_cache(self.kc, self.vc, k, v, np.array(slots))
+                self._store(k, v, np.array(slots))
             for a, b in wl.forks:
                 if a == s:
                     self.pool.fork(a, b)
@@ -107,8 +113,17 @@ class OracleStep:
             if wl.new_lens[s]:
                 k, v = wl.step_kv(s, layer)
                 n0 = sum(wl.new_lens[:s])
-                cache_ops.reshape_and_cache(self.kc, self.vc, k, v,
-                                            np.array(self.step_slots[n0:n0 + wl.new_lens[s]]))
+                self._store(k, v, np.array(self.step_slots[n0:n0 + wl.new_lens[s]]))
         self.step_slots = np.array(self.step_slots, dtype=np.int64)
         self.table = table_array(self.pool, range(S), bt_width)
         self.seq_lens = np.array([self.pool.seq_len(s) for s in range(S)], dtype=np.int32)
+
+    def _store(self, k, v, slots):
+        if self.fp8 is None:
+            cache_ops.reshape_and_cache(self.kc, self.vc, k, v, slots)
+        else:
+            cache_ops.reshape_and_cache_fp8(self.kc, self.vc, k, v, slots, *self.fp8)
+
+    def scales(self):
+        """Keyword arguments of the oracle attention for these caches."""
+        return {} if self.fp8 is None else {"k_scale": self.fp8[0], "v_scale": self.fp8[1]}
