@@ -45,6 +45,27 @@ def slot_mapping(block_tables: np.ndarray, query_start_loc, seq_lens, block_size
     return out
 
 
+def map_to_kernel_blocks(block_ids, blocks_per_alloc: int) -> np.ndarray:
+    """Allocation-block ids -> kernel-block ids.
+
+    "PagedAttention: fragmentation, blocks, block tables", the block-table
+    append (the hybrid-blocks branch) and the decoupling paragraph: an
+    allocation block of B_alloc tokens is split into k = B_alloc / B_kernel
+    kernel blocks, so a 32-token allocation block can feed a kernel that
+    wants 16-token pages.  Reading: allocation block b is the same memory as
+    kernel blocks b*k .. b*k + k - 1 of the cache viewed with B_kernel-token
+    blocks, and every allocation id of a row expands, in order, to its k
+    kernel ids (so a row of n ids becomes n*k ids).
+    """
+    ids = np.asarray(block_ids, dtype=np.int64).reshape(-1)
+    k = int(blocks_per_alloc)
+    out = []
+    for b in ids:
+        for j in range(k):
+            out.append(int(b) * k + j)
+    return np.array(out, dtype=np.int64)
+
+
 def reshape_and_cache(key_cache: np.ndarray, value_cache: np.ndarray,
                       key: np.ndarray, value: np.ndarray,
                       slot_mapping: np.ndarray) -> None:

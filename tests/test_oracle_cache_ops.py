@@ -134,3 +134,50 @@ def test_slot_mapping_padding_ids():
     assert got.tolist() == [-1, 28, 29]
     got = cache_ops.slot_mapping(bt, [0, 2], [10], 4, num_tokens=2)
     assert got.tolist() == [-1, -1]          # positions 8, 9 -> table index 2, past the row
+
+
+def test_kernel_blocks_small_example():
+    """Splitting each 32-token allocation block into two 16-token kernel
+    blocks: ids 3, 0, 7 become 6, 7, 0, 1, 14, 15; one kernel block per
+    allocation block is the identity."""
+    assert cache_ops.map_to_kernel_blocks([3, 0, 7], 2).tolist() == [6, 7, 0, 1, 14, 15]
+    assert cache_ops.map_to_kernel_blocks([5, 2], 1).tolist() == [5, 2]
+    assert cache_ops.map_to_kernel_blocks([1], 4).tolist() == [4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_kernel_block_view_changes_no_result(k):
+    """The same memory read through the kernel-block table (B / k-token
+    blocks) gives the same slots and the same attention, bit for bit, as
+    through the allocation table (B-token blocks)."""
+    from oracle import attention
+    from oracle.pool_model import PoolModel
+    rng = np.random.default_rng([12, k])
+    B, nb, hkv, d = 32, 10, 2, 64
+    lens = [1, 31, 32, 70, 100]
+    pool = PoolModel(nb * 2, B, rng.permutation(nb * 2))
+    kc = np.zeros((nb * 2, B, hkv, d), dtype=np.uint16)
+    vc = kc.copy()
+    for s, n in enumerate(lens):
+        pool.add_seq(s)
+        slots, _ = pool.append(s, n)
+        kb = (rng.standard_normal((n, hkv, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        vb = (rng.standard_normal((n, hkv, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        cache_ops.reshape_and_cache(kc, vc, kb, vb, np.array(slots))
+    width = max(-(-n // B) for n in lens)
+    alloc = np.zeros((len(lens), width), dtype=np.int64)
+    kern = np.zeros((len(lens), width * k), dtype=np.int64)
+    for s in range(len(lens)):
+        row = pool.block_table(s)
+        alloc[s, :len(row)] = row
+        kern[s, :len(row) * k] = cache_ops.map_to_kernel_blocks(row, k)
+    kck = kc.reshape(nb * 2 * k, B // k, hkv, d)
+    vck = vc.reshape(nb * 2 * k, B // k, hkv, d)
+    q = (rng.standard_normal((len(lens), 4, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    o1, l1 = attention.paged_decode(q, kc, vc, alloc, lens, 0.125)
+    o2, l2 = attention.paged_decode(q, kck, vck, kern, lens, 0.125)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    qsl = np.cumsum([0] + [min(n, 5) for n in lens])
+    s1 = cache_ops.slot_mapping(alloc, qsl, lens, B, int(qsl[-1]))
+    s2 = cache_ops.slot_mapping(kern, qsl, lens, B // k, int(qsl[-1]))
+    assert np.array_equal(s1, s2) and (s1 >= 0).all()
