@@ -207,6 +207,23 @@ int pa_pool_copies_done(pa_pool* pool);
 int pa_pool_block_table(const pa_pool* pool, const int64_t* seq_ids, int32_t n_seqs,
                         int32_t* table_out, int32_t bt_stride, int32_t* seq_lens_out);
 
+/* pa_pool_block_table for a kernel that wants smaller pages: every
+ * allocation block b of a row (block_size tokens) is written as the k =
+ * block_size / kernel_block_size kernel blocks b*k .. b*k + k - 1, which are
+ * the same memory when the cache is viewed with kernel_block_size-token
+ * blocks ([num_blocks * k][kernel_block_size][Hkv][D]).  Row i gets
+ * ceil(len_i / block_size) * k entries; slots are unchanged by the view.
+ * ("PagedAttention: fragmentation, blocks, block tables", the block-table
+ * append with hybrid blocks, and the paragraph on decoupling the allocation
+ * block from the kernel block: a 32-token allocation block can feed a kernel
+ * that wants 16-token pages.)
+ * Errors: PA_ERR_INVALID if kernel_block_size does not divide block_size, a
+ * row does not fit bt_stride, num_blocks * k exceeds INT32_MAX or a sequence
+ * is unknown (nothing written). */
+int pa_pool_kernel_block_table(const pa_pool* pool, const int64_t* seq_ids, int32_t n_seqs,
+                               int32_t kernel_block_size, int32_t* table_out, int32_t bt_stride,
+                               int32_t* seq_lens_out);
+
 /* Number of free blocks (the capacity test is a subtraction against it). */
 int pa_pool_num_free(const pa_pool* pool, int32_t* out);
 /* Number of cached block hashes (each names one block, free or in use). */

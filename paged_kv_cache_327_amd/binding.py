@@ -60,6 +60,7 @@ _SIGS = {
     "pa_pool_append_batch": (c_i32, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, P_i32]),
     "pa_pool_free_seq": (c_i32, [c_vp, c_i64]),
     "pa_pool_block_table": (c_i32, [c_vp, P_i64, c_i32, P_i32, c_i32, P_i32]),
+    "pa_pool_kernel_block_table": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, c_i32, P_i32]),
     "pa_pool_num_free": (c_i32, [c_vp, P_i32]),
     "pa_pool_refcount": (c_i32, [c_vp, c_i32, P_i32]),
     "pa_pool_seq_len": (c_i32, [c_vp, c_i64, P_i64]),
@@ -248,6 +249,17 @@ def pa_pool_block_table(pool, seq_ids, bt_stride, out=None, fill=0):
     assert table.dtype == np.int32 and table.flags.c_contiguous and table.shape == (len(ids), bt_stride)
     lens = np.empty(len(ids), dtype=np.int32)
     _check(lib().pa_pool_block_table(pool.handle, _i64p(ids), len(ids), _i32p(table), bt_stride, _i32p(lens)))
+    return table, lens
+
+
+def pa_pool_kernel_block_table(pool, seq_ids, kernel_block_size, bt_stride, fill=0):
+    """Returns (table int32 [n, bt_stride] of kernel-block ids, seq_lens
+    int32 [n])."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    table = np.full((len(ids), bt_stride), fill, dtype=np.int32)
+    lens = np.empty(len(ids), dtype=np.int32)
+    _check(lib().pa_pool_kernel_block_table(pool.handle, _i64p(ids), len(ids), kernel_block_size, _i32p(table),
+                                            bt_stride, _i32p(lens)))
     return table, lens
 
 

@@ -14,8 +14,13 @@
 //    split head_dim into 16-byte pieces (lane i holds d = 8i..8i+7 and, for
 //    D = 128, d = 64+8i..64+8i+7), so every K/V row load is a coalesced
 //    16-byte-per-lane access of the token's contiguous row.  A wave handles
-//    16-token tiles (2 tokens per group) and keeps the next two tiles' loads
-//    in flight while it computes the current one.
+//    16-token tiles (2 tokens per group) and keeps the next tile's loads in
+//    flight while it computes the current one.
+//  * E4M3 caches (one byte per element): lane i holds d = (D/8) i ..
+//    (D/8) i + D/8 - 1 of a token in one 16- (or 8-) byte load; the codes
+//    become bf16 pairs exactly (v_cvt_scalef32_pk_bf16_fp8 at scale 1) and
+//    the rest is the bf16 path; k_scale is folded into the logit scale and
+//    v_scale into the output.
 //  * Block lookup: with B >= 16 a tile lies inside one block, whose id is a
 //    scalar load from the table row and whose base address is scalar; with
 //    B < 16 the partition's table entries are staged in LDS and each token
@@ -45,27 +50,32 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kTile = 16;     // tokens per wave iteration
+constexpr int kHalf = 16;     // tokens of a half tile: two per lane group, inside one block when B >= 16
 constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
+constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1).  Two halves
+                              // (a tile's loads as large as with bf16 rows) measured 3%
+                              // faster on 16K-32K-token sequences but 8% slower on the
+                              // 600-token batch, so one half is kept
 constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-// A lane's share of the K and V rows of its group's two tokens: D / 8
-// elements each, bf16 in 16-byte pieces (element e is d = 64 (e / 8) + 8 li +
-// e % 8), or E4M3 codes in one 16- or 8-byte piece (element e is d =
-// (D / 8) li + e).  Either way a group's 8 lanes read a row's contiguous bytes.
-template <int D, bool F8>
+// A lane's share of the K and V rows of its group's NT tokens (two per half
+// tile): D / 8 elements each, bf16 in 16-byte pieces (element e is d =
+// 64 (e / 8) + 8 li + e % 8), or E4M3 codes in one 16- or 8-byte piece
+// (element e is d = (D / 8) li + e).  Either way a group's 8 lanes read a
+// row's contiguous bytes.
+template <int D, bool F8, int NT>
 struct KV {
   static constexpr int kPieces = D / 64;  // 16-byte bf16 pieces per lane per token
-  uint4 k[2][kPieces];
-  uint4 v[2][kPieces];
+  uint4 k[NT][kPieces];
+  uint4 v[NT][kPieces];
 };
-template <int D>
-struct KV<D, true> {
+template <int D, int NT>
+struct KV<D, true, NT> {
   using Piece = typename std::conditional<D == 128, uint4, uint2>::type;
-  Piece k[2];
-  Piece v[2];
+  Piece k[NT];
+  Piece v[NT];
 };
 
 // Element index e = 8 k + i of a lane -> dimension d.
@@ -128,6 +138,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
   constexpr int PPL = D / 64;   // groups of 8 elements per lane per token
   constexpr int NW = D / 16;    // packed bf16 pairs per lane per token
+  constexpr int NH = F8 ? kHalves8 : 1;   // half tiles per tile
+  constexpr int kTile = kHalf * NH;       // tokens per wave iteration
+  using KVt = KV<D, F8, 2 * NH>;
   constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score slot per lane per set
   __shared__ int32_t s_bt[BIG ? 1 : kChunk];
   __shared__ float s_acc[kWaves][4][G][D];
@@ -175,17 +188,22 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     }
   };
   if (!BIG) stage_table(start);
-  // BIG: the table entries of this wave's first two tiles and of the
-  // partition's first token, fetched before the length is known (indexes
-  // are kept inside the row), so that the first K/V loads wait for one
-  // round trip instead of two.
-  int pre0 = 0, pre1 = 0, pre_start = 0;
+  // BIG: the table entries of the halves of this wave's first two tiles and
+  // of the partition's first token, fetched before the length is known
+  // (indexes are kept inside the row), so that the first K/V loads wait for
+  // one round trip instead of two.
+  int pre[2][NH] = {}, pre_start = 0;
   if constexpr (BIG) {
     const int wmax = width - 1;
     const int tw = start + wave * kTile;
-    const int i0 = tw >> lgB, i1 = (tw + kWaves * kTile) >> lgB, is = start >> lgB;
-    pre0 = bt_row[i0 < wmax ? i0 : wmax];
-    pre1 = bt_row[i1 < wmax ? i1 : wmax];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int hf = 0; hf < NH; ++hf) {
+        const int i = (tw + k * kWaves * kTile + hf * kHalf) >> lgB;
+        pre[k][hf] = bt_row[i < wmax ? i : wmax];
+      }
+    const int is = start >> lgB;
     pre_start = bt_row[is < wmax ? is : wmax];
   }
 
@@ -221,71 +239,90 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     // prefetches the compiler's wait counts stay exact and the next tiles'
     // loads remain in flight while this one is computed.  All K loads are
     // issued before the V loads so q.k can start first.
-    // (with `fetched`, the block id is `pre`, fetched early for tile t0, or
-    // pre_start for a tile past c1)
-    auto load = [&](int t0, KV<D, F8>& r, bool fetched = false, int pre = 0) __attribute__((always_inline)) {
+    // (with `fetched`, the block ids are `pf`, fetched early for tile t0, or
+    // pre_start for a half past c1)
+    auto load = [&](int t0, KVt& r, bool fetched = false, const int* pf = nullptr) __attribute__((always_inline)) {
       if (BIG) {
-        const int tc = t0 < c1 ? t0 : c0;          // wave-uniform
-        int blk = __builtin_amdgcn_readfirstlane(fetched ? (t0 < c1 ? pre : pre_start) : bt_row[tc >> lgB]);
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
-        const T* kb = kcache + base;
-        const T* vb = vcache + base;
-        // tokens past c1 read the tile's first token (valid): their slots may
-        // hold anything, and a zero weight times a NaN is NaN
-        int64_t roff[2];
+        const T* kb[NH];
+        const T* vb[NH];
+        int64_t roff[NH][2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) roff[u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
+        for (int hf = 0; hf < NH; ++hf) {
+          const int th = t0 + hf * kHalf;
+          const int tc = th < c1 ? th : c0;          // wave-uniform
+          int blk = __builtin_amdgcn_readfirstlane(fetched ? (th < c1 ? pf[hf] : pre_start) : bt_row[tc >> lgB]);
+          blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+          const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
+          kb[hf] = kcache + base;
+          vb[hf] = vcache + base;
+          // tokens past c1 read the half's first token (valid): their slots
+          // may hold anything, and a zero weight times a NaN is NaN
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            roff[hf][u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
+        }
         if constexpr (F8) {
-          using P = typename KV<D, F8>::Piece;
+          using P = typename KVt::Piece;
 #pragma unroll
-          for (int u = 0; u < 2; ++u) r.k[u] = *reinterpret_cast<const P*>(kb + roff[u]);
+          for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) r.v[u] = *reinterpret_cast<const P*>(vb + roff[u]);
+            for (int u = 0; u < 2; ++u) r.k[2 * hf + u] = *reinterpret_cast<const P*>(kb[hf] + roff[hf][u]);
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) r.v[2 * hf + u] = *reinterpret_cast<const P*>(vb[hf] + roff[hf][u]);
         } else {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kb + roff[u] + 64 * k);
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+              for (int k = 0; k < PPL; ++k)
+                r.k[2 * hf + u][k] = *reinterpret_cast<const uint4*>(kb[hf] + roff[hf][u] + 64 * k);
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vb + roff[u] + 64 * k);
+          for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int k = 0; k < PPL; ++k)
+                r.v[2 * hf + u][k] = *reinterpret_cast<const uint4*>(vb[hf] + roff[hf][u] + 64 * k);
         }
       } else {
-        int64_t off[2];
+        int64_t off[2 * NH];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          int t = t0 + grp + 8 * u;
+        for (int u = 0; u < 2 * NH; ++u) {
+          int t = t0 + (u >> 1) * kHalf + grp + 8 * (u & 1);
           t = t < c1 ? t : c0;
           const int64_t blk = s_bt[(t >> lgB) - j0];
           off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
         }
         if constexpr (F8) {
-          using P = typename KV<D, F8>::Piece;
+          using P = typename KVt::Piece;
 #pragma unroll
-          for (int u = 0; u < 2; ++u) r.k[u] = *reinterpret_cast<const P*>(kcache + off[u]);
+          for (int u = 0; u < 2 * NH; ++u) r.k[u] = *reinterpret_cast<const P*>(kcache + off[u]);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) r.v[u] = *reinterpret_cast<const P*>(vcache + off[u]);
+          for (int u = 0; u < 2 * NH; ++u) r.v[u] = *reinterpret_cast<const P*>(vcache + off[u]);
         } else {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2 * NH; ++u)
 #pragma unroll
             for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kcache + off[u] + 64 * k);
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
+          for (int u = 0; u < 2 * NH; ++u)
 #pragma unroll
             for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vcache + off[u] + 64 * k);
         }
       }
     };
 
-    auto compute = [&](int t0, const KV<D, F8>& r) __attribute__((always_inline)) {
+    // One half tile: tokens t0 + grp and t0 + grp + 8 of each group, held in
+    // r.k / r.v [2 hf] and [2 hf + 1].
+    auto compute = [&](int t0, const KVt& r, const int hf) __attribute__((always_inline)) {
       const bool valid0 = t0 + grp < c1;
       const bool valid1 = t0 + grp + 8 < c1;
       uint32_t kw[2][NW];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) bf16_words<D, F8>(r.k[u], kw[u]);
+      for (int u = 0; u < 2; ++u) bf16_words<D, F8>(r.k[2 * hf + u], kw[u]);
       // partial dots: slot v of set j is head 4 j + v / 2, token v % 2
       float x[NSET];
 #pragma unroll
@@ -348,8 +385,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
       }
       // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
       uint32_t v0[NW], v1[NW];
-      bf16_words<D, F8>(r.v[0], v0);
-      bf16_words<D, F8>(r.v[1], v1);
+      bf16_words<D, F8>(r.v[2 * hf], v0);
+      bf16_words<D, F8>(r.v[2 * hf + 1], v1);
 #pragma unroll
       for (int jw = 0; jw < NW; ++jw) {
         const int k = jw >> 2, i = jw & 3;
@@ -373,23 +410,28 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     // wave-uniform.  The first loads are issued whatever n_tiles is (they
     // stay inside the cache), so nothing delays them.
     constexpr int kStep = kWaves * kTile;
+    constexpr int NB = kBuffers;
     int t = c0 + wave * kTile;
     const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
-    KV<D, F8> r[kBuffers];
+    KVt r[NB];
 #pragma unroll
-    for (int k = 0; k + 1 < kBuffers; ++k) load(t + k * kStep, r[k], BIG && k < 2, k == 0 ? pre0 : pre1);
+    for (int k = 0; k + 1 < NB; ++k) load(t + k * kStep, r[k], BIG && k < 2, pre[k < 2 ? k : 0]);
     int i = 0;
-    for (; i + kBuffers <= n_tiles; i += kBuffers) {
+    for (; i + NB <= n_tiles; i += NB) {
 #pragma unroll
-      for (int k = 0; k < kBuffers; ++k) {
-        load(t + (kBuffers - 1) * kStep, r[(k + kBuffers - 1) % kBuffers]);
-        compute(t, r[k]);
+      for (int k = 0; k < NB; ++k) {
+        load(t + (NB - 1) * kStep, r[(k + NB - 1) % NB]);
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) compute(t + hf * kHalf, r[k], hf);
         t += kStep;
       }
     }
 #pragma unroll
-    for (int k = 0; k + 1 < kBuffers; ++k)
-      if (n_tiles - i > k) compute(t + k * kStep, r[k]);
+    for (int k = 0; k + 1 < NB; ++k)
+      if (n_tiles - i > k) {
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) compute(t + k * kStep + hf * kHalf, r[k], hf);
+      }
   };
   if constexpr (BIG) {
     // one range: no outer loop, whose header would drain the query loads

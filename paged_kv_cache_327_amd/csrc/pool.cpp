@@ -24,6 +24,9 @@
 //   tokens and the previous block's hash, so it captures position.
 // "Memory management", Code -- append with copy-on-write: the capacity test
 //   covers the copy block and the new blocks before anything changes.
+// Kernel blocks (the block-table append's hybrid branch and the decoupling
+//   paragraph of the first page): an allocation block of B tokens is the
+//   same memory as k = B / B_kernel kernel blocks, ids b*k .. b*k + k - 1.
 //
 // Readings: the hash is 64-bit FNV-1a over the parent hash (8 bytes LE, 0 for
 // the first block) and the block's token ids (4 bytes LE each); only full
@@ -454,6 +457,37 @@ int pa_pool_block_table(const pa_pool* p, const int64_t* seq_ids, int32_t n_seqs
   for (int32_t i = 0; i < n_seqs; ++i) {
     const pa_pool::Seq& s = p->seqs.find(seq_ids[i])->second;
     std::copy(s.blocks.begin(), s.blocks.end(), table_out + (int64_t)i * bt_stride);
+    if (seq_lens_out) seq_lens_out[i] = (int32_t)s.len;
+  }
+  return PA_OK;
+}
+
+int pa_pool_kernel_block_table(const pa_pool* p, const int64_t* seq_ids, int32_t n_seqs, int32_t kernel_block_size,
+                               int32_t* table_out, int32_t bt_stride, int32_t* seq_lens_out) {
+  pa::clear_error();
+  if (!p || n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !table_out)) || bt_stride < 0)
+    return pa::fail(PA_ERR_INVALID, "kernel_block_table: bad argument");
+  if (kernel_block_size <= 0 || p->block_size % kernel_block_size != 0)
+    return pa::fail(PA_ERR_INVALID, "kernel_block_table: kernel_block_size %d does not divide block_size %d",
+                    kernel_block_size, p->block_size);
+  const int64_t k = p->block_size / kernel_block_size;
+  if ((int64_t)p->num_blocks * k > INT32_MAX)
+    return pa::fail(PA_ERR_INVALID, "kernel_block_table: kernel block ids exceed int32");
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto it = p->seqs.find(seq_ids[i]);
+    if (it == p->seqs.end())
+      return pa::fail(PA_ERR_INVALID, "kernel_block_table: unknown sequence %lld", (long long)seq_ids[i]);
+    if ((int64_t)it->second.blocks.size() * k > bt_stride)
+      return pa::fail(PA_ERR_INVALID, "kernel_block_table: sequence %lld needs %lld entries > bt_stride %d",
+                      (long long)seq_ids[i], (long long)(it->second.blocks.size() * k), bt_stride);
+    if (it->second.len > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID, "kernel_block_table: sequence length exceeds int32");
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const pa_pool::Seq& s = p->seqs.find(seq_ids[i])->second;
+    int32_t* row = table_out + (int64_t)i * bt_stride;
+    for (size_t j = 0; j < s.blocks.size(); ++j)
+      for (int64_t u = 0; u < k; ++u) row[(int64_t)j * k + u] = (int32_t)(s.blocks[j] * k + u);
     if (seq_lens_out) seq_lens_out[i] = (int32_t)s.len;
   }
   return PA_OK;

@@ -317,3 +317,31 @@ def test_device_calls_validate_on_host():
     assert dec() == B.PA_ERR_INVALID and "workspace" in L.pa_last_error().decode()
     assert L.pa_paged_decode_workspace_size(4, 32, 128, 1000, 512) > 0
     assert L.pa_paged_decode_workspace_size(4, 32, 128, 500, 512) == 0
+
+
+@pytest.mark.parametrize("kernel_bs", [32, 16, 8, 1])
+def test_kernel_block_table_matches_oracle(kernel_bs):
+    """Native kernel-block rows equal the oracle's expansion of the model's
+    allocation rows; rows and lengths after a random run of appends."""
+    from oracle import cache_ops
+    nb, bs = 24, 32
+    order = np.random.default_rng(17).permutation(nb)
+    m, p = PoolModel(nb, bs, order), B.pa_pool_create(nb, bs, order)
+    lens = [1, 31, 32, 33, 100, 0]
+    for s, n in enumerate(lens):
+        m.add_seq(s)
+        B.pa_pool_add_seq(p, s)
+        if n:
+            m.append(s, n)
+            B.pa_pool_append(p, s, n)
+    k = bs // kernel_bs
+    width = 4 * k
+    table, got_lens = B.pa_pool_kernel_block_table(p, list(range(len(lens))), kernel_bs, width, fill=-1)
+    assert got_lens.tolist() == lens
+    for s in range(len(lens)):
+        want = cache_ops.map_to_kernel_blocks(m.block_table(s), k).tolist()
+        assert table[s, :len(want)].tolist() == want and (table[s, len(want):] == -1).all()
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_kernel_block_table(p, [0], 12, width)          # does not divide 32
+    with pytest.raises(B.InvalidArgument):
+        B.pa_pool_kernel_block_table(p, [4], kernel_bs, 4 * k - 1)   # 4 blocks need 4k entries
