@@ -181,3 +181,69 @@ def test_kernel_block_view_changes_no_result(k):
     s1 = cache_ops.slot_mapping(alloc, qsl, lens, B, int(qsl[-1]))
     s2 = cache_ops.slot_mapping(kern, qsl, lens, B // k, int(qsl[-1]))
     assert np.array_equal(s1, s2) and (s1 >= 0).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_append_keeps_the_table_mirror_equal_to_the_pool(seed):
+    """Decode steps over a batch with forked prefixes (copy-on-write of
+    shared tails) and block boundaries: after every step the mirror rows,
+    updated from the slots alone, equal the pool model's tables, and every
+    sequence reads back its token ids through the mirror."""
+    rng = np.random.default_rng([seed, 21])
+    B, S = 4, 6
+    pool = PoolModel(200, B, rng.permutation(200))
+    kc = np.full((200, B, 1, 64), -1, dtype=np.int64)
+    vc = kc.copy()
+    ids = {}
+    nxt = [0]
+
+    def toks(n):
+        t = np.arange(nxt[0], nxt[0] + n)
+        nxt[0] += n
+        return t
+    for s in range(S):
+        if s % 2 and s > 0:
+            pool.fork(s - 1, s)                    # shares s-1's blocks, tail included
+            ids[s] = list(ids[s - 1])
+            continue
+        pool.add_seq(s)
+        n = int(rng.integers(1, 11))
+        slots, _ = pool.append(s, n)
+        t = toks(n)
+        cache_ops.reshape_and_cache(kc, vc, np.repeat(t, 64).reshape(n, 1, 64), np.repeat(t, 64).reshape(n, 1, 64),
+                                    np.array(slots))
+        ids[s] = t.tolist()
+    W = 16
+    table = np.zeros((S, W), dtype=np.int64)
+    lens = np.zeros(S, dtype=np.int64)
+    for s in range(S):
+        row = pool.block_table(s)
+        table[s, :len(row)] = row
+        lens[s] = pool.seq_len(s)
+    copies = 0
+    for step in range(12):
+        slots = []
+        pairs = []
+        for s in range(S):
+            sl, pair = pool.append(s, 1)
+            slots.append(sl[0])
+            if pair is not None:
+                pairs.append(pair)
+        copies += len(pairs)
+        cache_ops.copy_blocks([kc, vc], pairs, 200)
+        pool.copies_done()
+        t = toks(S)
+        rows = np.repeat(t, 64).reshape(S, 1, 64)
+        cache_ops.decode_append(table, lens, kc, vc, rows, rows, slots)
+        for s in range(S):
+            ids[s].append(int(t[s]))
+            n = pool.seq_len(s)
+            assert lens[s] == n
+            assert table[s, :-(-n // B)].tolist() == pool.block_table(s)
+            got = [int(kc[table[s, p // B], p % B, 0, 0]) for p in range(n)]
+            assert got == ids[s], (seed, step, s)
+    assert copies > 0
+    # the padding id changes nothing
+    before = (table.copy(), lens.copy(), kc.copy())
+    cache_ops.decode_append(table, lens, kc, vc, rows, rows, [-1] * S)
+    assert np.array_equal(table, before[0]) and np.array_equal(lens, before[1]) and np.array_equal(kc, before[2])
