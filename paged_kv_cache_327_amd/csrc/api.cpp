@@ -140,6 +140,29 @@ int pa_reshape_and_cache_fp8(const void* key, int64_t key_row_stride, const void
                       block_size, true, k_scale, v_scale, stream);
 }
 
+int pa_decode_append(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
+                     void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                     int32_t* block_tables, int32_t bt_stride, int32_t* seq_lens, const int64_t* slots,
+                     int32_t num_rows, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void* stream) {
+  pa::clear_error();
+  const char* fn = "decode_append";
+  if (int rc = check_heads(fn, num_kv_heads, num_kv_heads, head_dim, block_size)) return rc;
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (num_rows < 0) return pa::fail(PA_ERR_INVALID, "%s: num_rows %d < 0", fn, num_rows);
+  if (num_rows == 0) return PA_OK;
+  if (!key || !value || !block_tables || !seq_lens || !slots) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
+    return pa::fail(PA_ERR_INVALID, "%s: key/value must be 16-byte aligned", fn);
+  if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 || value_row_stride % 8)
+    return pa::fail(PA_ERR_INVALID, "%s: row strides must be multiples of 8 and >= Hkv*D", fn);
+  if (bt_stride < 1) return pa::fail(PA_ERR_INVALID, "%s: bt_stride %d < 1", fn, bt_stride);
+  pa::AppendArgs a{key_cache, value_cache, cache_block_stride, (int64_t)num_blocks * block_size, block_tables,
+                   bt_stride, seq_lens, key, key_row_stride, value, value_row_stride, (int32_t)row,
+                   ilog2(block_size)};
+  return hip_status(fn, pa::launch_decode_append(a, slots, num_rows, stream));
+}
+
 int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
                    int32_t num_blocks, const int32_t* pairs, int32_t n_pairs, void* stream) {
   pa::clear_error();

@@ -32,6 +32,24 @@ struct ReshapeArgs {
 };
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream);
 
+struct AppendArgs {
+  void* key_cache;
+  void* value_cache;
+  int64_t cache_block_stride;
+  int64_t num_slots;  // num_blocks * block_size
+  int32_t* block_tables;
+  int32_t bt_stride;
+  int32_t* seq_lens;
+  const void* key;
+  int64_t key_row_stride;
+  const void* value;
+  int64_t value_row_stride;
+  int32_t row_elems;  // num_kv_heads * head_dim
+  int32_t log2_block_size;
+};
+// slots: host array of num_rows entries (they travel in the kernel arguments)
+int launch_decode_append(const AppendArgs& a, const int64_t* slots, int32_t num_rows, void* stream);
+
 struct SlotArgs {
   int64_t* slot_mapping;
   int32_t num_tokens;

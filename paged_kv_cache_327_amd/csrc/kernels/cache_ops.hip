@@ -65,6 +65,55 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
   }
 }
 
+// One decode token per row; the rows' slots travel in the kernel arguments,
+// so a decode step needs no host-to-device copy of metadata.  One wave per
+// row writes the token's K and V rows to its slot (as the cache write above)
+// and, from lane 0, records the slot's block as the table entry of the
+// token's position p = seq_lens[row] and stores seq_lens[row] = p + 1.  By
+// the slot formula ("PagedAttention: fragmentation, blocks, block tables",
+// 3. The slot mapping) that entry is slot / B, so the device tables follow
+// the host pool -- a new block, or the in-place redirect of a copied tail
+// (copy-on-write section) -- without being copied.  A slot of -1 changes
+// nothing; an entry past the row's width is not written.
+constexpr int kAppendMax = 256;   // rows per launch
+
+struct AppendBatch {
+  int64_t slots[kAppendMax];
+  int32_t row0;
+  int32_t n;
+};
+
+__global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a, AppendBatch b) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + wave;
+  if (r >= b.n) return;
+  const int64_t slot = b.slots[r];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t row = b.row0 + r;
+  const int64_t blk = slot >> a.log2_block_size;
+  const int64_t off = slot & ((int64_t{1} << a.log2_block_size) - 1);
+  const int64_t dst = blk * a.cache_block_stride + off * a.row_elems;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.key) + row * a.key_row_stride);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.value) + row * a.value_row_stride);
+  uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
+  uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
+  const int nvec = a.row_elems >> 3;
+  for (int c = lane; c < nvec; c += 64) {
+    const uint4 k = ks[c];
+    const uint4 v = vs[c];
+    kd[c] = k;
+    vd[c] = v;
+  }
+  if (lane == 0) {
+    const int32_t p = a.seq_lens[row];
+    const int64_t j = p >> a.log2_block_size;
+    if (p >= 0 && j < a.bt_stride) {
+      a.block_tables[row * a.bt_stride + j] = (int32_t)blk;
+      a.seq_lens[row] = p + 1;
+    }
+  }
+}
+
 // One thread per step token.  Its request is the last i with
 // query_start_loc[i] <= t (binary search over the num_seqs + 1 entries; the
 // loop is bounded by log2 of that count even if the entries are not sorted,
@@ -140,6 +189,19 @@ int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
   else
     hipLaunchKernelGGL(reshape_and_cache_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
+}
+
+int launch_decode_append(const AppendArgs& a, const int64_t* slots, int32_t num_rows, void* stream) {
+  for (int32_t r0 = 0; r0 < num_rows; r0 += kAppendMax) {
+    AppendBatch b{};
+    b.row0 = r0;
+    b.n = num_rows - r0 < kAppendMax ? num_rows - r0 : kAppendMax;
+    for (int32_t i = 0; i < b.n; ++i) b.slots[i] = slots[r0 + i];
+    hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)((b.n + 3) / 4)), dim3(256), 0, (hipStream_t)stream, a, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
 }
 
 int launch_slot_mapping(const SlotArgs& a, void* stream) {

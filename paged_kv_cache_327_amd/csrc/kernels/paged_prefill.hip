@@ -43,7 +43,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKeys = 64;        // keys per tile
-constexpr int kQ = 32;           // queries per wave
+constexpr int kQB = 1;           // 32-query blocks per wave (two: 10 % slower, see below)
+constexpr int kQ = 32 * kQB;     // queries per wave
 constexpr int kXcds = 8;         // accelerator dies of an MI355X, one L2 each
 constexpr int kSortMax = 256;    // requests ordered by work up to this many
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -162,19 +163,20 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   const int kv_end = CAUSAL ? ctx + q_last + 1 : kv_len;
   const int n_tiles = (kv_end + kKeys - 1) / kKeys;
 
-  // Q^T operand: lane holds query qw + col, d = 16 ks + 8 hf .. +8.
-  uint4 qreg[DS];
-  {
-    int qi = qw + col;
+  // Q^T operands: in query block qb the lane holds query qw + 32 qb + col,
+  // d = 16 ks + 8 hf .. +8.
+  uint4 qreg[kQB][DS];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    int qi = qw + 32 * qb + col;
     qi = qi < q_len ? qi : q_len - 1;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * ks + 8 * hf);
-      qreg[ks] = make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
+      qreg[qb][ks] = make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
     }
   }
-  const int qpos = ctx + qw + col;           // absolute position of this lane's query
 
   // Tile staging.  Keys at or past kv_end are loaded from a valid row
   // instead (the wave's first key of the tile, or key 0) and are removed from the
@@ -272,12 +274,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     }
   };
 
-  f32x16_t o[DB];
+  f32x16_t o[kQB][DB];
+  float m[kQB], l[kQB];
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+  for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
-  float m = kNegInf, l = 0.f;
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][b][r] = 0.f;
+    m[qb] = kNegInf;
+    l[qb] = 0.f;
+  }
 
   // Staging is unconditional: tiles past the end read valid rows, so no
   // branch separates a load from its use.
@@ -293,14 +300,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     const int buf = t & 1;
     const uint16_t* K = sm.k[buf];
     const uint16_t* V = sm.v[buf];
-    // S^T[key][query] for the two 32-key halves of the tile.  The two halves
-    // are independent accumulations: their MFMAs alternate, and the next
-    // k-step's K operands are read from LDS before this step's MFMAs issue.
-    f32x16_t s[2];
+    // S^T[key][query] for the two 32-key halves of the tile and each query
+    // block.  The accumulations are independent: their MFMAs alternate, every
+    // K operand read from LDS feeds all query blocks, and the next k-step's K
+    // operands are read before this step's MFMAs issue.
+    f32x16_t s[kQB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
     {
       const uint16_t* krow0 = &K[col * Smem<D>::kRow + 8 * hf];
       const uint16_t* krow1 = &K[(32 + col) * Smem<D>::kRow + 8 * hf];
@@ -313,8 +323,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
           kn0 = *reinterpret_cast<const uint4*>(krow0 + 16 * (ks + 1));
           kn1 = *reinterpret_cast<const uint4*>(krow1 + 16 * (ks + 1));
         }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka0), as_bf16x8(qreg[ks]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka1), as_bf16x8(qreg[ks]), s[1], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          s[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka0), as_bf16x8(qreg[qb][ks]), s[qb][0], 0, 0, 0);
+          s[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka1), as_bf16x8(qreg[qb][ks]), s[qb][1], 0, 0, 0);
+        }
         ka0 = kn0;
         ka1 = kn1;
       }
@@ -322,50 +335,54 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     // mask and tile max on raw scores.  Register r of half kb holds key
     // n0 + 32 kb + 8 (r / 4) + 4 hf + r % 4; a key is visible iff its offset
     // 32 kb + 8 (r / 4) + r % 4 is at most `lim` (one compare per score, on
-    // tiles that reach past this wave's first query only).
+    // tiles that reach past the query block's first query only).
     const int n0 = t * kKeys;
-    const int lim = (CAUSAL ? qpos : kv_len - 1) - n0 - 4 * hf;
-    const bool need_mask = n0 + kKeys - 1 > (CAUSAL ? ctx + qw : kv_len - 1);
-    float mt = kNegInf;
-    if (need_mask) {
+    uint32_t pb[kQB][2][2][4];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qpos = ctx + qw + 32 * qb + col;     // absolute position of the lane's query
+      const int lim = (CAUSAL ? qpos : kv_len - 1) - n0 - 4 * hf;
+      const bool need_mask = n0 + kKeys - 1 > (CAUSAL ? ctx + qw + 32 * qb : kv_len - 1);
+      float mt = kNegInf;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[qb][kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[qb][kb][r] : kNegInf;
+            mt = fmaxf(mt, s[qb][kb][r]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale;
+      if (mt > m[qb] + kSlack) {
+        const float alpha = fast_exp2(m[qb] - mt);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qb][b][r] *= alpha;
+        m[qb] = mt;
+      }
+      // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s;
+      // weights are exp2(score * scale - m), and their bf16 values are summed.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[kb][r] : kNegInf;
-          mt = fmaxf(mt, s[kb][r]);
-        }
-    } else {
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = fast_exp2(fmaf(s[qb][kb][8 * ks + 2 * w], scale, -m[qb]));
+            const float e1 = fast_exp2(fmaf(s[qb][kb][8 * ks + 2 * w + 1], scale, -m[qb]));
+            const uint32_t pk = pack_bf16x2(e0, e1);
+            pb[qb][kb][ks][w] = pk;
+            l[qb] = dot2_bf16(pk, 0x3F803F80u, l[qb]);
+          }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale;
-    if (mt > m + kSlack) {
-      const float alpha = fast_exp2(m - mt);
-      l *= alpha;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
-      m = mt;
-    }
-    // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s;
-    // weights are exp2(score * scale - m), and their bf16 values are summed.
-    uint32_t pb[2][2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(fmaf(s[kb][8 * ks + 2 * w], scale, -m));
-          const float e1 = fast_exp2(fmaf(s[kb][8 * ks + 2 * w + 1], scale, -m));
-          const uint32_t pk = pack_bf16x2(e0, e1);
-          pb[kb][ks][w] = pk;
-          l = dot2_bf16(pk, 0x3F803F80u, l);
-        }
     // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
     // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.  The V^T
     // operand (lane: d = 32 b + col) comes from row-major V with transposing
@@ -386,13 +403,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
       const int kb = step >> 1, ks = step & 1;
-      const uint4 pv = make_uint4(pb[kb][ks][0], pb[kb][ks][1], pb[kb][ks][2], pb[kb][ks][3]);
+      uint4 pv[kQB];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        pv[qb] = make_uint4(pb[qb][kb][ks][0], pb[qb][kb][ks][1], pb[qb][kb][ks][2], pb[qb][kb][ks][3]);
       uint4 vn[DB];
 #pragma unroll
       for (int b = 0; b < DB; ++b) vn[b] = step + 1 < 4 ? read_vt(step + 1, b) : va[b];
 #pragma unroll
       for (int b = 0; b < DB; ++b)
-        o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[b]), as_bf16x8(pv), o[b], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          o[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[b]), as_bf16x8(pv[qb]), o[qb][b], 0, 0, 0);
 #pragma unroll
       for (int b = 0; b < DB; ++b) va[b] = vn[b];
     }
@@ -403,20 +425,24 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // normalise and write: lane owns query qw + col, d = 32 b + 8 (r / 4) + 4 hf + r % 4
-  l += __shfl_xor(l, 32);
-  const int qi = qw + col;
-  if (qi < q_len) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
+  // normalise and write: in query block qb the lane owns query
+  // qw + 32 qb + col, d = 32 b + 8 (r / 4) + 4 hf + r % 4
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const int qi = qw + 32 * qb + col;
+    if (qi < q_len) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const uint32_t lo = pack_bf16x2(o[b][4 * rr] * inv, o[b][4 * rr + 1] * inv);
-        const uint32_t hi = pack_bf16x2(o[b][4 * rr + 2] * inv, o[b][4 * rr + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * b + 8 * rr + 4 * hf) = make_uint2(lo, hi);
-      }
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t lo = pack_bf16x2(o[qb][b][4 * rr] * inv, o[qb][b][4 * rr + 1] * inv);
+          const uint32_t hi = pack_bf16x2(o[qb][b][4 * rr + 2] * inv, o[qb][b][4 * rr + 3] * inv);
+          *reinterpret_cast<uint2*>(op + 32 * b + 8 * rr + 4 * hf) = make_uint2(lo, hi);
+        }
+    }
   }
 }
 

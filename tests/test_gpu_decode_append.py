@@ -1,0 +1,104 @@
+"""GPU: decode steps through pa_decode_append keep the device block tables and
+lengths equal to the host pool's (new blocks and copy-on-write redirects
+learned from the slots alone), write the same cache bytes as the oracle, and
+decode over the mirrored tables matches the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, cache_ops
+from paged_kv_cache_327_amd import binding as B
+from paged_kv_cache_327_amd import workloads
+from tests.hip_side import HipStep, to_device
+from tests.oracle_side import OracleStep
+from tests.parity import assert_attention_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+
+
+def forked_batch(block_size):
+    """10 sequences: three prompts of 30, 45 and 70 tokens, each forked into
+    more rows (their partial tails are shared until the first decode step),
+    plus one short row; no step tokens yet."""
+    ctx = [30, 30, 30, 45, 45, 70, 70, 70, 70, 5]
+    forks = [(0, 1), (0, 2), (3, 4), (5, 6), (5, 7), (5, 8)]
+    nb = 1000
+    return workloads.Workload(f"append_b{block_size}", 77, 8, 2, 128, block_size, nb, ctx_lens=ctx,
+                              new_lens=[0] * len(ctx), free_order=np.random.default_rng(77).permutation(nb),
+                              forks=forks)
+
+
+@pytest.mark.parametrize("block_size", [16, 4, 1])
+def test_decode_steps_keep_tables_and_caches_exact(block_size):
+    wl = forked_batch(block_size)
+    print(f"[decode append] B={block_size}", flush=True)
+    steps = 20
+    S = wl.num_seqs
+    width = -(-(max(wl.seq_lens) + steps) // block_size)
+    h, o = HipStep(wl, bt_width=width), OracleStep(wl, bt_width=width)
+    t_dev = h.table_dev.clone()
+    l_dev = h.seq_lens_dev.clone()
+    o_table = o.table.astype(np.int64).copy()
+    o_lens = o.seq_lens.astype(np.int64).copy()
+    seqs = list(range(S))
+    rng = np.random.default_rng([block_size, 5])
+    n_pairs = 0
+    for step in range(steps):
+        slots, pairs = B.pa_pool_append_batch(h.pool, seqs, [1] * S)
+        pairs = [tuple(p) for p in pairs.tolist() if p[0] >= 0]
+        o_slots, o_pairs = [], []
+        for s in seqs:
+            sl, pair = o.pool.append(s, 1)
+            o_slots += sl
+            if pair is not None:
+                o_pairs.append(pair)
+        assert slots.tolist() == o_slots and pairs == o_pairs
+        n_pairs += len(pairs)
+        B.pa_copy_blocks([h.kc, h.vc], pairs)
+        B.pa_pool_copies_done(h.pool)
+        cache_ops.copy_blocks([o.kc, o.vc], o_pairs, wl.num_blocks)
+        o.pool.copies_done()
+        k = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
+        v = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
+        B.pa_decode_append(to_device(k), to_device(v), h.kc, h.vc, t_dev, l_dev, slots)
+        cache_ops.decode_append(o_table, o_lens, o.kc, o.vc, k, v, o_slots)
+    assert n_pairs > 0 or block_size == 1        # one-token blocks are never partial
+    torch.cuda.synchronize()
+    host_table, host_lens = B.pa_pool_block_table(h.pool, seqs, width)
+    got_t, got_l = t_dev.cpu().numpy(), l_dev.cpu().numpy()
+    assert got_l.tolist() == host_lens.tolist() == o_lens.tolist()
+    for s in seqs:
+        n = -(-int(host_lens[s]) // block_size)
+        assert got_t[s, :n].tolist() == host_table[s, :n].tolist() == o_table[s, :n].tolist()
+    assert np.array_equal(h.kc.view(torch.int16).cpu().numpy().view(np.uint16), o.kc)
+    assert np.array_equal(h.vc.view(torch.int16).cpu().numpy().view(np.uint16), o.vc)
+
+    q = workloads.query_bits(wl.seed, S, wl.num_q_heads, wl.head_dim, layer=3)
+    out = torch.empty((S, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    msl = int(got_l.max())
+    B.pa_paged_decode(out, to_device(q), h.kc, h.vc, t_dev, l_dev, msl, wl.scale, partition_size=64)
+    want, _ = attention.paged_decode(q, o.kc, o.vc, o_table, o_lens, wl.scale)
+    assert_attention_close(out, want, what=f"decode after {steps} appended steps")
+
+
+def test_padding_rows_change_nothing_and_bad_calls_are_rejected():
+    wl = forked_batch(16)
+    h = HipStep(wl, bt_width=8)
+    t0, l0 = h.table_dev.clone(), h.seq_lens_dev.clone()
+    kc0 = h.kc.clone()
+    S = wl.num_seqs
+    k = torch.zeros((S, wl.num_kv_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.full(S, -1, dtype=np.int64))
+    torch.cuda.synchronize()
+    assert torch.equal(h.table_dev, t0) and torch.equal(h.seq_lens_dev, l0)
+    assert torch.equal(h.kc.view(torch.int16), kc0.view(torch.int16))
+    with pytest.raises(B.InvalidArgument):
+        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.zeros(S - 1, dtype=np.int64))
+    with pytest.raises(B.InvalidArgument):
+        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev.to(torch.int64), h.seq_lens_dev, np.zeros(S, dtype=np.int64))
