@@ -2,11 +2,13 @@
 
 One step is the whole path for one batch:
   1. the host pool appends one token to each of the 64 sequences (new block
-     ids, slots, copy-on-write pairs) and writes the block table;
-  2. table, lengths and slots go host -> device from pinned staging buffers;
-  3. pending copy-on-write block copies run (none arise in this workload);
-  4. the step's new K/V rows are written to their slots;
-  5. paged decode (partition pass, plus the log-sum-exp merge when a
+     ids, slots, copy-on-write pairs);
+  2. pending copy-on-write block copies run (none arise in this workload);
+  3. pa_decode_append writes the step's new K/V rows to their slots and
+     updates the device block tables and lengths from the slots, which
+     travel in the kernel arguments (the tables were copied to the device
+     once, at set-up; no metadata moves host -> device per step);
+  4. paged decode (partition pass, plus the log-sum-exp merge when a
      sequence spans several partitions) attends over the cache.
 
 Workload: Llama-3-8B-shaped decode (32 query / 8 KV heads, head_dim 128,
@@ -66,55 +68,47 @@ def decode_bytes(seq_lens, num_q_heads, num_kv_heads, head_dim, block_size, elem
 
 
 class Instance:
-    """One pool with its caches, a pinned staging buffer and the step's inputs.
+    """One pool with its caches and the step's inputs.
 
-    The per-step metadata (block table, lengths, slots) is packed into one
-    pinned int32 buffer so that a single host->device copy moves it.  The
-    pool writes straight into that buffer."""
+    The device block tables and lengths are copied to the GPU once, at
+    set-up.  Every step after that updates them on the device:
+    pa_decode_append writes the new tokens and learns new blocks (and
+    copy-on-write redirects) from their slots, which travel in the kernel
+    arguments, so a step moves no metadata from host to device."""
 
     def __init__(self, wl, torch, B, hip_side, workloads, max_seq_len, partition_size, workspace):
         self.wl = wl
-        self.state = hip_side.HipStep(wl)          # set-up: contexts + one step's token
         S = wl.num_seqs
         self.S = S
         self.width = -(-max_seq_len // wl.block_size)
-        n_i32 = S * self.width + S + 2 * S          # table | lens | slots (int64 as 2 x int32)
-        self.h_stage = torch.zeros(n_i32, dtype=torch.int32).pin_memory()
-        self.d_stage = torch.zeros(n_i32, dtype=torch.int32, device="cuda")
-        hs = self.h_stage.numpy()
-        self.h_table = hs[:S * self.width].reshape(S, self.width)
-        self.h_lens = hs[S * self.width:S * self.width + S]
-        self.h_slots = hs[S * self.width + S:].view(np.int64)
-        ds = self.d_stage
-        self.d_table = ds[:S * self.width].view(S, self.width)
-        self.d_lens = ds[S * self.width:S * self.width + S]
-        self.d_slots = ds[S * self.width + S:].view(torch.int64)
+        self.state = hip_side.HipStep(wl, bt_width=self.width)   # set-up: contexts + one step's token
+        self.d_table = self.state.table_dev
+        self.d_lens = self.state.seq_lens_dev
+        self.h_lens = self.state.seq_lens.astype(np.int64).copy()  # host copy of the lengths, for the byte count
         rng = np.random.default_rng([wl.seed, 99])
         self.new_k = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
         self.new_v = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
         self.q = hip_side.to_device(workloads.normal_bf16(rng, (S, wl.num_q_heads, wl.head_dim)))
         self.out = torch.empty_like(self.q)
-        self.staged = torch.cuda.Event()
-        self.staged.record()
         self.seq_ids = np.arange(S, dtype=np.int64)
         self.ones = np.ones(S, dtype=np.int32)
+        self.h_slots = np.empty(S, dtype=np.int64)
         self.pairs = np.empty((S, 2), dtype=np.int32)
         self.done = B.c_i32(0)
         kc, vc = self.state.kc, self.state.vc
         L = B.lib()
         self.lib = L
         # argument tuples of the C calls (validated once by the binding's
-        # checks in HipStep; the device pointers do not change)
+        # checks in HipStep; the pointers do not change)
         self.append_args = (self.state.pool.handle, self.seq_ids.ctypes.data_as(B.P_i64),
                             self.ones.ctypes.data_as(B.P_i32), S,
                             self.h_slots.ctypes.data_as(B.P_i64), self.pairs.ctypes.data_as(B.P_i32),
                             B.ctypes.byref(self.done))
-        self.table_args = (self.state.pool.handle, self.seq_ids.ctypes.data_as(B.P_i64), S,
-                           self.h_table.ctypes.data_as(B.P_i32), self.width, self.h_lens.ctypes.data_as(B.P_i32))
         bstride = kc.stride(0)
-        self.reshape_args = (self.new_k.data_ptr(), self.new_k.stride(0), self.new_v.data_ptr(),
-                             self.new_v.stride(0), kc.data_ptr(), vc.data_ptr(), bstride, wl.num_blocks,
-                             self.d_slots.data_ptr(), S, wl.num_kv_heads, wl.head_dim, wl.block_size)
+        self.write_args = (self.new_k.data_ptr(), self.new_k.stride(0), self.new_v.data_ptr(),
+                           self.new_v.stride(0), kc.data_ptr(), vc.data_ptr(), bstride, wl.num_blocks,
+                           self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(),
+                           self.h_slots.ctypes.data_as(B.P_i64), S, wl.num_kv_heads, wl.head_dim, wl.block_size)
         self.decode_args = (self.out.data_ptr(), None, self.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bstride,
                             wl.num_blocks, self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(), S,
                             wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, max_seq_len,
@@ -127,25 +121,22 @@ class Instance:
 
 
 def run_step(inst, B, stream):
-    """One decode step on one instance; returns the attended lengths."""
+    """One decode step on one instance (host pool append, copy-on-write
+    copies if any, the token write with its table update, decode); returns
+    the attended lengths."""
     L = inst.lib
-    inst.staged.synchronize()                     # the previous copy out of the staging buffer is done
     rc = L.pa_pool_append_batch(*inst.append_args)
     if rc != 0:
         raise RuntimeError(L.pa_last_error().decode())
-    rc = L.pa_pool_block_table(*inst.table_args)
-    if rc != 0:
-        raise RuntimeError(L.pa_last_error().decode())
-    inst.d_stage.copy_(inst.h_stage, non_blocking=True)
-    inst.staged.record()
     cow = inst.pairs[inst.pairs[:, 0] >= 0]
     if len(cow):
         B.pa_copy_blocks([inst.state.kc, inst.state.vc], cow)
         B.pa_pool_copies_done(inst.state.pool)
-    rc = L.pa_reshape_and_cache(*inst.reshape_args, stream)
+    rc = L.pa_decode_append(*inst.write_args, stream)
     if rc != 0:
         raise RuntimeError(L.pa_last_error().decode())
     inst.decode(stream)
+    inst.h_lens += 1
     return inst.h_lens.copy()
 
 
@@ -222,6 +213,32 @@ def measure_prefill(torch, B, hip_side, workloads, block_size=16, reps=10):
             "us": round(sec * 1e6, 1), "gflop": round(flops / 1e9, 2),
             "tflops": round(flops / sec / 1e12, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def measure_copy_bandwidth(torch, nbytes=1 << 30, reps=20):
+    """A plain device-to-device copy of nbytes (read + write counted): the
+    box's practical HBM ceiling, a second denominator beside the 8 TB/s
+    published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sec = time_launches(torch, lambda: dst.copy_(src), reps)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * nbytes, "us": round(sec * 1e6, 1), "gbps": round(2 * nbytes / sec / 1e9, 1),
+            "hbm_frac": round(2 * nbytes / sec / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def measure_tiny(torch, B, hip_side, workloads, reps=200):
+    """The tiny decode (4 sequences of 1, 17, 33, 100 tokens; 8/2 heads, d 64):
+    latency only, no roofline claim."""
+    wl = workloads.tiny_decode()
+    h = hip_side.HipStep(wl)
+    q = hip_side.to_device(workloads.query_bits(wl.seed, wl.num_seqs, wl.num_q_heads, wl.head_dim))
+    out = torch.empty_like(q)
+    msl = max(wl.seq_lens)
+    sec = time_launches(torch, lambda: B.pa_paged_decode(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl,
+                                                         wl.scale, partition_size=0), reps)
+    return {"workload": "4 sequences of 1, 17, 33, 100 tokens, 8/2 heads, d 64, B 16", "decode_us": round(sec * 1e6, 2)}
 
 
 def warm_clocks(torch, fn, seconds=0.3):
@@ -688,6 +705,15 @@ def main():
     alg_per_launch = np.mean([decode_bytes(cur_lens[k], wl.num_q_heads, wl.num_kv_heads,
                                            wl.head_dim, wl.block_size) for k in range(len(insts))])
     achieved = alg_per_launch / dec_s / 1e9
+    # the step's cache write alone (no table update): 64 new tokens' K and V
+    # rows to their slots
+    w_inst = insts[0]
+    w_slots = torch.from_numpy(w_inst.h_slots.copy()).cuda()
+    kc0 = w_inst.state.kc
+    w_args = (w_inst.new_k.data_ptr(), w_inst.new_k.stride(0), w_inst.new_v.data_ptr(), w_inst.new_v.stride(0),
+              kc0.data_ptr(), w_inst.state.vc.data_ptr(), kc0.stride(0), wl.num_blocks, w_slots.data_ptr(), S,
+              wl.num_kv_heads, wl.head_dim, wl.block_size, stream)
+    res_s = time_launches(torch, lambda: w_inst.lib.pa_reshape_and_cache(*w_args), 200)
 
     ms_per_step = elapsed / args.steps * 1e3
     kv_per_step = np.mean([kv_bytes(l, wl.num_kv_heads, wl.head_dim) for l in step_lens])
@@ -715,6 +741,7 @@ def main():
         "step_hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "decode_kernel_us": round(dec_s * 1e6, 2),
         "decode_seqs_per_s": round(S / dec_s, 1),
+        "reshape_64_tokens_us": round(res_s * 1e6, 2),
         "roofline": {
             "bound": "hbm",
             "kernel": DECODE_KERNEL + (" + decode_merge_kernel<128>" if nparts > 1 else ""),
@@ -734,6 +761,9 @@ def main():
         line["prefill"] = measure_prefill(torch, B, hip_side, workloads)
     if not args.no_configs:
         cfg = {}
+        print("[bench] tiny decode, copy bandwidth", file=sys.stderr, flush=True)
+        cfg["tiny_decode"] = measure_tiny(torch, B, hip_side, workloads)
+        cfg["d2d_copy"] = measure_copy_bandwidth(torch)
         print("[bench] long-context 32-layer pool", file=sys.stderr, flush=True)
         cfg["long_context_decode"] = measure_long_context(torch, B, hip_side, workloads)
         print("[bench] prefix sharing + copy-on-write", file=sys.stderr, flush=True)
