@@ -600,12 +600,26 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), insta
 def counter_run(kind, reps):
     """Launch only one kernel kind, for rocprofv3 --pmc passes:
     'decode' = the decode call of this workload on rotating pools,
-    'copy' = a plain device copy of COPY_CALIBRATION_BYTES (calibration)."""
+    'copy' = a plain device copy of COPY_CALIBRATION_BYTES (calibration),
+    'prefill' = the mixed step's prefill chunks (MFMA counters)."""
     import torch
 
     from paged_kv_cache_327_amd import binding as B
     from paged_kv_cache_327_amd import workloads
     from tests import hip_side
+    if kind == "prefill":
+        wl = workloads.mixed_step(16, n_decode=0)
+        h = hip_side.HipStep(wl)
+        q = hip_side.to_device(workloads.query_bits(wl.seed, sum(wl.q_lens), wl.num_q_heads, wl.head_dim))
+        out = torch.empty_like(q)
+        qsl = torch.tensor(np.concatenate([[0], np.cumsum(wl.q_lens)]), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            B.pa_paged_prefill(out, q, h.kc, h.vc, h.table_dev, qsl, h.seq_lens_dev, max(wl.q_lens),
+                               int(max(wl.seq_lens)), wl.scale)
+        torch.cuda.synchronize()
+        print(f"prefill x {reps}; {prefill_flops(wl.q_lens, wl.seq_lens, 32, 128):.0f} flop per launch", flush=True)
+        return
     if kind == "copy":
         x = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
         y = torch.empty_like(x)
@@ -643,7 +657,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the long-context, prefix-sharing and mixed-step measurements")
-    ap.add_argument("--counter-run", choices=["decode", "copy"],
+    ap.add_argument("--counter-run", choices=["decode", "copy", "prefill"],
                     help="only launch one kernel kind (for rocprofv3 --pmc passes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
