@@ -93,6 +93,7 @@ class Instance:
         self.seq_ids = np.arange(S, dtype=np.int64)
         self.ones = np.ones(S, dtype=np.int32)
         self.h_slots = np.empty(S, dtype=np.int64)
+        self.h_pos = np.empty(S, dtype=np.int32)         # each row's length before the step
         self.pairs = np.empty((S, 2), dtype=np.int32)
         self.done = B.c_i32(0)
         kc, vc = self.state.kc, self.state.vc
@@ -108,7 +109,8 @@ class Instance:
         self.write_args = (self.new_k.data_ptr(), self.new_k.stride(0), self.new_v.data_ptr(),
                            self.new_v.stride(0), kc.data_ptr(), vc.data_ptr(), bstride, wl.num_blocks,
                            self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(),
-                           self.h_slots.ctypes.data_as(B.P_i64), S, wl.num_kv_heads, wl.head_dim, wl.block_size)
+                           self.h_slots.ctypes.data_as(B.P_i64), self.h_pos.ctypes.data_as(B.P_i32), S,
+                           wl.num_kv_heads, wl.head_dim, wl.block_size)
         self.decode_args = (self.out.data_ptr(), None, self.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bstride,
                             wl.num_blocks, self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(), S,
                             wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, max_seq_len,
@@ -132,6 +134,7 @@ def run_step(inst, B, stream):
     if len(cow):
         B.pa_copy_blocks([inst.state.kc, inst.state.vc], cow)
         B.pa_pool_copies_done(inst.state.pool)
+    inst.h_pos[:] = inst.h_lens
     rc = L.pa_decode_append(*inst.write_args, stream)
     if rc != 0:
         raise RuntimeError(L.pa_last_error().decode())

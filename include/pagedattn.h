@@ -321,28 +321,32 @@ int pa_reshape_and_cache_fp8(const void* key, int64_t key_row_stride,
 
 /* A decode step's cache write that also keeps device block tables current:
  * row i (i < num_rows) has one new token whose K and V rows are row i of
- * key/value (as in pa_reshape_and_cache) and whose slot is slots[i], the slot
- * pa_pool_append returned for it.  With p = seq_lens[i] on entry, the call
- * writes the token to its slot, sets block_tables[i][p / B] = slots[i] / B
- * and seq_lens[i] = p + 1.  By the slot formula that entry is the block the
- * pool put position p in, so the device table follows the host pool -- a
- * newly allocated block, or the in-place redirect of a copied tail -- with
- * no host-to-device copy: the slots travel in the kernel arguments.  A slot
- * of -1 leaves row i unchanged; an entry p / B >= bt_stride is not written
- * (size the table for the longest sequence).  Run pa_copy_blocks for the
- * step's pairs first, as for pa_reshape_and_cache.
+ * key/value (as in pa_reshape_and_cache), whose slot is slots[i] (the slot
+ * pa_pool_append returned for it) and whose position is positions[i] = p
+ * (the row's length before the step).  The call writes the token to its
+ * slot, sets block_tables[i][p / B] = slots[i] / B and seq_lens[i] = p + 1.
+ * By the slot formula that entry is the block the pool put position p in,
+ * so the device table follows the host pool -- a newly allocated block, or
+ * the in-place redirect of a copied tail -- with no host-to-device copy:
+ * slots and positions travel in the kernel arguments.  A slot of -1 leaves
+ * row i unchanged; an entry p / B >= bt_stride is not written (size the
+ * table for the longest sequence).  Run pa_copy_blocks for the step's pairs
+ * first, as for pa_reshape_and_cache.
  * ("PagedAttention: fragmentation, blocks, block tables", 2. The block table
  * (append-only rows), 3. The slot mapping, and the copy-on-write section.)
  * key/value: device bf16 [num_rows][num_kv_heads][head_dim] rows.
  * block_tables: device int32 [num_rows][bt_stride]; seq_lens: device int32
- * [num_rows] (both updated); slots: HOST int64 [num_rows].
- * Errors as pa_reshape_and_cache (nothing is launched on an error). */
+ * [num_rows] (both written); slots: HOST int64 [num_rows]; positions: HOST
+ * int32 [num_rows].
+ * Errors as pa_reshape_and_cache, plus PA_ERR_INVALID for a negative position
+ * of a row with a slot (nothing is launched on an error). */
 int pa_decode_append(const void* key, int64_t key_row_stride,
                      const void* value, int64_t value_row_stride,
                      void* key_cache, void* value_cache, int64_t cache_block_stride,
                      int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
-                     int32_t* seq_lens, const int64_t* slots, int32_t num_rows,
-                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void* stream);
+                     int32_t* seq_lens, const int64_t* slots, const int32_t* positions,
+                     int32_t num_rows, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     void* stream);
 
 /* Copy whole blocks: for every cache c and pair (src, dst),
  * bytes [0, block_bytes) of block dst <- the same bytes of block src, where

@@ -46,17 +46,18 @@ def slot_mapping(block_tables: np.ndarray, query_start_loc, seq_lens, block_size
 
 
 def decode_append(block_tables: np.ndarray, seq_lens: np.ndarray, key_cache: np.ndarray,
-                  value_cache: np.ndarray, key: np.ndarray, value: np.ndarray, slots) -> None:
+                  value_cache: np.ndarray, key: np.ndarray, value: np.ndarray, slots, positions) -> None:
     """One decode token per row, written and entered into a device mirror of
     the block tables (arrays are updated in place).
 
-    Row i's new token sits at position p = seq_lens[i] (before the call) and
-    at slot slots[i], which the pool returned for it.  By the slot formula
+    Row i's new token sits at position p = positions[i] (the row's length
+    before the step, which the host pool knows) and at slot slots[i], which
+    the pool returned for it.  By the slot formula
     (the pool page, 3. The slot mapping) its block is slots[i] // B and that
     block is entry p // B of the row, so the mirror learns a newly allocated
     block, and the in-place redirect of a copied tail (copy-on-write
     section), from the slot alone: table[i][p // B] = slots[i] // B.  The K/V
-    rows are written as reshape_and_cache does, and seq_lens[i] grows by one.
+    rows are written as reshape_and_cache does, and seq_lens[i] becomes p + 1.
 
     Reading: a negative slot (the padding id) leaves row i unchanged; the row
     has room for entry p // B (the caller sizes the table).
@@ -65,7 +66,7 @@ def decode_append(block_tables: np.ndarray, seq_lens: np.ndarray, key_cache: np.
     for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
         if slot < 0:
             continue
-        p = int(seq_lens[i])
+        p = int(positions[i])
         block_tables[i, p // B] = int(slot) // B
         seq_lens[i] = p + 1
     reshape_and_cache(key_cache, value_cache, key, value, np.asarray(slots, dtype=np.int64))

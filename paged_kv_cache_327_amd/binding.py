@@ -73,7 +73,7 @@ _SIGS = {
     "pa_reshape_and_cache_fp8": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp,
                                          c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_vp]),
     "pa_decode_append": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, P_i64,
-                                 c_i32, c_i32, c_i32, c_i32, c_vp]),
+                                 P_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_i32, P_i32, c_i32, c_vp]),
     "pa_paged_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_paged_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
@@ -392,10 +392,11 @@ def _reshape(key, value, key_cache, value_cache, slot_mapping, stream, fp8, k_sc
         _check(lib().pa_reshape_and_cache(*args, _stream(key_cache, stream)))
 
 
-def pa_decode_append(key, value, key_cache, value_cache, block_tables, seq_lens, slots, stream=None):
+def pa_decode_append(key, value, key_cache, value_cache, block_tables, seq_lens, slots, positions, stream=None):
     """key/value [S, Hkv, D] bf16 device rows (one new token per row);
     block_tables int32 [S, W] and seq_lens int32 [S] device tensors, updated
-    in place; slots: host int64 [S] (the pool's slots for the new tokens)."""
+    in place; slots: host int64 [S] (the pool's slots for the new tokens);
+    positions: host int32 [S] (each row's length before the step)."""
     import torch
     nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
     _bf16(key, "key")
@@ -410,11 +411,12 @@ def pa_decode_append(key, value, key_cache, value_cache, block_tables, seq_lens,
     if seq_lens.dtype != torch.int32 or seq_lens.shape[0] < S or not seq_lens.is_contiguous() or not seq_lens.is_cuda:
         raise InvalidArgument(PA_ERR_INVALID, "seq_lens must be a contiguous device int32 [>= S] tensor")
     sl = np.ascontiguousarray(slots, dtype=np.int64)
-    if sl.shape != (S,):
-        raise InvalidArgument(PA_ERR_INVALID, "slots must have one entry per row")
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    if sl.shape != (S,) or pos.shape != (S,):
+        raise InvalidArgument(PA_ERR_INVALID, "slots and positions must have one entry per row")
     _check(lib().pa_decode_append(key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0),
                                   key_cache.data_ptr(), value_cache.data_ptr(), bstride, nb, block_tables.data_ptr(),
-                                  block_tables.stride(0), seq_lens.data_ptr(), _i64p(sl), S, hkv, d, bs,
+                                  block_tables.stride(0), seq_lens.data_ptr(), _i64p(sl), _i32p(pos), S, hkv, d, bs,
                                   _stream(key_cache, stream)))
 
 

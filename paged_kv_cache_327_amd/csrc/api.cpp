@@ -143,7 +143,8 @@ int pa_reshape_and_cache_fp8(const void* key, int64_t key_row_stride, const void
 int pa_decode_append(const void* key, int64_t key_row_stride, const void* value, int64_t value_row_stride,
                      void* key_cache, void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
                      int32_t* block_tables, int32_t bt_stride, int32_t* seq_lens, const int64_t* slots,
-                     int32_t num_rows, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void* stream) {
+                     const int32_t* positions, int32_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, void* stream) {
   pa::clear_error();
   const char* fn = "decode_append";
   if (int rc = check_heads(fn, num_kv_heads, num_kv_heads, head_dim, block_size)) return rc;
@@ -151,7 +152,11 @@ int pa_decode_append(const void* key, int64_t key_row_stride, const void* value,
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
   if (num_rows < 0) return pa::fail(PA_ERR_INVALID, "%s: num_rows %d < 0", fn, num_rows);
   if (num_rows == 0) return PA_OK;
-  if (!key || !value || !block_tables || !seq_lens || !slots) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!key || !value || !block_tables || !seq_lens || !slots || !positions)
+    return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  for (int32_t i = 0; i < num_rows; ++i)
+    if (slots[i] >= 0 && (positions[i] < 0 || positions[i] == INT32_MAX))
+      return pa::fail(PA_ERR_INVALID, "%s: row %d has position %d", fn, i, positions[i]);
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4))
     return pa::fail(PA_ERR_INVALID, "%s: key/value must be 16-byte aligned", fn);
   if (key_row_stride < row || value_row_stride < row || key_row_stride % 8 || value_row_stride % 8)
@@ -160,7 +165,7 @@ int pa_decode_append(const void* key, int64_t key_row_stride, const void* value,
   pa::AppendArgs a{key_cache, value_cache, cache_block_stride, (int64_t)num_blocks * block_size, block_tables,
                    bt_stride, seq_lens, key, key_row_stride, value, value_row_stride, (int32_t)row,
                    ilog2(block_size)};
-  return hip_status(fn, pa::launch_decode_append(a, slots, num_rows, stream));
+  return hip_status(fn, pa::launch_decode_append(a, slots, positions, num_rows, stream));
 }
 
 int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,

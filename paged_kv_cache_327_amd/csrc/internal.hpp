@@ -47,8 +47,10 @@ struct AppendArgs {
   int32_t row_elems;  // num_kv_heads * head_dim
   int32_t log2_block_size;
 };
-// slots: host array of num_rows entries (they travel in the kernel arguments)
-int launch_decode_append(const AppendArgs& a, const int64_t* slots, int32_t num_rows, void* stream);
+// slots, positions: host arrays of num_rows entries (they travel in the
+// kernel arguments)
+int launch_decode_append(const AppendArgs& a, const int64_t* slots, const int32_t* positions, int32_t num_rows,
+                         void* stream);
 
 struct SlotArgs {
   int64_t* slot_mapping;

@@ -31,9 +31,32 @@ __device__ __forceinline__ uint2 quantize8(const uint4 x, float r) {
   return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
 }
 
+// A token's K and V rows, nvec 16-byte pieces each, moved by one wave: two
+// pieces of each per lane are loaded before any is stored, so the loads of a
+// row overlap.
+__device__ __forceinline__ void copy_row(const uint4* ks, const uint4* vs, uint4* kd, uint4* vd, int nvec,
+                                         int lane) {
+  for (int c = lane; c < nvec; c += 128) {
+    const bool two = c + 64 < nvec;
+    const uint4 k0 = ks[c], v0 = vs[c];
+    uint4 k1 = k0, v1 = v0;
+    if (two) {
+      k1 = ks[c + 64];
+      v1 = vs[c + 64];
+    }
+    kd[c] = k0;
+    vd[c] = v0;
+    if (two) {
+      kd[c + 64] = k1;
+      vd[c + 64] = v1;
+    }
+  }
+}
+
 template <bool F8>
 __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform (SGPR), so that the per-token loads below are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= a.num_tokens) return;
   const int64_t slot = a.slot_mapping[t];
@@ -56,20 +79,16 @@ __global__ void __launch_bounds__(256) reshape_and_cache_kernel(ReshapeArgs a) {
   } else {
     uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
     uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
-    for (int c = lane; c < nvec; c += 64) {
-      const uint4 k = ks[c];
-      const uint4 v = vs[c];
-      kd[c] = k;
-      vd[c] = v;
-    }
+    copy_row(ks, vs, kd, vd, nvec, lane);
   }
 }
 
-// One decode token per row; the rows' slots travel in the kernel arguments,
-// so a decode step needs no host-to-device copy of metadata.  One wave per
-// row writes the token's K and V rows to its slot (as the cache write above)
-// and, from lane 0, records the slot's block as the table entry of the
-// token's position p = seq_lens[row] and stores seq_lens[row] = p + 1.  By
+// One decode token per row; the rows' slots and positions travel in the
+// kernel arguments, so a decode step needs no host-to-device copy of
+// metadata and reads nothing but the new rows.  One wave per row writes the
+// token's K and V rows to its slot (as the cache write above) and, from lane
+// 0, records the slot's block as the table entry of the token's position p
+// and stores seq_lens[row] = p + 1.  By
 // the slot formula ("PagedAttention: fragmentation, blocks, block tables",
 // 3. The slot mapping) that entry is slot / B, so the device tables follow
 // the host pool -- a new block, or the in-place redirect of a copied tail
@@ -79,17 +98,20 @@ constexpr int kAppendMax = 256;   // rows per launch
 
 struct AppendBatch {
   int64_t slots[kAppendMax];
+  int32_t pos[kAppendMax];
   int32_t row0;
   int32_t n;
 };
 
 __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a, AppendBatch b) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform (SGPR), so that the per-token loads below are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + wave;
   if (r >= b.n) return;
   const int64_t slot = b.slots[r];
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t row = b.row0 + r;
+  const int32_t p = b.pos[r];
   const int64_t blk = slot >> a.log2_block_size;
   const int64_t off = slot & ((int64_t{1} << a.log2_block_size) - 1);
   const int64_t dst = blk * a.cache_block_stride + off * a.row_elems;
@@ -97,15 +119,8 @@ __global__ void __launch_bounds__(256) decode_append_kernel(AppendArgs a, Append
   const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.value) + row * a.value_row_stride);
   uint4* kd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.key_cache) + dst);
   uint4* vd = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.value_cache) + dst);
-  const int nvec = a.row_elems >> 3;
-  for (int c = lane; c < nvec; c += 64) {
-    const uint4 k = ks[c];
-    const uint4 v = vs[c];
-    kd[c] = k;
-    vd[c] = v;
-  }
+  copy_row(ks, vs, kd, vd, a.row_elems >> 3, lane);
   if (lane == 0) {
-    const int32_t p = a.seq_lens[row];
     const int64_t j = p >> a.log2_block_size;
     if (p >= 0 && j < a.bt_stride) {
       a.block_tables[row * a.bt_stride + j] = (int32_t)blk;
@@ -191,12 +206,16 @@ int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_decode_append(const AppendArgs& a, const int64_t* slots, int32_t num_rows, void* stream) {
+int launch_decode_append(const AppendArgs& a, const int64_t* slots, const int32_t* positions, int32_t num_rows,
+                         void* stream) {
   for (int32_t r0 = 0; r0 < num_rows; r0 += kAppendMax) {
     AppendBatch b{};
     b.row0 = r0;
     b.n = num_rows - r0 < kAppendMax ? num_rows - r0 : kAppendMax;
-    for (int32_t i = 0; i < b.n; ++i) b.slots[i] = slots[r0 + i];
+    for (int32_t i = 0; i < b.n; ++i) {
+      b.slots[i] = slots[r0 + i];
+      b.pos[i] = positions[r0 + i];
+    }
     hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)((b.n + 3) / 4)), dim3(256), 0, (hipStream_t)stream, a, b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;

@@ -66,8 +66,9 @@ def test_decode_steps_keep_tables_and_caches_exact(block_size):
         o.pool.copies_done()
         k = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
         v = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
-        B.pa_decode_append(to_device(k), to_device(v), h.kc, h.vc, t_dev, l_dev, slots)
-        cache_ops.decode_append(o_table, o_lens, o.kc, o.vc, k, v, o_slots)
+        pos = o_lens.copy()                      # the rows' lengths before the step
+        B.pa_decode_append(to_device(k), to_device(v), h.kc, h.vc, t_dev, l_dev, slots, pos)
+        cache_ops.decode_append(o_table, o_lens, o.kc, o.vc, k, v, o_slots, pos)
     assert n_pairs > 0 or block_size == 1        # one-token blocks are never partial
     torch.cuda.synchronize()
     host_table, host_lens = B.pa_pool_block_table(h.pool, seqs, width)
@@ -94,11 +95,16 @@ def test_padding_rows_change_nothing_and_bad_calls_are_rejected():
     kc0 = h.kc.clone()
     S = wl.num_seqs
     k = torch.zeros((S, wl.num_kv_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
-    B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.full(S, -1, dtype=np.int64))
+    pos = h.seq_lens.astype(np.int32)
+    B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.full(S, -1, dtype=np.int64), pos)
     torch.cuda.synchronize()
     assert torch.equal(h.table_dev, t0) and torch.equal(h.seq_lens_dev, l0)
     assert torch.equal(h.kc.view(torch.int16), kc0.view(torch.int16))
     with pytest.raises(B.InvalidArgument):
-        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.zeros(S - 1, dtype=np.int64))
+        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.zeros(S - 1, dtype=np.int64), pos)
     with pytest.raises(B.InvalidArgument):
-        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev.to(torch.int64), h.seq_lens_dev, np.zeros(S, dtype=np.int64))
+        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev.to(torch.int64), h.seq_lens_dev,
+                           np.zeros(S, dtype=np.int64), pos)
+    with pytest.raises(B.InvalidArgument):
+        B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.zeros(S, dtype=np.int64),
+                           np.full(S, -1, dtype=np.int32))       # a row with a slot needs a position

@@ -234,7 +234,7 @@ def test_decode_append_keeps_the_table_mirror_equal_to_the_pool(seed):
         pool.copies_done()
         t = toks(S)
         rows = np.repeat(t, 64).reshape(S, 1, 64)
-        cache_ops.decode_append(table, lens, kc, vc, rows, rows, slots)
+        cache_ops.decode_append(table, lens, kc, vc, rows, rows, slots, lens.copy())
         for s in range(S):
             ids[s].append(int(t[s]))
             n = pool.seq_len(s)
@@ -245,5 +245,5 @@ def test_decode_append_keeps_the_table_mirror_equal_to_the_pool(seed):
     assert copies > 0
     # the padding id changes nothing
     before = (table.copy(), lens.copy(), kc.copy())
-    cache_ops.decode_append(table, lens, kc, vc, rows, rows, [-1] * S)
+    cache_ops.decode_append(table, lens, kc, vc, rows, rows, [-1] * S, lens.copy())
     assert np.array_equal(table, before[0]) and np.array_equal(lens, before[1]) and np.array_equal(kc, before[2])
