@@ -4,12 +4,12 @@ One step is the whole path for one batch:
   1. the host pool appends one token to each of the 64 sequences (new block
      ids, slots, copy-on-write pairs);
   2. pending copy-on-write block copies run (none arise in this workload);
-  3. pa_decode_append writes the step's new K/V rows to their slots and
-     updates the device block tables and lengths from the slots, which
-     travel in the kernel arguments (the tables were copied to the device
-     once, at set-up; no metadata moves host -> device per step);
-  4. paged decode (partition pass, plus the log-sum-exp merge when a
-     sequence spans several partitions) attends over the cache.
+  3. one pa_paged_decode_append launch writes the step's new K/V rows to
+     their slots, updates the device block tables and lengths from the
+     slots, which travel in the kernel arguments (the tables were copied to
+     the device once, at set-up; no metadata moves host -> device per step),
+     and runs paged decode (partition pass, plus the log-sum-exp merge when a
+     sequence spans several partitions) over the cache.
 
 Workload: Llama-3-8B-shaped decode (32 query / 8 KV heads, head_dim 128,
 bf16, block_size 16), batch 64, each sequence 512 prompt + U{0..100}
@@ -72,9 +72,11 @@ class Instance:
 
     The device block tables and lengths are copied to the GPU once, at
     set-up.  Every step after that updates them on the device:
-    pa_decode_append writes the new tokens and learns new blocks (and
+    pa_paged_decode_append writes the new tokens, learns new blocks (and
     copy-on-write redirects) from their slots, which travel in the kernel
-    arguments, so a step moves no metadata from host to device."""
+    arguments with the positions, and decodes, so a step moves no metadata
+    from host to device and launches one kernel (plus the merge when a
+    sequence spans several partitions)."""
 
     def __init__(self, wl, torch, B, hip_side, workloads, max_seq_len, partition_size, workspace):
         self.wl = wl
@@ -106,15 +108,17 @@ class Instance:
                             self.h_slots.ctypes.data_as(B.P_i64), self.pairs.ctypes.data_as(B.P_i32),
                             B.ctypes.byref(self.done))
         bstride = kc.stride(0)
-        self.write_args = (self.new_k.data_ptr(), self.new_k.stride(0), self.new_v.data_ptr(),
-                           self.new_v.stride(0), kc.data_ptr(), vc.data_ptr(), bstride, wl.num_blocks,
-                           self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(),
-                           self.h_slots.ctypes.data_as(B.P_i64), self.h_pos.ctypes.data_as(B.P_i32), S,
-                           wl.num_kv_heads, wl.head_dim, wl.block_size)
         self.decode_args = (self.out.data_ptr(), None, self.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bstride,
                             wl.num_blocks, self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(), S,
                             wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, max_seq_len,
                             partition_size, wl.scale, workspace.data_ptr(), workspace.numel())
+        # the step: new tokens written, tables updated and decode, one launch
+        self.step_args = (self.out.data_ptr(), None, self.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bstride,
+                          wl.num_blocks, self.d_table.data_ptr(), self.width, self.d_lens.data_ptr(), S,
+                          wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, max_seq_len,
+                          partition_size, wl.scale, self.new_k.data_ptr(), self.new_k.stride(0),
+                          self.new_v.data_ptr(), self.new_v.stride(0), self.h_slots.ctypes.data_as(B.P_i64),
+                          self.h_pos.ctypes.data_as(B.P_i32), workspace.data_ptr(), workspace.numel())
 
     def decode(self, stream):
         rc = self.lib.pa_paged_decode(*self.decode_args, stream)
@@ -124,8 +128,9 @@ class Instance:
 
 def run_step(inst, B, stream):
     """One decode step on one instance (host pool append, copy-on-write
-    copies if any, the token write with its table update, decode); returns
-    the attended lengths."""
+    copies if any, then one launch that writes the new tokens, updates the
+    device tables and lengths from the slots and decodes); returns the
+    attended lengths."""
     L = inst.lib
     rc = L.pa_pool_append_batch(*inst.append_args)
     if rc != 0:
@@ -135,10 +140,9 @@ def run_step(inst, B, stream):
         B.pa_copy_blocks([inst.state.kc, inst.state.vc], cow)
         B.pa_pool_copies_done(inst.state.pool)
     inst.h_pos[:] = inst.h_lens
-    rc = L.pa_decode_append(*inst.write_args, stream)
+    rc = L.pa_paged_decode_append(*inst.step_args, stream)
     if rc != 0:
         raise RuntimeError(L.pa_last_error().decode())
-    inst.decode(stream)
     inst.h_lens += 1
     return inst.h_lens.copy()
 

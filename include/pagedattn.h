@@ -402,6 +402,34 @@ int pa_paged_decode(void* out, float* lse, const void* q,
                     int32_t partition_size, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode_append followed by pa_paged_decode, in one launch per 256
+ * sequences: row s's new token (K/V rows = row s of key/value, slot
+ * slots[s], position positions[s]) is written to the cache, block_tables[s]
+ * [positions[s] / B] becomes slots[s] / B and seq_lens[s] becomes
+ * positions[s] + 1, and the row attends over all positions[s] + 1 tokens.
+ * Every work-group of a row takes the row's length and the new position's
+ * block from the host arrays and reads the new token from key/value, so none
+ * reads what the launch writes; rows with slot -1 are plain decode rows
+ * (seq_lens[s] as stored).  Run pa_copy_blocks for the step's pairs first.
+ * ("PagedAttention: fragmentation, blocks, block tables", 2. The block table,
+ * 3. The slot mapping, the copy-on-write section and the attention-metadata
+ * section.)
+ * Arguments as pa_paged_decode and pa_decode_append (slots, positions: HOST
+ * arrays of num_seqs entries; block_tables and seq_lens are written);
+ * bf16 caches only.  Errors as those two, plus PA_ERR_INVALID for a
+ * position outside [0, max_seq_len) or a slot past the pool. */
+int pa_paged_decode_append(void* out, float* lse, const void* q,
+                           void* key_cache, void* value_cache,
+                           int64_t cache_block_stride, int32_t num_blocks,
+                           int32_t* block_tables, int32_t bt_stride, int32_t* seq_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                           int32_t partition_size, float scale,
+                           const void* key, int64_t key_row_stride,
+                           const void* value, int64_t value_row_stride,
+                           const int64_t* slots, const int32_t* positions,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_paged_decode over E4M3 caches written by pa_reshape_and_cache_fp8: K_t
  * and V_t above are the codes' values times k_scale and v_scale.  Codes are
  * converted to bf16 exactly; the logits use scale * k_scale (rounded to fp32)

@@ -78,6 +78,9 @@ _SIGS = {
     "pa_paged_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_paged_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "pa_paged_decode_append": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
+                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
+                                       c_vp, c_i64, c_vp, c_i64, P_i64, P_i32, c_vp, c_sz, c_vp]),
     "pa_paged_decode_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                     c_vp, c_sz, c_vp]),
@@ -461,8 +464,27 @@ def pa_paged_decode_fp8(out, q, key_cache, value_cache, block_tables, seq_lens, 
             workspace, stream, True, k_scale, v_scale)
 
 
+def pa_paged_decode_append(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale,
+                           key, value, slots, positions, partition_size=512, lse=None, workspace=None,
+                           stream=None):
+    """pa_decode_append + pa_paged_decode in one launch: key/value [S, Hkv, D]
+    bf16 device rows of the new tokens; slots (host int64 [S]) and positions
+    (host int32 [S]); block_tables and seq_lens are updated in place."""
+    for t, name in ((key, "key"), (value, "value")):
+        _bf16(t, name)
+        if t.dim() != 3 or t.shape[0] != q.shape[0] or tuple(t.shape[1:]) != tuple(key_cache.shape[2:]) \
+                or t.stride()[1:] != (t.shape[2], 1):
+            raise InvalidArgument(PA_ERR_INVALID, f"{name} must be [S, Hkv, D] with contiguous rows")
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    if sl.shape != (q.shape[0],) or pos.shape != (q.shape[0],):
+        raise InvalidArgument(PA_ERR_INVALID, "slots and positions must have one entry per sequence")
+    _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
+            workspace, stream, False, 1.0, 1.0, append=(key, value, sl, pos))
+
+
 def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
-            workspace, stream, fp8, k_scale, v_scale):
+            workspace, stream, fp8, k_scale, v_scale, append=None):
     import torch
     nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache, fp8)
     _bf16(q, "q")
@@ -485,7 +507,11 @@ def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len,
     args = (out.data_ptr(), lse.data_ptr() if lse is not None else None, q.data_ptr(), key_cache.data_ptr(),
             value_cache.data_ptr(), bstride, nb, block_tables.data_ptr(), block_tables.stride(0),
             seq_lens.data_ptr(), S, hq, hkv, d, bs, max_seq_len, partition_size, scale)
-    if fp8:
+    if append is not None:
+        k, v, sl, pos = append
+        _check(lib().pa_paged_decode_append(*args, k.data_ptr(), k.stride(0), v.data_ptr(), v.stride(0), _i64p(sl),
+                                            _i32p(pos), ws_ptr, ws_bytes, _stream(q, stream)))
+    elif fp8:
         _check(lib().pa_paged_decode_fp8(*args, k_scale, v_scale, ws_ptr, ws_bytes, _stream(q, stream)))
     else:
         _check(lib().pa_paged_decode(*args, ws_ptr, ws_bytes, _stream(q, stream)))

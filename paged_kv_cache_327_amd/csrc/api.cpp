@@ -208,12 +208,22 @@ size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int
 
 namespace {
 
+// The new tokens of an appending decode (all NULL for a plain one).
+struct NewTokens {
+  const void* key = nullptr;
+  int64_t key_row_stride = 0;
+  const void* value = nullptr;
+  int64_t value_row_stride = 0;
+  const int64_t* slots = nullptr;
+  const int32_t* positions = nullptr;
+};
+
 int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* key_cache,
                 const void* value_cache, int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
                 int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
                 int32_t partition_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, const NewTokens& nt = NewTokens()) {
   pa::clear_error();
   if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
@@ -243,6 +253,23 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
                     workspace ? workspace_bytes : (size_t)0);
   if (parts > 65535) return pa::fail(PA_ERR_INVALID, "%s: too many partitions (%lld)", fn, (long long)parts);
+  const bool append = nt.slots != nullptr;
+  if (append) {
+    if (!nt.key || !nt.value || !nt.positions) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+    if (!aligned(nt.key, 16) || !aligned(nt.value, 16))
+      return pa::fail(PA_ERR_INVALID, "%s: key/value must be 16-byte aligned", fn);
+    if (nt.key_row_stride < row || nt.value_row_stride < row || nt.key_row_stride % 8 || nt.value_row_stride % 8)
+      return pa::fail(PA_ERR_INVALID, "%s: row strides must be multiples of 8 and >= Hkv*D", fn);
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      if (nt.slots[i] < 0) continue;
+      if (nt.slots[i] >= num_slots)
+        return pa::fail(PA_ERR_INVALID, "%s: row %d has slot %lld past the pool", fn, i, (long long)nt.slots[i]);
+      if (nt.positions[i] < 0 || nt.positions[i] >= max_seq_len)
+        return pa::fail(PA_ERR_INVALID, "%s: row %d has position %d outside [0, max_seq_len)", fn, i,
+                        nt.positions[i]);
+    }
+  }
   pa::DecodeArgs a{};
   a.out = out;
   a.lse = lse;
@@ -270,6 +297,15 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     a.ws_out = static_cast<float*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((rows * head_dim * 4) + 255) / 256 * 256);
   }
+  if (append) {
+    a.new_key = nt.key;
+    a.new_key_stride = nt.key_row_stride;
+    a.new_value = nt.value;
+    a.new_value_stride = nt.value_row_stride;
+    a.wr_tables = const_cast<int32_t*>(block_tables);
+    a.wr_lens = const_cast<int32_t*>(seq_lens);
+    return hip_status(fn, pa::launch_paged_decode_append(a, nt.slots, nt.positions, stream));
+  }
   return hip_status(fn, pa::launch_paged_decode(a, stream));
 }
 
@@ -285,6 +321,29 @@ int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache,
   return decode_impl("paged_decode", out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks,
                      block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_seq_len, partition_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_append(void* out, float* lse, const void* q, void* key_cache, void* value_cache,
+                           int64_t cache_block_stride, int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
+                           int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_seq_len, int32_t partition_size,
+                           float scale, const void* key, int64_t key_row_stride, const void* value,
+                           int64_t value_row_stride, const int64_t* slots, const int32_t* positions, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  NewTokens nt;
+  nt.key = key;
+  nt.key_row_stride = key_row_stride;
+  nt.value = value;
+  nt.value_row_stride = value_row_stride;
+  nt.slots = slots;
+  nt.positions = positions;
+  if (num_seqs > 0 && !slots) {
+    pa::clear_error();
+    return pa::fail(PA_ERR_INVALID, "paged_decode_append: NULL argument");
+  }
+  return decode_impl("paged_decode_append", out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                     block_tables, bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_seq_len, partition_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream, nt);
 }
 
 int pa_paged_decode_fp8(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,

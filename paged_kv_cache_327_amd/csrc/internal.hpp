@@ -89,8 +89,18 @@ struct DecodeArgs {
   int32_t fp8;     // caches hold E4M3 codes (1 byte per element)
   float* ws_out;  // [S][Hq][max_parts][D]   (max_parts > 1 only)
   float* ws_lse;  // [S][Hq][max_parts]
+  // appending decode only: the new tokens' K/V rows and the writable tables
+  // and lengths (the same arrays as block_tables and seq_lens)
+  const void* new_key;
+  int64_t new_key_stride;
+  const void* new_value;
+  int64_t new_value_stride;
+  int32_t* wr_tables;
+  int32_t* wr_lens;
 };
 int launch_paged_decode(const DecodeArgs& a, void* stream);
+// slots, positions: host arrays of num_seqs entries (kernel arguments)
+int launch_paged_decode_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, void* stream);
 
 struct PrefillArgs {
   void* out;

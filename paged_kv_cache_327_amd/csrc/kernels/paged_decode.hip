@@ -133,8 +133,31 @@ __device__ __forceinline__ void broadcast4(uint32_t x, bool up4, uint32_t (&out)
   out[3] = up4 ? b : b2;
 }
 
-template <int D, int G, bool BIG, bool F8>
-__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
+// Appending decode (APP): one new token per sequence of the launch, its slot
+// and position in the kernel arguments (up to kAppendRows sequences per
+// launch).  Every work-group of sequence s takes the sequence's length
+// (position + 1) and the block of the new position's table entry (slot / B)
+// from these arguments and reads the new token's K/V from the input rows, so
+// it never reads a table entry, length or cache row that this launch writes;
+// the work-group of the partition holding the new token writes its head's
+// K/V rows to the slot, and the one of head 0 also the table entry and the
+// length.  The result is that of the cache write with the table update
+// followed by decode, in one launch.
+constexpr int kAppendRows = 256;
+struct AppendRows {
+  int64_t slots[kAppendRows];
+  int32_t pos[kAppendRows];
+  int32_t row0;
+  int32_t n;
+};
+struct NoAppend {
+  int32_t row0;
+};
+template <bool APP>
+using RowsOf = typename std::conditional<APP, AppendRows, NoAppend>::type;
+
+template <int D, int G, bool BIG, bool F8, bool APP>
+__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, RowsOf<APP> rows) {
   using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
   constexpr int PPL = D / 64;   // groups of 8 elements per lane per token
   constexpr int NW = D / 16;    // packed bf16 pairs per lane per token
@@ -147,7 +170,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   __shared__ float s_l[kWaves][4][G];
   __shared__ float s_m[kWaves][G];
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  static_assert(!(APP && F8), "appending decode takes bf16 caches");
+  const int part = blockIdx.x, g = blockIdx.y, s = APP ? rows.row0 + (int)blockIdx.z : (int)blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (SGPR) so that the tile loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -166,9 +190,28 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   const int width = (a.max_seq_len + Bmask) >> lgB;   // table entries that may be read
   const float scale = a.scale * kLog2e;
 
+  // APP: this sequence's new token (position, slot) and the block its
+  // position's table entry names after the append
+  int64_t app_slot = -1;
+  int app_pos = -1;
+  if constexpr (APP) {
+    app_slot = rows.slots[blockIdx.z];
+    app_pos = rows.pos[blockIdx.z];
+  }
+  const bool app = APP && app_slot >= 0;
+  const int app_j = app ? app_pos >> lgB : -1;
+  const int app_blk = app ? (int)(app_slot >> lgB) : 0;
+  // table entry j as the kernel sees it (APP: the new position's entry from
+  // the arguments)
+  auto entry = [&](int j) __attribute__((always_inline)) {
+    const int b = bt_row[j];
+    return APP && j == app_j ? app_blk : b;
+  };
+
   // Independent loads first: the length, the queries and (B < 16) the first
   // chunk's table entries, so that their latencies overlap.
   int len = a.seq_lens[s];
+  if (app) len = app_pos + 1;
   uint4 qr[G][PPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -182,7 +225,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
     int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
     nj = nj < width - j0 ? nj : width - j0;
     for (int i = tid; i < nj; i += 256) {
-      int b = bt_row[j0 + i];
+      int b = entry(j0 + i);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       s_bt[i] = b;
     }
@@ -201,10 +244,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf) {
         const int i = (tw + k * kWaves * kTile + hf * kHalf) >> lgB;
-        pre[k][hf] = bt_row[i < wmax ? i : wmax];
+        pre[k][hf] = entry(i < wmax ? i : wmax);
       }
     const int is = start >> lgB;
-    pre_start = bt_row[is < wmax ? is : wmax];
+    pre_start = entry(is < wmax ? is : wmax);
   }
 
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
@@ -217,6 +260,26 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
   // per-lane constant part of a K/V element offset (BIG: tokens grp, grp + 8
   // of the tile relative to its first token)
   const int lane_off = g * D + lane_dim<D, F8>(0, 0, li);
+
+  // APP: the new token's K/V rows of this head in the input, and their copy
+  // into the cache by the partition that holds the new position
+  const T* new_k = nullptr;
+  const T* new_v = nullptr;
+  if constexpr (APP) {
+    new_k = static_cast<const T*>(a.new_key) + (int64_t)s * a.new_key_stride + g * D;
+    new_v = static_cast<const T*>(a.new_value) + (int64_t)s * a.new_value_stride + g * D;
+    if (app && app_pos / P == part && wave == 0 && lane < 2 * (D / 8)) {
+      const int c = lane % (D / 8);
+      const int64_t dst = (int64_t)app_blk * bstride + (app_slot & Bmask) * row_elems + g * D + 8 * c;
+      T* cache = const_cast<T*>(lane < D / 8 ? kcache : vcache);
+      const T* src = lane < D / 8 ? new_k : new_v;
+      *reinterpret_cast<uint4*>(cache + dst) = *reinterpret_cast<const uint4*>(src + 8 * c);
+      if (g == 0 && lane == 0) {
+        if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
+        a.wr_lens[s] = app_pos + 1;
+      }
+    }
+  }
 
   float m_own[NSET], l_own[NSET], acc[G][PPL][8];
 #pragma unroll
@@ -246,11 +309,12 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
         const T* kb[NH];
         const T* vb[NH];
         int64_t roff[NH][2];
+        bool isnew[NH][2] = {};
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) {
           const int th = t0 + hf * kHalf;
           const int tc = th < c1 ? th : c0;          // wave-uniform
-          int blk = __builtin_amdgcn_readfirstlane(fetched ? (th < c1 ? pf[hf] : pre_start) : bt_row[tc >> lgB]);
+          int blk = __builtin_amdgcn_readfirstlane(fetched ? (th < c1 ? pf[hf] : pre_start) : entry(tc >> lgB));
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
           const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
           kb[hf] = kcache + base;
@@ -260,6 +324,13 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u)
             roff[hf][u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
+          if constexpr (APP) {
+            // the token a lane loads is tc + its row offset; the new one comes
+            // from the input
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              isnew[hf][u] = app && tc + (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) == app_pos;
+          }
         }
         if constexpr (F8) {
           using P = typename KVt::Piece;
@@ -272,29 +343,40 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) r.v[2 * hf + u] = *reinterpret_cast<const P*>(vb[hf] + roff[hf][u]);
         } else {
+          const T* kp[NH][2];
+          const T* vp[NH][2];
+#pragma unroll
+          for (int hf = 0; hf < NH; ++hf)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              kp[hf][u] = APP && isnew[hf][u] ? new_k + lane_dim<D, F8>(0, 0, li) : kb[hf] + roff[hf][u];
+              vp[hf][u] = APP && isnew[hf][u] ? new_v + lane_dim<D, F8>(0, 0, li) : vb[hf] + roff[hf][u];
+            }
 #pragma unroll
           for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
               for (int k = 0; k < PPL; ++k)
-                r.k[2 * hf + u][k] = *reinterpret_cast<const uint4*>(kb[hf] + roff[hf][u] + 64 * k);
+                r.k[2 * hf + u][k] = *reinterpret_cast<const uint4*>(kp[hf][u] + 64 * k);
 #pragma unroll
           for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
               for (int k = 0; k < PPL; ++k)
-                r.v[2 * hf + u][k] = *reinterpret_cast<const uint4*>(vb[hf] + roff[hf][u] + 64 * k);
+                r.v[2 * hf + u][k] = *reinterpret_cast<const uint4*>(vp[hf][u] + 64 * k);
         }
       } else {
         int64_t off[2 * NH];
+        bool isnew[2 * NH] = {};
 #pragma unroll
         for (int u = 0; u < 2 * NH; ++u) {
           int t = t0 + (u >> 1) * kHalf + grp + 8 * (u & 1);
           t = t < c1 ? t : c0;
           const int64_t blk = s_bt[(t >> lgB) - j0];
           off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
+          if constexpr (APP) isnew[u] = app && t == app_pos;
         }
         if constexpr (F8) {
           using P = typename KVt::Piece;
@@ -303,14 +385,21 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
           for (int u = 0; u < 2 * NH; ++u) r.v[u] = *reinterpret_cast<const P*>(vcache + off[u]);
         } else {
+          const T* kp[2 * NH];
+          const T* vp[2 * NH];
+#pragma unroll
+          for (int u = 0; u < 2 * NH; ++u) {
+            kp[u] = APP && isnew[u] ? new_k + lane_dim<D, F8>(0, 0, li) : kcache + off[u];
+            vp[u] = APP && isnew[u] ? new_v + lane_dim<D, F8>(0, 0, li) : vcache + off[u];
+          }
 #pragma unroll
           for (int u = 0; u < 2 * NH; ++u)
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kcache + off[u] + 64 * k);
+            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kp[u] + 64 * k);
 #pragma unroll
           for (int u = 0; u < 2 * NH; ++u)
 #pragma unroll
-            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vcache + off[u] + 64 * k);
+            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vp[u] + 64 * k);
         }
       }
     };
@@ -550,24 +639,53 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[row] = (M + fast_log2(W)) * kLn2;
 }
 
-template <int D, int G>
-int launch_g(const DecodeArgs& a, hipStream_t st) {
+template <int D, int G, bool BIG, bool F8>
+int launch_parts(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  if (a.fp8) {
-    if (a.log2_block_size >= 4)
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, true>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, true>), grid, dim3(256), 0, st, a);
-  } else {
-    if (a.log2_block_size >= 4)
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false>), grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false>), grid, dim3(256), 0, st, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return (int)e;
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, BIG, F8, false>), grid, dim3(256), 0, st, a, NoAppend{0});
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int launch_merge(const DecodeArgs& a, hipStream_t st) {
+  if (a.max_parts <= 1) return 0;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, st, a);
   return (int)hipGetLastError();
+}
+
+template <int D, int G>
+int launch_g(const DecodeArgs& a, hipStream_t st) {
+  const bool big = a.log2_block_size >= 4;
+  int e;
+  if (a.fp8)
+    e = big ? launch_parts<D, G, true, true>(a, st) : launch_parts<D, G, false, true>(a, st);
+  else
+    e = big ? launch_parts<D, G, true, false>(a, st) : launch_parts<D, G, false, false>(a, st);
+  return e != 0 ? e : launch_merge<D>(a, st);
+}
+
+// Appending decode: the sequences go in launches of up to kAppendRows, each
+// with its rows' slots and positions in the arguments; one merge follows.
+template <int D, int G>
+int launch_g_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, hipStream_t st) {
+  const bool big = a.log2_block_size >= 4;
+  for (int32_t r0 = 0; r0 < a.num_seqs; r0 += kAppendRows) {
+    AppendRows rows{};
+    rows.row0 = r0;
+    rows.n = a.num_seqs - r0 < kAppendRows ? a.num_seqs - r0 : kAppendRows;
+    for (int32_t i = 0; i < rows.n; ++i) {
+      rows.slots[i] = slots[r0 + i];
+      rows.pos[i] = positions[r0 + i];
+    }
+    const dim3 grid(a.max_parts, a.num_kv_heads, rows.n);
+    if (big)
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(256), 0, st, a, rows);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false, true>), grid, dim3(256), 0, st, a, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return launch_merge<D>(a, st);
 }
 
 template <int D>
@@ -585,11 +703,32 @@ int launch_d(const DecodeArgs& a, hipStream_t st) {
   return (int)hipErrorInvalidValue;
 }
 
+template <int D>
+int launch_d_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, hipStream_t st) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g_append<D, 1>(a, slots, positions, st);
+    case 2: return launch_g_append<D, 2>(a, slots, positions, st);
+    case 3: return launch_g_append<D, 3>(a, slots, positions, st);
+    case 4: return launch_g_append<D, 4>(a, slots, positions, st);
+    case 5: return launch_g_append<D, 5>(a, slots, positions, st);
+    case 6: return launch_g_append<D, 6>(a, slots, positions, st);
+    case 7: return launch_g_append<D, 7>(a, slots, positions, st);
+    case 8: return launch_g_append<D, 8>(a, slots, positions, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int launch_paged_decode(const DecodeArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
   return a.head_dim == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+int launch_paged_decode_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, void* stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  return a.head_dim == 64 ? launch_d_append<64>(a, slots, positions, st)
+                          : launch_d_append<128>(a, slots, positions, st);
 }
 
 }  // namespace pa

@@ -108,3 +108,66 @@ def test_padding_rows_change_nothing_and_bad_calls_are_rejected():
     with pytest.raises(B.InvalidArgument):
         B.pa_decode_append(k, k, h.kc, h.vc, h.table_dev, h.seq_lens_dev, np.zeros(S, dtype=np.int64),
                            np.full(S, -1, dtype=np.int32))       # a row with a slot needs a position
+
+
+@pytest.mark.parametrize("block_size,partition_size", [(16, 64), (16, 0), (4, 64), (1, 128)])
+def test_fused_decode_append_equals_append_then_decode(block_size, partition_size):
+    """pa_paged_decode_append gives the same bits as pa_decode_append followed
+    by pa_paged_decode: outputs, lse, caches, tables and lengths, over steps
+    with copy-on-write of forked tails and with padding rows (slot -1)."""
+    print(f"[fused append] B={block_size} P={partition_size}", flush=True)
+    wl = forked_batch(block_size)
+    steps = 6
+    S = wl.num_seqs
+    width = -(-(max(wl.seq_lens) + steps) // block_size)
+    msl = max(wl.seq_lens) + steps
+    h1, h2 = HipStep(wl, bt_width=width), HipStep(wl, bt_width=width)
+    lens = h1.seq_lens.astype(np.int64).copy()
+    rng = np.random.default_rng([block_size, 9])
+    for step in range(steps):
+        rows = [s for s in range(S) if not (step == 2 and s % 3 == 1)]     # some rows skip a step
+        slots = np.full(S, -1, dtype=np.int64)
+        pairs_all = []
+        for h in (h1, h2):
+            sl, pairs = B.pa_pool_append_batch(h.pool, rows, [1] * len(rows))
+            pairs_all.append([tuple(p) for p in pairs.tolist() if p[0] >= 0])
+            B.pa_copy_blocks([h.kc, h.vc], pairs_all[-1])
+            B.pa_pool_copies_done(h.pool)
+            slots[rows] = sl
+        assert pairs_all[0] == pairs_all[1]
+        pos = lens.astype(np.int32)
+        k = to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
+        v = to_device(workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim)))
+        q = to_device(workloads.normal_bf16(rng, (S, wl.num_q_heads, wl.head_dim)))
+        o1, o2 = torch.empty_like(q), torch.empty_like(q)
+        l1 = torch.empty((S, wl.num_q_heads), dtype=torch.float32, device="cuda")
+        l2 = torch.empty_like(l1)
+        B.pa_decode_append(k, v, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, slots, pos)
+        B.pa_paged_decode(o1, q, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, msl, wl.scale,
+                          partition_size=partition_size, lse=l1)
+        B.pa_paged_decode_append(o2, q, h2.kc, h2.vc, h2.table_dev, h2.seq_lens_dev, msl, wl.scale, k, v, slots,
+                                 pos, partition_size=partition_size, lse=l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2), step
+        lens[rows] += 1
+    assert torch.equal(h1.table_dev, h2.table_dev) and torch.equal(h1.seq_lens_dev, h2.seq_lens_dev)
+    assert h1.seq_lens_dev.cpu().numpy().tolist() == lens.tolist()
+    assert torch.equal(h1.kc.view(torch.int16), h2.kc.view(torch.int16))
+    assert torch.equal(h1.vc.view(torch.int16), h2.vc.view(torch.int16))
+
+
+def test_fused_decode_append_rejects_bad_positions():
+    wl = forked_batch(16)
+    h = HipStep(wl, bt_width=8)
+    S = wl.num_seqs
+    k = torch.zeros((S, wl.num_kv_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((S, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    msl = max(wl.seq_lens) + 1
+    slots = np.zeros(S, dtype=np.int64)
+    with pytest.raises(B.InvalidArgument):                      # position past max_seq_len
+        B.pa_paged_decode_append(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale, k, k, slots,
+                                 np.full(S, msl, dtype=np.int32))
+    with pytest.raises(B.InvalidArgument):                      # slot past the pool
+        B.pa_paged_decode_append(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale, k, k,
+                                 np.full(S, wl.num_blocks * 16, dtype=np.int64), np.zeros(S, dtype=np.int32))
