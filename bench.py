@@ -39,7 +39,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s; prefill TFLOP/s"
-DECODE_KERNEL = "decode_partition_kernel<128, 4>"
+DECODE_KERNEL = "decode_partition_kernel<128, 4, true, false, false>"  # D, G, B >= 16, E4M3, appending
 COUNTERS = os.path.join(ROOT, "profiles", "decode_partition_llama3_8b_traffic.txt")
 COPY_CALIBRATION_BYTES = 512 << 20
 
@@ -243,8 +243,13 @@ def measure_tiny(torch, B, hip_side, workloads, reps=200):
     q = hip_side.to_device(workloads.query_bits(wl.seed, wl.num_seqs, wl.num_q_heads, wl.head_dim))
     out = torch.empty_like(q)
     msl = max(wl.seq_lens)
-    sec = time_launches(torch, lambda: B.pa_paged_decode(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl,
-                                                         wl.scale, partition_size=0), reps)
+    B.pa_paged_decode(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale, partition_size=0)  # checks
+    args = (out.data_ptr(), None, q.data_ptr(), h.kc.data_ptr(), h.vc.data_ptr(), h.kc.stride(0), wl.num_blocks,
+            h.table_dev.data_ptr(), h.table_dev.stride(0), h.seq_lens_dev.data_ptr(), wl.num_seqs, wl.num_q_heads,
+            wl.num_kv_heads, wl.head_dim, wl.block_size, msl, 0, wl.scale, None, 0,
+            torch.cuda.current_stream().cuda_stream)
+    L = B.lib()
+    sec = time_launches(torch, lambda: L.pa_paged_decode(*args), reps)
     return {"workload": "4 sequences of 1, 17, 33, 100 tokens, 8/2 heads, d 64, B 16", "decode_us": round(sec * 1e6, 2)}
 
 
@@ -567,9 +572,14 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), insta
     # one step's write: 64 new tokens quantised into their slots
     k = hip_side.to_device(workloads.normal_bf16(np.random.default_rng(1), (S, wl.num_kv_heads, wl.head_dim)))
     slots = torch.from_numpy(hs[0].step_slots.astype(np.int64)).cuda()
-    t_w = time_launches(torch, lambda: B.pa_reshape_and_cache_fp8(k, k, hs[0].kc, hs[0].vc, slots, *scales), 200)
+    B.pa_reshape_and_cache_fp8(k, k, hs[0].kc, hs[0].vc, slots, *scales)          # argument checks
+    w_args = (k.data_ptr(), k.stride(0), k.data_ptr(), k.stride(0), hs[0].kc.data_ptr(), hs[0].vc.data_ptr(),
+              hs[0].kc.stride(0), wl.num_blocks, slots.data_ptr(), S, wl.num_kv_heads, wl.head_dim, wl.block_size,
+              scales[0], scales[1], torch.cuda.current_stream().cuda_stream)
+    L = B.lib()
+    t_w = time_launches(torch, lambda: L.pa_reshape_and_cache_fp8(*w_args), 200)
     res = {"workload": f"{wl.name}, E4M3 K/V with per-cache scales", "scales": list(scales),
-           "kernel": DECODE_KERNEL.replace(">", ", fp8>"), "decode_us": round(sec * 1e6, 2),
+           "kernel": "decode_partition_kernel<128, 4, true, true, false>", "decode_us": round(sec * 1e6, 2),
            "bytes_per_launch": int(alg), "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
            "seqs_per_s": round(S / sec, 1), "write_64_tokens_us": round(t_w * 1e6, 2)}
     del hs, qs
