@@ -317,6 +317,25 @@ def test_device_calls_validate_on_host():
     assert dec() == B.PA_ERR_INVALID and "workspace" in L.pa_last_error().decode()
     assert L.pa_paged_decode_workspace_size(4, 32, 128, 1000, 512) > 0
     assert L.pa_paged_decode_workspace_size(4, 32, 128, 500, 512) == 0
+    # appending decode and decode append: a position outside [0, max_seq_len),
+    # a slot past the pool, a missing positions array, a negative position
+    slots = np.array([0, 17, -1, 40], dtype=np.int64)
+    pos = np.array([0, 5, 7, 999], dtype=np.int32)
+
+    def dap(sl=slots, ps=pos, msl=1000):
+        return L.pa_paged_decode_append(_vp(fake), None, _vp(fake), _vp(fake), _vp(fake), 16 * 8 * 128, 100,
+                                        _vp(fake), 64, _vp(fake), 4, 32, 8, 128, 16, msl, 0, 0.1, _vp(fake),
+                                        8 * 128, _vp(fake), 8 * 128,
+                                        sl.ctypes.data_as(B.P_i64) if sl is not None else None,
+                                        ps.ctypes.data_as(B.P_i32) if ps is not None else None, None, 0, None)
+    assert dap(msl=999) == B.PA_ERR_INVALID and "position" in L.pa_last_error().decode()
+    assert dap(sl=np.array([0, 17, -1, 1600], dtype=np.int64)) == B.PA_ERR_INVALID      # 100 blocks x 16
+    assert dap(ps=None) == B.PA_ERR_INVALID
+    assert dap(sl=None) == B.PA_ERR_INVALID
+    neg = np.array([0, -3, 7, 9], dtype=np.int32)
+    assert L.pa_decode_append(_vp(fake), 1024, _vp(fake), 1024, _vp(fake), _vp(fake), 16 * 1024, 100, _vp(fake),
+                              64, _vp(fake), slots.ctypes.data_as(B.P_i64), neg.ctypes.data_as(B.P_i32), 4, 8,
+                              128, 16, None) == B.PA_ERR_INVALID
 
 
 @pytest.mark.parametrize("kernel_bs", [32, 16, 8, 1])

@@ -171,3 +171,45 @@ def test_fused_decode_append_rejects_bad_positions():
     with pytest.raises(B.InvalidArgument):                      # slot past the pool
         B.pa_paged_decode_append(out, q, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale, k, k,
                                  np.full(S, wl.num_blocks * 16, dtype=np.int64), np.zeros(S, dtype=np.int32))
+
+
+def test_fused_decode_append_over_more_than_one_launch_of_rows():
+    """300 sequences (two launches of rows, 256 + 44): the same bits as the
+    separate write and decode, and the oracle's attention."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 60, size=300).tolist()
+    wl = workloads.custom("fused_300", 81, 8, 2, 64, 16, lens, q_lens=[0] * 300, extra_blocks=400)
+    print("[fused append] 300 rows", flush=True)
+    S = wl.num_seqs
+    width = -(-(max(lens) + 1) // 16)
+    msl = max(lens) + 1
+    h1, h2, o = HipStep(wl, bt_width=width), HipStep(wl, bt_width=width), OracleStep(wl, bt_width=width)
+    seqs = list(range(S))
+    slots = None
+    for h in (h1, h2):
+        sl, pairs = B.pa_pool_append_batch(h.pool, seqs, [1] * S)
+        assert (pairs[:, 0] < 0).all()
+        slots = sl if slots is None else slots
+        assert sl.tolist() == slots.tolist()
+    o_slots = []
+    for s in seqs:
+        sl, pair = o.pool.append(s, 1)
+        o_slots += sl
+    pos = np.array(lens, dtype=np.int32)
+    k = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
+    v = workloads.normal_bf16(rng, (S, wl.num_kv_heads, wl.head_dim))
+    q = workloads.normal_bf16(rng, (S, wl.num_q_heads, wl.head_dim))
+    kd, vd, qd = to_device(k), to_device(v), to_device(q)
+    o1, o2 = torch.empty_like(qd), torch.empty_like(qd)
+    B.pa_decode_append(kd, vd, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, slots, pos)
+    B.pa_paged_decode(o1, qd, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, msl, wl.scale, partition_size=64)
+    B.pa_paged_decode_append(o2, qd, h2.kc, h2.vc, h2.table_dev, h2.seq_lens_dev, msl, wl.scale, kd, vd, slots, pos,
+                             partition_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.table_dev, h2.table_dev) and torch.equal(h1.seq_lens_dev, h2.seq_lens_dev)
+    o_table = o.table.astype(np.int64).copy()
+    o_lens = o.seq_lens.astype(np.int64).copy()
+    cache_ops.decode_append(o_table, o_lens, o.kc, o.vc, k, v, o_slots, pos)
+    want, _ = attention.paged_decode(q, o.kc, o.vc, o_table, o_lens, wl.scale)
+    assert_attention_close(o2, want, what="fused append, 300 rows")
