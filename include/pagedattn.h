@@ -226,6 +226,16 @@ int pa_pool_kernel_block_table(const pa_pool* pool, const int64_t* seq_ids, int3
 
 /* Number of free blocks (the capacity test is a subtraction against it). */
 int pa_pool_num_free(const pa_pool* pool, int32_t* out);
+/* Pool usage, into out[0..4]: blocks in use (owned, pinned or held for a
+ * pending copy), free blocks, cached block hashes, tokens over all sequences,
+ * and tail waste -- slots of the sequences' blocks not holding a token,
+ * sum over sequences of B * ceil(len / B) - len (a block shared by forked
+ * sequences counts once per sequence).  ("PagedAttention: fragmentation,
+ * blocks, block tables": the waste is bounded by the last block of each
+ * sequence; "The pantry of pigeonholes", The maths that matter: waste =
+ * B ceil(n / B) - n.)  Errors: PA_ERR_INVALID for a NULL pool or out, or
+ * n_out < 5. */
+int pa_pool_stats(const pa_pool* pool, int64_t* out, int32_t n_out);
 /* Number of cached block hashes (each names one block, free or in use). */
 int pa_pool_num_cached(const pa_pool* pool, int32_t* out);
 /* Pins, pending copies and cached hash of block_id (*hashed_out 0 or 1; the

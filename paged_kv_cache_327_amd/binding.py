@@ -54,6 +54,7 @@ _SIGS = {
     "pa_pool_unpin": (c_i32, [c_vp, c_i64]),
     "pa_pool_copies_done": (c_i32, [c_vp]),
     "pa_pool_num_cached": (c_i32, [c_vp, P_i32]),
+    "pa_pool_stats": (c_i32, [c_vp, P_i64, c_i32]),
     "pa_pool_block_state": (c_i32, [c_vp, c_i32, P_i32, P_i32, ctypes.POINTER(ctypes.c_uint64), P_i32]),
     "pa_pool_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pa_pool_append": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32]),
@@ -195,6 +196,14 @@ def pa_pool_unpin(pool, transfer_id):
 
 def pa_pool_copies_done(pool):
     _check(lib().pa_pool_copies_done(pool.handle))
+
+
+def pa_pool_stats(pool):
+    """dict(used_blocks, free_blocks, cached_blocks, tokens, tail_waste_slots)."""
+    out = np.zeros(5, dtype=np.int64)
+    _check(lib().pa_pool_stats(pool.handle, _i64p(out), 5))
+    return dict(zip(("used_blocks", "free_blocks", "cached_blocks", "tokens", "tail_waste_slots"),
+                    out.tolist()))
 
 
 def pa_pool_num_cached(pool):

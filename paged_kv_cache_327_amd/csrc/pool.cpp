@@ -500,6 +500,22 @@ int pa_pool_num_free(const pa_pool* p, int32_t* out) {
   return PA_OK;
 }
 
+int pa_pool_stats(const pa_pool* p, int64_t* out, int32_t n_out) {
+  pa::clear_error();
+  if (!p || !out || n_out < 5) return pa::fail(PA_ERR_INVALID, "stats: need a pool and room for 5 values");
+  int64_t tokens = 0, held = 0;
+  for (const auto& kv : p->seqs) {
+    tokens += kv.second.len;
+    held += (int64_t)kv.second.blocks.size();
+  }
+  out[0] = (int64_t)p->num_blocks - p->count;           // blocks in use (owned, pinned or held)
+  out[1] = p->count;                                     // free blocks
+  out[2] = (int64_t)p->cached.size();                    // cached block hashes
+  out[3] = tokens;                                       // tokens over all sequences
+  out[4] = held * p->block_size - tokens;                // slots allocated but not yet written
+  return PA_OK;
+}
+
 int pa_pool_num_cached(const pa_pool* p, int32_t* out) {
   pa::clear_error();
   if (!p || !out) return pa::fail(PA_ERR_INVALID, "num_cached: NULL argument");

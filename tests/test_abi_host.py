@@ -152,6 +152,11 @@ def run_cached(seed):
         B.pa_pool_check(p)
         native, model = full_state(p, m, live)
         assert native == model, (seed, op)
+        st = B.pa_pool_stats(p)
+        lens = [m.seq_len(x) for x in live]
+        assert st == {"used_blocks": nb - m.num_free(), "free_blocks": m.num_free(),
+                      "cached_blocks": m.num_cached(), "tokens": sum(lens),
+                      "tail_waste_slots": sum(sizing.tail_waste(n, bs) for n in lens)}, (seed, op)
     return hits
 
 
