@@ -115,14 +115,15 @@ def paged_decode(q_bits: np.ndarray, key_cache: np.ndarray, value_cache: np.ndar
 
 def paged_prefill(q_bits: np.ndarray, key_cache: np.ndarray, value_cache: np.ndarray,
                   block_tables: np.ndarray, query_start_loc, seq_lens, scale: float,
-                  causal: bool = True, rows=None):
+                  causal: bool = True, rows=None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Chunked-prefill attention: request i's queries are rows
     query_start_loc[i] .. query_start_loc[i+1]-1 of q and occupy the last
     q_i positions of its seq_lens[i] tokens.
 
-    q_bits [Tq, Hq, D]; returns out [Tq, Hq, D] fp64 (rows not computed
-    stay zero).  ``rows`` optionally restricts the computation to a set of
-    (request, query row within request) pairs.
+    q_bits [Tq, Hq, D]; caches bf16 bits, or E4M3 codes (uint8) with
+    per-cache scales k_scale / v_scale; returns out [Tq, Hq, D] fp64 (rows
+    not computed stay zero).  ``rows`` optionally restricts the computation
+    to a set of (request, query row within request) pairs.
     """
     Tq, Hq, D = q_bits.shape
     Hkv = key_cache.shape[2]
@@ -149,8 +150,8 @@ def paged_prefill(q_bits: np.ndarray, key_cache: np.ndarray, value_cache: np.nda
         if causal:
             visible = keys[None, :] <= (ctx + js)[:, None]
         for g in range(Hkv):
-            k = gather_sequence(key_cache, block_tables[i], n, g)
-            v = gather_sequence(value_cache, block_tables[i], n, g)
+            k = gather_sequence(key_cache, block_tables[i], n, g, k_scale)
+            v = gather_sequence(value_cache, block_tables[i], n, g, v_scale)
             for h in range(g * G, (g + 1) * G):
                 o, _ = softmax_attend(q[qsl[i] + js, h], k, v, scale, visible)
                 out[qsl[i] + js, h] = o

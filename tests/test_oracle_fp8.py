@@ -127,6 +127,13 @@ def test_decode_over_fp8_caches_equals_bf16_caches_of_the_same_values(k_scale, v
     o8, l8 = attention.paged_decode(q, kc8, vc8, table, lens, 0.125, k_scale, v_scale)
     ob, lb = attention.paged_decode(q, kcb, vcb, table, lens, 0.125)
     assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+    # and chunked prefill: each sequence's last 3 (or fewer) positions as queries
+    ql = [min(3, n) for n in lens]
+    qsl = np.concatenate([[0], np.cumsum(ql)])
+    qp = (rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    p8 = attention.paged_prefill(qp, kc8, vc8, table, qsl, lens, 0.125, k_scale=k_scale, v_scale=v_scale)
+    pb = attention.paged_prefill(qp, kcb, vcb, table, qsl, lens, 0.125)
+    assert np.array_equal(p8, pb)
     # and the E4M3 write touched only the written slots
     written = np.zeros(nb * bs, dtype=bool)
     written[np.concatenate([np.array(x) for x in slots])] = True
