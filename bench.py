@@ -216,7 +216,7 @@ def measure_prefill(torch, B, hip_side, workloads, block_size=16, reps=10):
     sec = time_launches(torch, launch, reps)
     flops = prefill_flops(wl.q_lens, wl.seq_lens, wl.num_q_heads, wl.head_dim)
     return {"workload": "16 prefill chunks of 512 queries over U{0..8192} context tokens",
-            "block_size": block_size, "kernel": "prefill_kernel<128, 4, true, true>",
+            "block_size": block_size, "kernel": "prefill_kernel<128, 4, true, true, false>",
             "us": round(sec * 1e6, 1), "gflop": round(flops / 1e9, 2),
             "tflops": round(flops / sec / 1e12, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -583,6 +583,28 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), insta
            "bytes_per_launch": int(alg), "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
            "seqs_per_s": round(S / sec, 1), "write_64_tokens_us": round(t_w * 1e6, 2)}
     del hs, qs
+    torch.cuda.empty_cache()
+
+    # the mixed step's prefill chunks over E4M3 caches
+    pw = workloads.mixed_step(16, n_decode=0)
+    ph = hip_side.HipStep(pw, gen="device", fp8=scales)
+    pq = hip_side.to_device(workloads.query_bits(pw.seed, sum(pw.q_lens), pw.num_q_heads, pw.head_dim))
+    pout = torch.empty_like(pq)
+    pqsl = torch.tensor(np.concatenate([[0], np.cumsum(pw.q_lens)]), dtype=torch.int32, device="cuda")
+    pmsl = int(max(pw.seq_lens))
+    B.pa_paged_prefill_fp8(pout, pq, ph.kc, ph.vc, ph.table_dev, pqsl, ph.seq_lens_dev, max(pw.q_lens), pmsl,
+                           pw.scale, *scales)                                   # argument checks
+    p_args = (pout.data_ptr(), pq.data_ptr(), ph.kc.data_ptr(), ph.vc.data_ptr(), ph.kc.stride(0), pw.num_blocks,
+              ph.table_dev.data_ptr(), ph.table_dev.stride(0), pqsl.data_ptr(), ph.seq_lens_dev.data_ptr(),
+              pw.num_seqs, max(pw.q_lens), pmsl, pw.num_q_heads, pw.num_kv_heads, pw.head_dim, pw.block_size,
+              pw.scale, scales[0], scales[1], 1, torch.cuda.current_stream().cuda_stream)
+    t_p = time_launches(torch, lambda: L.pa_paged_prefill_fp8(*p_args), 10)
+    pflops = prefill_flops(pw.q_lens, pw.seq_lens, pw.num_q_heads, pw.head_dim)
+    res["prefill"] = {"workload": "16 prefill chunks of 512 queries over U{0..8192} context tokens",
+                      "kernel": "prefill_kernel<128, 4, true, true, true>", "us": round(t_p * 1e6, 1),
+                      "tflops": round(pflops / t_p / 1e12, 1),
+                      "frac": round(pflops / t_p / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del ph, pq, pout
     torch.cuda.empty_cache()
 
     # the 32-layer long-context pool in E4M3 (half the bytes of the bf16 pool)

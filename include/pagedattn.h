@@ -482,6 +482,24 @@ int pa_paged_prefill(void* out, const void* q,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, float scale, int32_t causal, void* stream);
 
+/* pa_paged_prefill over E4M3 caches written by pa_reshape_and_cache_fp8: K
+ * and V are the codes' values times k_scale and v_scale.  Each key tile's
+ * codes become bf16 exactly while they are staged; the logits use
+ * scale * k_scale (rounded to fp32) and the output is multiplied by v_scale.
+ * cache_block_stride is in bytes and must be a multiple of 16.
+ * ("The pantry of pigeonholes", knobs table and "With KV quantisation".)
+ * Errors as pa_paged_prefill, plus PA_ERR_INVALID for a scale that is not
+ * positive and finite. */
+int pa_paged_prefill_fp8(void* out, const void* q,
+                         const void* key_cache, const void* value_cache,
+                         int64_t cache_block_stride, int32_t num_blocks,
+                         const int32_t* block_tables, int32_t bt_stride,
+                         const int32_t* query_start_loc, const int32_t* seq_lens,
+                         int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, float scale, float k_scale, float v_scale,
+                         int32_t causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -85,6 +85,9 @@ _SIGS = {
     "pa_paged_decode_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                     c_vp, c_sz, c_vp]),
+    "pa_paged_prefill_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
+                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
+                                     c_i32, c_vp]),
     "pa_paged_prefill": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
 }
@@ -530,8 +533,22 @@ def pa_paged_prefill(out, q, key_cache, value_cache, block_tables, query_start_l
                      max_query_len, max_seq_len, scale, causal=True, stream=None):
     """out/q [Tq, Hq, D] bf16 contiguous; query_start_loc int32 [S+1];
     seq_lens int32 [S]; block_tables int32 [S, W]."""
+    _prefill(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, max_query_len, max_seq_len,
+             scale, causal, stream, None)
+
+
+def pa_paged_prefill_fp8(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,
+                         max_query_len, max_seq_len, scale, k_scale=1.0, v_scale=1.0, causal=True, stream=None):
+    """pa_paged_prefill over E4M3 caches (uint8 or float8_e4m3fn) with
+    per-cache scales."""
+    _prefill(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, max_query_len, max_seq_len,
+             scale, causal, stream, (k_scale, v_scale))
+
+
+def _prefill(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, max_query_len, max_seq_len,
+             scale, causal, stream, fp8):
     import torch
-    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache, fp8 is not None)
     _bf16(q, "q")
     _bf16(out, "out")
     hq = q.shape[1]
@@ -545,7 +562,10 @@ def pa_paged_prefill(out, q, key_cache, value_cache, block_tables, query_start_l
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1 \
             or block_tables.shape[0] != S:
         raise InvalidArgument(PA_ERR_INVALID, "block_tables must be int32 [S, W] with unit column stride")
-    _check(lib().pa_paged_prefill(out.data_ptr(), q.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-                                  bstride, nb, block_tables.data_ptr(), block_tables.stride(0),
-                                  query_start_loc.data_ptr(), seq_lens.data_ptr(), S, max_query_len,
-                                  max_seq_len, hq, hkv, d, bs, scale, int(bool(causal)), _stream(q, stream)))
+    args = (out.data_ptr(), q.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), bstride, nb,
+            block_tables.data_ptr(), block_tables.stride(0), query_start_loc.data_ptr(), seq_lens.data_ptr(), S,
+            max_query_len, max_seq_len, hq, hkv, d, bs, scale)
+    if fp8 is None:
+        _check(lib().pa_paged_prefill(*args, int(bool(causal)), _stream(q, stream)))
+    else:
+        _check(lib().pa_paged_prefill_fp8(*args, fp8[0], fp8[1], int(bool(causal)), _stream(q, stream)))

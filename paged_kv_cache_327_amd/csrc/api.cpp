@@ -357,16 +357,25 @@ int pa_paged_decode_fp8(void* out, float* lse, const void* q, const void* key_ca
                      max_seq_len, partition_size, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
-int pa_paged_prefill(void* out, const void* q, const void* key_cache, const void* value_cache,
-                     int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
-                     const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
-                     int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                     int32_t block_size, float scale, int32_t causal, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int prefill_impl(const char* fn, void* out, const void* q, const void* key_cache, const void* value_cache,
+                 int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                 const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, float scale, int32_t causal, bool fp8, float k_scale, float v_scale,
+                 void* stream) {
   pa::clear_error();
-  const char* fn = "paged_prefill";
   if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
+  if (fp8 && cache_block_stride % 16)
+    return pa::fail(PA_ERR_INVALID, "%s: cache_block_stride %lld must be a multiple of 16 for E4M3 caches", fn,
+                    (long long)cache_block_stride);
+  if (fp8 && !(k_scale > 0.f && v_scale > 0.f && k_scale < __builtin_huge_valf() && v_scale < __builtin_huge_valf()))
+    return pa::fail(PA_ERR_INVALID, "%s: k_scale and v_scale must be positive and finite", fn);
   if (num_seqs < 0 || max_query_len < 0) return pa::fail(PA_ERR_INVALID, "%s: negative size", fn);
   if (num_seqs == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !block_tables || !query_start_loc || !seq_lens)
@@ -395,9 +404,36 @@ int pa_paged_prefill(void* out, const void* q, const void* key_cache, const void
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.log2_block_size = ilog2(block_size);
-  a.scale = scale;
+  a.scale = fp8 ? scale * k_scale : scale;
   a.causal = causal;
+  a.fp8 = fp8 ? 1 : 0;
+  a.v_scale = fp8 ? v_scale : 1.f;
   return hip_status(fn, pa::launch_paged_prefill(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_prefill(void* out, const void* q, const void* key_cache, const void* value_cache,
+                     int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                     const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+                     int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, float scale, int32_t causal, void* stream) {
+  return prefill_impl("paged_prefill", out, q, key_cache, value_cache, cache_block_stride, num_blocks, block_tables,
+                      bt_stride, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len, num_q_heads,
+                      num_kv_heads, head_dim, block_size, scale, causal, false, 1.f, 1.f, stream);
+}
+
+int pa_paged_prefill_fp8(void* out, const void* q, const void* key_cache, const void* value_cache,
+                         int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
+                         int32_t bt_stride, const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, float scale, float k_scale, float v_scale,
+                         int32_t causal, void* stream) {
+  return prefill_impl("paged_prefill_fp8", out, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                      block_tables, bt_stride, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len,
+                      num_q_heads, num_kv_heads, head_dim, block_size, scale, causal, true, k_scale, v_scale, stream);
 }
 
 }  // extern "C"

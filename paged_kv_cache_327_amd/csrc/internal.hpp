@@ -116,8 +116,10 @@ struct PrefillArgs {
   int32_t num_seqs, max_query_len, max_seq_len;
   int32_t num_q_heads, num_kv_heads, head_dim;
   int32_t log2_block_size;
-  float scale;
+  float scale;     // softmax scale (times k_scale for E4M3 caches)
   int32_t causal;
+  int32_t fp8;     // caches hold E4M3 codes (1 byte per element)
+  float v_scale;   // 1 for bf16 caches
 };
 int launch_paged_prefill(const PrefillArgs& a, void* stream);
 

@@ -77,13 +77,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D, int HW, bool CAUSAL, bool BIG>
+template <int D, int HW, bool CAUSAL, bool BIG, bool F8>
 __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
   constexpr int DB = D / 32;                 // 32-row blocks of head_dim in O^T
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   constexpr int UPT = 32 * CPR / 256;        // (key pair, chunk) units per thread
+  // E4M3 caches (F8): a row is D bytes, in 16-byte chunks of 16 codes that
+  // become two 16-byte bf16 pieces in LDS
+  constexpr int CPR8 = D / 16;               // chunks per row
+  constexpr int KPI8 = 64 / CPR8;            // BIG: keys per load instruction
+  constexpr int NU8 = 64 * CPR8 / 256;       // otherwise: (key, chunk) units per thread
   __shared__ Smem<D> sm;
 
   // Work-groups are dealt to the 8 XCDs round-robin by linear id, and each
@@ -205,14 +210,40 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     ch_[u] = unit % CPR;
   }
   int blk_next[BIG ? 1 : UPT][2];             // table entries, one tile ahead of the loads
-  u32x4_t kr[NI], vr[NI];                     // staged K/V of the tile being loaded
+  constexpr int NS = F8 ? (BIG ? 16 / KPI8 : NU8) : NI;
+  u32x4_t kr[NS], vr[NS];                     // staged K/V of the tile being loaded
+  // F8 staging: lane -> (key kr08 of each load, chunk chunk8); byte offsets
+  const int kr08 = lane / CPR8, chunk8 = lane % CPR8;
+  uint32_t voff8[F8 && BIG ? NS : 1];
+  if constexpr (F8 && BIG) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      voff8[j] = (uint32_t)((KPI8 * j + kr08) * row_elems + (int64_t)g * D + 16 * chunk8);
+  }
+  const uint32_t voff8_row0 = (uint32_t)((int64_t)g * D + 16 * chunk8);
+  int key8_[F8 && !BIG ? NU8 : 1], ch8_[F8 && !BIG ? NU8 : 1], blk8_[F8 && !BIG ? NU8 : 1];
+  if constexpr (F8 && !BIG) {
+#pragma unroll
+    for (int u = 0; u < NU8; ++u) {
+      key8_[u] = (tid + 256 * u) / CPR8;
+      ch8_[u] = (tid + 256 * u) % CPR8;
+    }
+  }
 
   auto wave_key = [&](int tile) {
     const int kw = tile * kKeys + 16 * wave;
     return kw < kv_end ? kw : 0;
   };
   auto fetch_table = [&](int tile) {
-    if constexpr (BIG) {
+    if constexpr (F8 && !BIG) {
+#pragma unroll
+      for (int u = 0; u < NU8; ++u) {
+        int p = tile * kKeys + key8_[u];
+        p = p < kv_end ? p : 0;
+        const int b = bt_row[p >> lgB];
+        blk8_[u] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+      }
+    } else if constexpr (BIG) {
       int b = bt_row[wave_key(tile) >> lgB];
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       blk_next[0][0] = __builtin_amdgcn_readfirstlane(b);
@@ -229,7 +260,29 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     }
   };
   auto issue_loads = [&](int tile) {
-    if constexpr (BIG) {
+    if constexpr (F8 && BIG) {
+      const int kw = wave_key(tile);
+      const int lim = kv_end - 1 - kw;        // rows 0 .. lim of the wave's 16 are keys
+      const int64_t base = (int64_t)blk_next[0][0] * bstride + (int64_t)(kw & Bmask) * row_elems;
+      const char* kb = reinterpret_cast<const char*>(a.key_cache) + base;
+      const char* vb = reinterpret_cast<const char*>(a.value_cache) + base;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint32_t off = KPI8 * j + kr08 <= lim ? voff8[j] : voff8_row0;
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
+      }
+    } else if constexpr (F8) {
+#pragma unroll
+      for (int u = 0; u < NU8; ++u) {
+        int p = tile * kKeys + key8_[u];
+        p = p < kv_end ? p : 0;
+        const int64_t off = (int64_t)blk8_[u] * bstride + (int64_t)(p & Bmask) * row_elems + (int64_t)g * D +
+                            16 * ch8_[u];
+        kr[u] = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.key_cache) + off);
+        vr[u] = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.value_cache) + off);
+      }
+    } else if constexpr (BIG) {
       const int kw = wave_key(tile);
       const int lim = kv_end - 1 - kw;        // rows 0 .. lim of the wave's 16 are keys
       const int64_t base = ((int64_t)blk_next[0][0] * bstride + (int64_t)(kw & Bmask) * row_elems) * 2;
@@ -254,8 +307,30 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         }
     }
   };
+  // 16 E4M3 codes -> two 16-byte pieces of bf16 (exact conversion)
+  auto store8 = [&](uint16_t* dst, const u32x4_t c) __attribute__((always_inline)) {
+    u32x4_t lo, hi;
+    lo[0] = e4m3x2_to_bf16x2<false>(c[0]);
+    lo[1] = e4m3x2_to_bf16x2<true>(c[0]);
+    lo[2] = e4m3x2_to_bf16x2<false>(c[1]);
+    lo[3] = e4m3x2_to_bf16x2<true>(c[1]);
+    hi[0] = e4m3x2_to_bf16x2<false>(c[2]);
+    hi[1] = e4m3x2_to_bf16x2<true>(c[2]);
+    hi[2] = e4m3x2_to_bf16x2<false>(c[3]);
+    hi[3] = e4m3x2_to_bf16x2<true>(c[3]);
+    *reinterpret_cast<u32x4_t*>(dst) = lo;
+    *reinterpret_cast<u32x4_t*>(dst + 8) = hi;
+  };
   auto store_tile = [&](int buf) {
-    if constexpr (BIG) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int key = BIG ? 16 * wave + KPI8 * j + kr08 : key8_[BIG ? 0 : j];
+        const int c = BIG ? chunk8 : ch8_[BIG ? 0 : j];
+        store8(&sm.k[buf][key * Smem<D>::kRow + 16 * c], kr[j]);
+        store8(&sm.v[buf][key * Smem<D>::kVRow + 16 * c], vr[j]);
+      }
+    } else if constexpr (BIG) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int key = 16 * wave + KPI * j + kr0;
@@ -432,7 +507,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
     const int qi = qw + 32 * qb + col;
     if (qi < q_len) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? (F8 ? a.v_scale / lt : 1.f / lt) : 0.f;
       uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)(q_begin + qi) * a.num_q_heads + h) * D;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
@@ -455,14 +530,23 @@ int launch_hw(const PrefillArgs& a, hipStream_t st) {
   if (n * 256 > 0xffffffffLL) return (int)hipErrorInvalidConfiguration;   // grid size in work-items is 32-bit
   const dim3 grid((unsigned)n);
   const bool big = a.log2_block_size >= 4;
-  if (a.causal && big)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, true, true>), grid, dim3(256), 0, st, a);
+  if (a.fp8) {
+    if (a.causal && big)
+      hipLaunchKernelGGL((prefill_kernel<D, HW, true, true, true>), grid, dim3(256), 0, st, a);
+    else if (a.causal)
+      hipLaunchKernelGGL((prefill_kernel<D, HW, true, false, true>), grid, dim3(256), 0, st, a);
+    else if (big)
+      hipLaunchKernelGGL((prefill_kernel<D, HW, false, true, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, HW, false, false, true>), grid, dim3(256), 0, st, a);
+  } else if (a.causal && big)
+    hipLaunchKernelGGL((prefill_kernel<D, HW, true, true, false>), grid, dim3(256), 0, st, a);
   else if (a.causal)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, true, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, HW, true, false, false>), grid, dim3(256), 0, st, a);
   else if (big)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, HW, false, true, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, HW, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, HW, false, false, false>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 

@@ -168,6 +168,10 @@ class HipStep:
         bt = self.table_dev[seqs].contiguous()
         sl = self.seq_lens_dev[seqs].contiguous()
         msl = max_seq_len or max(1, int(self.seq_lens[seqs].max()))
-        B.pa_paged_prefill(out, q, self.kc, self.vc, bt, torch.from_numpy(qsl).to(dev), sl,
-                           max(q_lens), msl, self.wl.scale, causal=causal)
+        if self.fp8 is None:
+            B.pa_paged_prefill(out, q, self.kc, self.vc, bt, torch.from_numpy(qsl).to(dev), sl,
+                               max(q_lens), msl, self.wl.scale, causal=causal)
+        else:
+            B.pa_paged_prefill_fp8(out, q, self.kc, self.vc, bt, torch.from_numpy(qsl).to(dev), sl,
+                                   max(q_lens), msl, self.wl.scale, *self.fp8, causal=causal)
         return out

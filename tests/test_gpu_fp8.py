@@ -143,3 +143,65 @@ def test_fp8_rejects_bad_scales_and_strides():
     view = wide[:, :16 * 64].view(4, 16, 1, 64)                                           # stride 1032
     with pytest.raises(B.InvalidArgument):
         B.pa_reshape_and_cache_fp8(k, k, view, view, sl)
+
+
+def run_prefill_parity(wl, scales, causal=True):
+    print(f"[fp8] prefill {wl.name} scales={scales} causal={causal}", flush=True)
+    seqs = list(range(wl.num_seqs))
+    h, o = HipStep(wl, fp8=scales), OracleStep(wl, fp8=scales)
+    q = workloads.query_bits(wl.seed, sum(wl.q_lens), wl.num_q_heads, wl.head_dim)
+    out = h.prefill(q, seqs, causal=causal)
+    qsl = np.concatenate([[0], np.cumsum(wl.q_lens)]).astype(np.int64)
+    want = attention.paged_prefill(q, o.kc, o.vc, o.table, qsl, o.seq_lens, wl.scale, causal=causal, **o.scales())
+    assert_attention_close(out, want, what=f"{wl.name} fp8 prefill")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("gqa", [(4, 4), (8, 2), (32, 8), (12, 4)])
+@pytest.mark.parametrize("block_size", [1, 16, 32])
+def test_fp8_prefill_shapes(head_dim, gqa, block_size):
+    hq, hkv = gqa
+    ctx = [0, 5, 64, 100, 0, 1, 200]
+    q = [1, 31, 32, 33, 70, 128, 1]
+    lens = [c + n for c, n in zip(ctx, q)]
+    wl = workloads.custom(f"fp8_prefill_d{head_dim}_g{hq // hkv}_b{block_size}", 61, hq, hkv, head_dim,
+                          block_size, lens, q_lens=q)
+    run_prefill_parity(wl, (0.0173, 0.05))
+
+
+@pytest.mark.parametrize("scales", SCALES)
+def test_fp8_prefill_scales_and_non_causal(scales):
+    wl = workloads.custom("fp8_prefill_scales", 62, 32, 8, 128, 16, [40, 300, 77, 513], q_lens=[40, 65, 7, 256])
+    run_prefill_parity(wl, scales, causal=True)
+    run_prefill_parity(wl, scales, causal=False)
+
+
+def test_fp8_mixed_step_prefill_sampled():
+    """The mixed step's 16 chunks of 512 queries over U{0..8192}-token contexts
+    (K/V drawn on the device) on E4M3 caches: sampled rows against the oracle."""
+    wl = workloads.mixed_step(16, n_decode=0)
+    print("[fp8] mixed-step prefill", flush=True)
+    scales = (0.05, 0.05)
+    h = HipStep(wl, gen="device", fp8=scales)
+    seqs = list(range(wl.num_seqs))
+    q = workloads.query_bits(wl.seed, sum(wl.q_lens), wl.num_q_heads, wl.head_dim)
+    out = h.prefill(q, seqs).float().cpu().numpy()
+    rng = np.random.default_rng(3)
+    qsl = np.concatenate([[0], np.cumsum(wl.q_lens)])
+    for i in rng.choice(wl.num_seqs, 4, replace=False):
+        kb, vb = h.logical_kv_bits(int(i))
+        k8, v8 = fp8.quantize_bf16(kb, scales[0]), fp8.quantize_bf16(vb, scales[1])
+        n = len(kb)
+        for j in (0, wl.q_lens[i] - 1):
+            row = int(qsl[i] + j)
+            vis = n - wl.q_lens[i] + j + 1
+            G = wl.num_q_heads // wl.num_kv_heads
+            want = np.zeros((wl.num_q_heads, wl.head_dim))
+            for g in range(wl.num_kv_heads):
+                kk = fp8.dequantize(k8[:vis, g], scales[0])
+                vv = fp8.dequantize(v8[:vis, g], scales[1])
+                qq = attention.bf16_to_f64(q[row, g * G:(g + 1) * G])
+                o_, _ = attention.softmax_attend(qq, kk, vv, wl.scale)
+                want[g * G:(g + 1) * G] = o_
+            err = np.abs(out[row] - want)
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3, (i, j, err.max())
