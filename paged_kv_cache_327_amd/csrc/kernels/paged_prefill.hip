@@ -11,13 +11,20 @@
 // head, a tile of 32 * (4 / HW) queries).  Each wave owns one head and 32
 // queries.  Key tiles of 64 keys are gathered through the block table into
 // LDS once per work-group and used by all of its waves (the GQA sharing):
-//   * K and V are stored row-major [key][d]; the V^T operand is read with
-//     gfx950's transposing LDS read (ds_read_b64_tr_b16).  Loads of keys past
-//     the sequence end are redirected to a written row and those keys are
-//     masked out of the softmax, so bytes of unwritten slots (NaN, say) can
-//     never reach a product.
-//   * With B >= 16 each wave stages one 16-key run of a block per tile: the
-//     block id is a scalar load and the row base a scalar address.
+//   * K and V are stored row-major [key][d] with the 16-byte chunks of each
+//     row permuted (an XOR with a function of the row), which keeps both the
+//     S^T operand reads and the transposing V^T reads (gfx950's
+//     ds_read_b64_tr_b16) free of bank conflicts without padding.  Loads of
+//     keys past the sequence end are redirected to a written row and those
+//     keys are masked out of the softmax, so bytes of unwritten slots (NaN,
+//     say) can never reach a product.
+//   * bf16 caches go from HBM straight into LDS (global_load_lds_dwordx4:
+//     lane l of a wave writes bytes 16 l .. 16 l + 15 of a 1 KiB window, so
+//     each lane fetches the chunk that the permuted layout puts there); no
+//     register holds a staged tile.  E4M3 codes are staged in registers and
+//     converted to bf16 on their way into LDS.
+//   * Each wave stages 16 keys of the tile.  With B >= 16 they lie in one
+//     block: the block id is a scalar load and the row base a scalar address.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
 //     so the softmax max and sum are in-lane (plus one exchange between the
 //     two lane halves).
@@ -28,8 +35,10 @@
 //     running maximum only when a score exceeds it by more than 8 (log2
 //     units), which keeps the result exact and rescales rare.
 //   * The next key tile's K/V loads are in flight while the current tile is
-//     computed (register staging, double-buffered LDS, one barrier per tile);
-//     block-table entries are fetched one further tile ahead.
+//     computed (double-buffered LDS, one barrier per tile); block-table
+//     entries are fetched one further tile ahead.
+#include <type_traits>
+
 #include "../internal.hpp"
 #include "common.hpp"
 
@@ -50,20 +59,33 @@ constexpr int kSortMax = 256;    // requests ordered by work up to this many
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kSlack = 8.0f;
 
-// Both tiles are row-major [key][d] in LDS of 64 four-byte banks.  K rows
-// are padded to D + 8 elements (the rows read by one S^T operand fall on
-// distinct banks).  V rows are padded to D + 32 elements, a stride of 16 (or
-// 48) banks: a transposing read serves 32 lanes at a time, two 16-lane groups
-// 16 elements apart, each reading 8 bytes from four consecutive rows, and with
-// this stride the 32 lanes cover all 64 banks once (with D + 16 they met
-// twice on half the banks; measured as 25 % of LDS cycles lost to conflicts).
+// LDS tiles (K and V alike): 64 rows [key][d] of D bf16 elements, no
+// padding.  Chunk c (elements 8c .. 8c + 7) of row r is stored at chunk
+// position c ^ chunk_swz(r).  LDS has 64 four-byte banks.  With D = 128 a
+// row spans all of them and the XOR takes the row's low four bits with its
+// two halves exchanged; with D = 64 two rows share the banks and the XOR
+// takes row bits 1..3, bit 1 moved to the top.  Either way:
+//   * the S^T operand read (16 lanes, rows r .. r + 15, one chunk each)
+//     meets 16 different chunk positions (D = 64: 8 per row parity);
+//   * a transposing V^T read (32 lanes, 4 consecutive rows from a multiple
+//     of 4, 4 consecutive chunks from a multiple of 4, 8 bytes per lane)
+//     puts the 4 rows into 4 different 64-byte groups of banks.
 template <int D>
-struct Smem {
-  static constexpr int kRow = D + 8;
-  static constexpr int kVRow = D + 32;
-  uint16_t k[2][kKeys * kRow];
-  uint16_t v[2][kKeys * kVRow];
-};
+__device__ __forceinline__ int chunk_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) | ((row >> 2) & 3) : (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+// element offset of chunk c of row r in a tile
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * D + 8 * (chunk ^ chunk_swz<D>(row));
+}
+
+// One 16-byte piece per lane from global memory straight into LDS: lane l
+// writes dst + 16 l (dst is the same for the whole wave).
+__device__ __forceinline__ void load_to_lds16(const void* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -82,14 +104,15 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
   constexpr int DB = D / 32;                 // 32-row blocks of head_dim in O^T
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int UPT = 32 * CPR / 256;        // (key pair, chunk) units per thread
+  constexpr int CPR = D / 8;                 // 16-byte bf16 chunks per K/V row
   // E4M3 caches (F8): a row is D bytes, in 16-byte chunks of 16 codes that
-  // become two 16-byte bf16 pieces in LDS
+  // become two bf16 chunks in LDS
   constexpr int CPR8 = D / 16;               // chunks per row
-  constexpr int KPI8 = 64 / CPR8;            // BIG: keys per load instruction
-  constexpr int NU8 = 64 * CPR8 / 256;       // otherwise: (key, chunk) units per thread
-  __shared__ Smem<D> sm;
+  constexpr int KPI8 = 64 / CPR8;            // keys per load instruction
+  // two buffers of each tile, as separate objects: the compiler then sees
+  // that reads of one never wait for the LDS writes in flight to the other
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kKeys * D], s_k1[kKeys * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kKeys * D], s_v1[kKeys * D];
 
   // Work-groups are dealt to the 8 XCDs round-robin by linear id, and each
   // XCD has its own L2.  Work item (request i, head group y, query tile) is
@@ -183,169 +206,123 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // Tile staging.  Keys at or past kv_end are loaded from a valid row
-  // instead (the wave's first key of the tile, or key 0) and are removed from the
-  // softmax by the score mask below, so whatever bytes unwritten slots hold
-  // never reach a product and the loads need no branch.
-  //   BIG (B >= 16): wave w stages keys n0 + 16 w .. n0 + 16 w + 15, which lie
-  //   in one block; the block id is a scalar load and the row base a scalar
-  //   address, each lane adds a fixed 32-bit offset.
-  //   otherwise: unit u = (key pair kp, 16-byte chunk c); every key looks up
-  //   its own block.
-  constexpr int KPI = 64 / CPR;              // BIG: keys per load instruction
-  constexpr int NI = BIG ? 16 / KPI : 2 * UPT;
-  const int kr0 = lane / CPR, chunk = lane % CPR;
-  uint32_t voff[BIG ? NI : 1];
-  if constexpr (BIG) {
+  // Tile staging.  Wave w stages keys n0 + 16 w .. n0 + 16 w + 15 of tile
+  // n0 / 64, KPI of them per load instruction (bf16: 64 / CPR; E4M3: KPI8),
+  // the lane taking key kr0 and one chunk.  Keys at or past kv_end are loaded
+  // from a valid row instead (the wave's first key of the tile, or key 0) and
+  // are removed from the softmax by the score mask below, so whatever bytes
+  // unwritten slots hold never reach a product and the loads need no branch.
+  //   BIG (B >= 16): the 16 keys lie in one block; its id is a scalar load
+  //   and the row base a scalar address, each lane adds a fixed offset.
+  //   otherwise: every key looks up its own block.
+  // bf16: the lane at byte 16 l of an instruction's LDS window holds row
+  // KPI j + l / CPR, chunk position l % CPR, i.e. chunk cg[j] of that row.
+  constexpr int KPI = F8 ? KPI8 : 64 / CPR;
+  constexpr int NI = 16 / KPI;               // load instructions per wave and tile, each of K and V
+  const int kr0 = lane / (F8 ? CPR8 : CPR);
+  const int pos = lane % (F8 ? CPR8 : CPR);  // bf16: chunk position; E4M3: code chunk
+  uint32_t voff[NI], voff0[NI];              // byte offsets of the lane's row and of row 0 (BIG)
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-      voff[j] = (uint32_t)(((KPI * j + kr0) * row_elems + (int64_t)g * D + 8 * chunk) * 2);
+  for (int j = 0; j < NI; ++j) {
+    const int cg = F8 ? pos : pos ^ chunk_swz<D>(KPI * j + kr0);
+    const int64_t cb = (int64_t)g * D * (F8 ? 1 : 2) + 16 * cg;
+    voff[j] = (uint32_t)((KPI * j + kr0) * row_elems * (F8 ? 1 : 2) + cb);
+    voff0[j] = (uint32_t)cb;
   }
-  const uint32_t voff_row0 = (uint32_t)(((int64_t)g * D + 8 * chunk) * 2);
-  int kp_[UPT], ch_[UPT];
-#pragma unroll
-  for (int u = 0; u < UPT; ++u) {
-    const int unit = tid + 256 * u;
-    kp_[u] = unit / CPR;
-    ch_[u] = unit % CPR;
-  }
-  int blk_next[BIG ? 1 : UPT][2];             // table entries, one tile ahead of the loads
-  constexpr int NS = F8 ? (BIG ? 16 / KPI8 : NU8) : NI;
-  u32x4_t kr[NS], vr[NS];                     // staged K/V of the tile being loaded
-  // F8 staging: lane -> (key kr08 of each load, chunk chunk8); byte offsets
-  const int kr08 = lane / CPR8, chunk8 = lane % CPR8;
-  uint32_t voff8[F8 && BIG ? NS : 1];
-  if constexpr (F8 && BIG) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-      voff8[j] = (uint32_t)((KPI8 * j + kr08) * row_elems + (int64_t)g * D + 16 * chunk8);
-  }
-  const uint32_t voff8_row0 = (uint32_t)((int64_t)g * D + 16 * chunk8);
-  int key8_[F8 && !BIG ? NU8 : 1], ch8_[F8 && !BIG ? NU8 : 1], blk8_[F8 && !BIG ? NU8 : 1];
-  if constexpr (F8 && !BIG) {
-#pragma unroll
-    for (int u = 0; u < NU8; ++u) {
-      key8_[u] = (tid + 256 * u) / CPR8;
-      ch8_[u] = (tid + 256 * u) % CPR8;
-    }
-  }
+  u32x4_t kr[F8 ? NI : 1], vr[F8 ? NI : 1];  // E4M3: staged codes of the tile being loaded
 
   auto wave_key = [&](int tile) {
     const int kw = tile * kKeys + 16 * wave;
     return kw < kv_end ? kw : 0;
   };
-  auto fetch_table = [&](int tile) {
-    if constexpr (F8 && !BIG) {
-#pragma unroll
-      for (int u = 0; u < NU8; ++u) {
-        int p = tile * kKeys + key8_[u];
-        p = p < kv_end ? p : 0;
-        const int b = bt_row[p >> lgB];
-        blk8_[u] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      }
-    } else if constexpr (BIG) {
-      int b = bt_row[wave_key(tile) >> lgB];
-      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      blk_next[0][0] = __builtin_amdgcn_readfirstlane(b);
-    } else {
-#pragma unroll
-      for (int u = 0; u < UPT; ++u)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          int p = tile * kKeys + 2 * kp_[u] + e;
-          p = p < kv_end ? p : 0;
-          int b = bt_row[p >> lgB];
-          blk_next[u][e] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-        }
-    }
+  auto clamp_blk = [&](int b) { return b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b); };
+  // Block ids.  BIG: a wave needs one table entry per tile; lane i of `tab`
+  // holds the entry of tile win + i (a window of 64 tiles, read with
+  // readlane), and `tab_next` the following window, fetched one window
+  // ahead, so the tile loop itself issues no table loads.  Otherwise: the
+  // entries of each lane's NI keys, fetched two tiles ahead (before the
+  // loads of the next tile) and clamped where they are used.
+  int tab = 0, tab_next = 0, win = 0;
+  auto load_window = [&](int w0) {
+    return bt_row[wave_key(w0 + lane) >> lgB];
   };
-  auto issue_loads = [&](int tile) {
-    if constexpr (F8 && BIG) {
-      const int kw = wave_key(tile);
-      const int lim = kv_end - 1 - kw;        // rows 0 .. lim of the wave's 16 are keys
-      const int64_t base = (int64_t)blk_next[0][0] * bstride + (int64_t)(kw & Bmask) * row_elems;
-      const char* kb = reinterpret_cast<const char*>(a.key_cache) + base;
-      const char* vb = reinterpret_cast<const char*>(a.value_cache) + base;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const uint32_t off = KPI8 * j + kr08 <= lim ? voff8[j] : voff8_row0;
-        kr[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
-        vr[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
-      }
-    } else if constexpr (F8) {
-#pragma unroll
-      for (int u = 0; u < NU8; ++u) {
-        int p = tile * kKeys + key8_[u];
-        p = p < kv_end ? p : 0;
-        const int64_t off = (int64_t)blk8_[u] * bstride + (int64_t)(p & Bmask) * row_elems + (int64_t)g * D +
-                            16 * ch8_[u];
-        kr[u] = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.key_cache) + off);
-        vr[u] = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(a.value_cache) + off);
-      }
-    } else if constexpr (BIG) {
-      const int kw = wave_key(tile);
-      const int lim = kv_end - 1 - kw;        // rows 0 .. lim of the wave's 16 are keys
-      const int64_t base = ((int64_t)blk_next[0][0] * bstride + (int64_t)(kw & Bmask) * row_elems) * 2;
-      const char* kb = reinterpret_cast<const char*>(a.key_cache) + base;
-      const char* vb = reinterpret_cast<const char*>(a.value_cache) + base;
+  int ent[BIG ? 1 : NI], ent_next[BIG ? 1 : NI];
+  auto fetch_entries = [&](int tile, int (&e)[BIG ? 1 : NI]) {
+    if constexpr (!BIG) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const uint32_t off = KPI * j + kr0 <= lim ? voff[j] : voff_row0;
-        kr[j] = *reinterpret_cast<const u32x4_t*>(kb + off);
-        vr[j] = *reinterpret_cast<const u32x4_t*>(vb + off);
+        int p = tile * kKeys + 16 * wave + KPI * j + kr0;
+        p = p < kv_end ? p : 0;
+        e[j] = bt_row[p >> lgB];
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < UPT; ++u)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          int p = tile * kKeys + 2 * kp_[u] + e;
-          p = p < kv_end ? p : 0;
-          const int64_t off = (int64_t)blk_next[u][e] * bstride + (int64_t)(p & Bmask) * row_elems + 8 * ch_[u];
-          kr[2 * u + e] = *reinterpret_cast<const u32x4_t*>(kc + off);
-          vr[2 * u + e] = *reinterpret_cast<const u32x4_t*>(vc + off);
-        }
     }
   };
-  // 16 E4M3 codes -> two 16-byte pieces of bf16 (exact conversion)
-  auto store8 = [&](uint16_t* dst, const u32x4_t c) __attribute__((always_inline)) {
+  // the window must cover `tile` (called with tiles in increasing order, one
+  // window at a time)
+  auto advance_window = [&](int tile) {
+    if constexpr (BIG) {
+      if (tile >= win + 64) {
+        win += 64;
+        tab = tab_next;
+        if (win + 64 < n_tiles) tab_next = load_window(win + 64);
+      }
+    }
+  };
+  // byte offset of the piece that load j of `tile` fetches, from a cache's base
+  auto src_off = [&](int tile, int j) __attribute__((always_inline)) {
+    if constexpr (BIG) {
+      const int kw = wave_key(tile);
+      const int lim = kv_end - 1 - kw;       // rows 0 .. lim of the wave's 16 are keys
+      const int blk = clamp_blk(__builtin_amdgcn_readlane(tab, tile - win));
+      const int64_t base = ((int64_t)blk * bstride + (int64_t)(kw & Bmask) * row_elems) * (F8 ? 1 : 2);
+      return base + (KPI * j + kr0 <= lim ? voff[j] : voff0[j]);
+    } else {
+      int p = tile * kKeys + 16 * wave + KPI * j + kr0;
+      p = p < kv_end ? p : 0;
+      return ((int64_t)clamp_blk(ent[j]) * bstride + (int64_t)(p & Bmask) * row_elems) * (F8 ? 1 : 2) + voff0[j];
+    }
+  };
+  const char* kcb = static_cast<const char*>(a.key_cache);
+  const char* vcb = static_cast<const char*>(a.value_cache);
+  // bf16: tile `tile` into LDS tiles kd / vd (rows 16 w .. 16 w + 15)
+  auto load_tile = [&](int tile, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t off = src_off(tile, j);
+      load_to_lds16(kcb + off, kd + (16 * wave + KPI * j) * D);
+      load_to_lds16(vcb + off, vd + (16 * wave + KPI * j) * D);
+    }
+  };
+  // E4M3: codes of tile `tile` into registers
+  auto issue_loads = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t off = src_off(tile, j);
+      kr[j] = *reinterpret_cast<const u32x4_t*>(kcb + off);
+      vr[j] = *reinterpret_cast<const u32x4_t*>(vcb + off);
+    }
+  };
+  // 16 E4M3 codes (code chunk c of row `key`) -> bf16 chunks 2c and 2c + 1
+  // (exact conversion)
+  auto store8 = [&](uint16_t* tile, int key, int c, const u32x4_t x) __attribute__((always_inline)) {
     u32x4_t lo, hi;
-    lo[0] = e4m3x2_to_bf16x2<false>(c[0]);
-    lo[1] = e4m3x2_to_bf16x2<true>(c[0]);
-    lo[2] = e4m3x2_to_bf16x2<false>(c[1]);
-    lo[3] = e4m3x2_to_bf16x2<true>(c[1]);
-    hi[0] = e4m3x2_to_bf16x2<false>(c[2]);
-    hi[1] = e4m3x2_to_bf16x2<true>(c[2]);
-    hi[2] = e4m3x2_to_bf16x2<false>(c[3]);
-    hi[3] = e4m3x2_to_bf16x2<true>(c[3]);
-    *reinterpret_cast<u32x4_t*>(dst) = lo;
-    *reinterpret_cast<u32x4_t*>(dst + 8) = hi;
+    lo[0] = e4m3x2_to_bf16x2<false>(x[0]);
+    lo[1] = e4m3x2_to_bf16x2<true>(x[0]);
+    lo[2] = e4m3x2_to_bf16x2<false>(x[1]);
+    lo[3] = e4m3x2_to_bf16x2<true>(x[1]);
+    hi[0] = e4m3x2_to_bf16x2<false>(x[2]);
+    hi[1] = e4m3x2_to_bf16x2<true>(x[2]);
+    hi[2] = e4m3x2_to_bf16x2<false>(x[3]);
+    hi[3] = e4m3x2_to_bf16x2<true>(x[3]);
+    *reinterpret_cast<u32x4_t*>(&tile[tile_off<D>(key, 2 * c)]) = lo;
+    *reinterpret_cast<u32x4_t*>(&tile[tile_off<D>(key, 2 * c + 1)]) = hi;
   };
-  auto store_tile = [&](int buf) {
-    if constexpr (F8) {
+  auto store_tile = [&](uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int key = BIG ? 16 * wave + KPI8 * j + kr08 : key8_[BIG ? 0 : j];
-        const int c = BIG ? chunk8 : ch8_[BIG ? 0 : j];
-        store8(&sm.k[buf][key * Smem<D>::kRow + 16 * c], kr[j]);
-        store8(&sm.v[buf][key * Smem<D>::kVRow + 16 * c], vr[j]);
-      }
-    } else if constexpr (BIG) {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int key = 16 * wave + KPI * j + kr0;
-        *reinterpret_cast<u32x4_t*>(&sm.k[buf][key * Smem<D>::kRow + 8 * chunk]) = kr[j];
-        *reinterpret_cast<u32x4_t*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * chunk]) = vr[j];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < UPT; ++u)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int key = 2 * kp_[u] + e;
-          *reinterpret_cast<u32x4_t*>(&sm.k[buf][key * Smem<D>::kRow + 8 * ch_[u]]) = kr[2 * u + e];
-          *reinterpret_cast<u32x4_t*>(&sm.v[buf][key * Smem<D>::kVRow + 8 * ch_[u]]) = vr[2 * u + e];
-        }
+    for (int j = 0; j < NI; ++j) {
+      const int key = 16 * wave + KPI * j + kr0;
+      store8(kd, key, pos, kr[j]);
+      store8(vd, key, pos, vr[j]);
     }
   };
 
@@ -361,20 +338,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     l[qb] = 0.f;
   }
 
-  // Staging is unconditional: tiles past the end read valid rows, so no
-  // branch separates a load from its use.
-  fetch_table(0);
-  issue_loads(0);
-  fetch_table(1);
-  store_tile(0);
-  issue_loads(1);
-  fetch_table(2);
-  __syncthreads();
+  // lane constants of the operand reads: S^T reads chunk 2 ks + hf of rows
+  // col and 32 + col (same permutation); V^T reads (see below) rows
+  // tr_c + 4 hf + 8 e (+ multiples of 16) at element 16 tr_g + 4 tr_a + 32 b
+  const int kswz = 8 * (hf ^ chunk_swz<D>(col));
+  const int tr_a = lane & 3, tr_c = (lane >> 2) & 3, tr_g = (lane >> 4) & 1;
+  auto vt_off = [&](int e, int b) __attribute__((always_inline)) {
+    const int r = tr_c + 4 * hf + 8 * e;
+    return tile_off<D>(r, 4 * b + 2 * tr_g + (tr_a >> 1)) + 4 * (tr_a & 1);
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const uint16_t* K = sm.k[buf];
-    const uint16_t* V = sm.v[buf];
+  // One key tile from LDS tiles K / V.
+  auto compute = [&](const int t, const uint16_t* K, const uint16_t* V) __attribute__((always_inline)) {
     // S^T[key][query] for the two 32-key halves of the tile and each query
     // block.  The accumulations are independent: their MFMAs alternate, every
     // K operand read from LDS feeds all query blocks, and the next k-step's K
@@ -387,16 +362,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
     {
-      const uint16_t* krow0 = &K[col * Smem<D>::kRow + 8 * hf];
-      const uint16_t* krow1 = &K[(32 + col) * Smem<D>::kRow + 8 * hf];
-      uint4 ka0 = *reinterpret_cast<const uint4*>(krow0);
-      uint4 ka1 = *reinterpret_cast<const uint4*>(krow1);
+      const uint16_t* krow0 = &K[col * D];
+      const uint16_t* krow1 = &K[(32 + col) * D];
+      auto kread = [&](const uint16_t* row, int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(row + (kswz ^ (16 * ks)));
+      };
+      uint4 ka0 = kread(krow0, 0);
+      uint4 ka1 = kread(krow1, 0);
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         uint4 kn0 = ka0, kn1 = ka1;
         if (ks + 1 < DS) {
-          kn0 = *reinterpret_cast<const uint4*>(krow0 + 16 * (ks + 1));
-          kn1 = *reinterpret_cast<const uint4*>(krow1 + 16 * (ks + 1));
+          kn0 = kread(krow0, ks + 1);
+          kn1 = kread(krow1, ks + 1);
         }
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
@@ -463,13 +441,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     // operand (lane: d = 32 b + col) comes from row-major V with transposing
     // reads: in each 16-lane group (d = dg .. dg + 15), lane a + 4 c points at
     // V[key0 + c][dg + 4 a], which hands lane j the 4 keys of d = dg + j.
-    const int tr_a = lane & 3, tr_c = (lane >> 2) & 3, tr_g = (lane >> 4) & 1;
-    const uint16_t* vbase = &V[tr_c * Smem<D>::kVRow + 16 * tr_g + 4 * tr_a + 4 * hf * Smem<D>::kVRow];
-    auto read_vt = [&](int step, int b) {
+    auto read_vt = [&](int step, int b) __attribute__((always_inline)) {
       const int kb = step >> 1, ks = step & 1;
-      const uint16_t* src = vbase + (32 * kb + 16 * ks) * Smem<D>::kVRow + 32 * b;
-      const uint2 lo = lds_read_tr16(src);
-      const uint2 hi = lds_read_tr16(src + 8 * Smem<D>::kVRow);
+      const uint16_t* src = V + (32 * kb + 16 * ks) * D;
+      const uint2 lo = lds_read_tr16(src + vt_off(0, b));
+      const uint2 hi = lds_read_tr16(src + vt_off(1, b));
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
     uint4 va[DB];
@@ -493,11 +469,55 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) va[b] = vn[b];
     }
-    // stage the next tile into the other buffer and start the one after
-    store_tile(buf ^ 1);
-    issue_loads(t + 2);
-    fetch_table(t + 3);
+  };
+
+  // Tile t from buffer BUF, the next one into the other buffer.  bf16: the
+  // next tile's loads go straight to LDS at the start; E4M3: the staged
+  // codes of the next tile are converted into LDS at the end and the loads
+  // of the one after are issued.  The barrier (which also waits for this
+  // wave's loads into LDS) ends the step.
+  auto step = [&](auto bufc, const int t) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    uint16_t* const kd = BUF ? s_k0 : s_k1;
+    uint16_t* const vd = BUF ? s_v0 : s_v1;
+    if constexpr (!F8) {
+      fetch_entries(t + 2, ent_next);
+      advance_window(t + 1);
+      if (t + 1 < n_tiles) load_tile(t + 1, kd, vd);
+    }
+    compute(t, BUF ? s_k1 : s_k0, BUF ? s_v1 : s_v0);
+    if constexpr (F8) {
+      store_tile(kd, vd);
+      advance_window(t + 2);
+      issue_loads(t + 2);
+      fetch_entries(t + 3, ent);
+    }
     __syncthreads();
+    if constexpr (!F8 && !BIG) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) ent[j] = ent_next[j];
+    }
+  };
+
+  if constexpr (BIG) {
+    tab = load_window(0);
+    if (64 < n_tiles) tab_next = load_window(64);
+  }
+  fetch_entries(0, ent);
+  if constexpr (F8) {
+    issue_loads(0);
+    fetch_entries(1, ent);
+    store_tile(s_k0, s_v0);
+    issue_loads(1);
+    fetch_entries(2, ent);
+  } else {
+    load_tile(0, s_k0, s_v0);
+    fetch_entries(1, ent);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(std::integral_constant<int, 0>(), t);
+    if (t + 1 < n_tiles) step(std::integral_constant<int, 1>(), t + 1);
   }
 
   // normalise and write: in query block qb the lane owns query
