@@ -36,8 +36,10 @@
 //    8 (weights stay <= 2^8): a ballot sends the wave to a rare slow path, so
 //    the fast path has no per-lane branches and the lane groups never need
 //    rescaling against each other.
-//  * Merge: the two groups of each 16-lane row are summed with DPP, rows and
-//    waves go through LDS and are combined with the log-sum-exp identity.  A
+//  * Merge: the two groups of each 16-lane row are summed with DPP, the four
+//    rows with gfx950's lane swaps (v_permlane32_swap, v_permlane16_swap),
+//    and the waves go through LDS and are combined with the log-sum-exp
+//    identity.  A
 //    sequence with one partition writes its bf16 output directly; otherwise
 //    partials (normalised output, log2 lse) go to the workspace for the merge
 //    pass.
@@ -166,8 +168,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   using KVt = KV<D, F8, 2 * NH>;
   constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score slot per lane per set
   __shared__ int32_t s_bt[BIG ? 1 : kChunk];
-  __shared__ float s_acc[kWaves][4][G][D];
-  __shared__ float s_l[kWaves][4][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][D];
+  __shared__ float s_l[kWaves][G];
   __shared__ float s_m[kWaves][G];
 
   static_assert(!(APP && F8), "appending decode takes bf16 caches");
@@ -541,41 +543,82 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   const int nparts = len > 0 ? (len + P - 1) / P : 1;
 
   // Merge.  All lane groups of a wave share the running maxima, so their
-  // partial sums add directly: the two groups of a row with DPP, the four
-  // rows and four waves through LDS.
+  // partial sums add directly: the two groups of each 16-lane row with DPP,
+  // the four rows in registers with gfx950's lane swaps, the four waves
+  // through LDS.  permlane32_swap(x, y) exchanges lanes 32..63 of x with
+  // lanes 0..31 of y, permlane16_swap(x, y) the odd 16-lane rows of x with
+  // the even rows of y; adding the two results of a swap sums rows (0, 2)
+  // and (1, 3), then rows 0 and 1.  With the lane's NV sums flattened as
+  // v = (h PPL + k) 8 + i and paired as below, row r ends with the totals of
+  // v = r Q .. r Q + Q - 1 in its lanes 0..7 (lanes 8..15 hold copies).
+  constexpr int NV = G * PPL * 8;
+  constexpr int Q = NV / 4;
+  float xs[NV];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int k = 0; k < PPL; ++k)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][k][i] += dpp<kDppRor8>(acc[h][k][i]);
+      for (int i = 0; i < 8; ++i) xs[(h * PPL + k) * 8 + i] = acc[h][k][i] + dpp<kDppRor8>(acc[h][k][i]);
+  auto swap_add32 = [](float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+  auto swap_add16 = [](float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+  float tot[Q];
+#pragma unroll
+  for (int m = 0; m < Q; ++m) {
+    // pair 2m = (v m, v 2Q + m) and pair 2m + 1 = (v Q + m, v 3Q + m): after
+    // the 32-lane step each holds its first value in rows 0-1 and its second
+    // in rows 2-3; the 16-lane step then puts v m, Q + m, 2Q + m, 3Q + m in
+    // rows 0, 1, 2, 3
+    const float a = swap_add32(xs[m], xs[2 * Q + m]);
+    const float b = swap_add32(xs[Q + m], xs[3 * Q + m]);
+    tot[m] = swap_add16(a, b);
+  }
   float lp[NSET];
 #pragma unroll
   for (int j = 0; j < NSET; ++j) {
     lp[j] = l_own[j] + dpp<kDppXor1>(l_own[j]);
     lp[j] += dpp<kDppRor8>(lp[j]);
+    lp[j] = swap_add32(lp[j], lp[j]);
+    lp[j] = swap_add16(lp[j], lp[j]);
   }
   if ((lane & 8) == 0) {
+    if constexpr (Q % 8 == 0) {
+      // row r: (h, k) pairs r Q / 8 + c, 8 consecutive elements each
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int c = 0; c < Q / 8; ++c) {
+        const int hk = row * (Q / 8) + c;
+        float* dst = &s_acc[wave][hk / PPL][lane_dim<D, F8>(hk % PPL, 0, li)];
+        *reinterpret_cast<float4*>(dst) = make_float4(tot[8 * c], tot[8 * c + 1], tot[8 * c + 2], tot[8 * c + 3]);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(tot[8 * c + 4], tot[8 * c + 5], tot[8 * c + 6], tot[8 * c + 7]);
+      }
+    } else {
 #pragma unroll
-      for (int k = 0; k < PPL; ++k)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s_acc[wave][row][h][lane_dim<D, F8>(k, i, li)] = acc[h][k][i];
-    if (!b0) {
+      for (int m = 0; m < Q; ++m) {
+        const int v = row * Q + m, hk = v >> 3;
+        s_acc[wave][hk / PPL][lane_dim<D, F8>(hk % PPL, v & 7, li)] = tot[m];
+      }
+    }
+    if (row == 0 && !b0) {
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
         const int h = 4 * j + (li >> 1);
         if (h < G) {
-          s_l[wave][row][h] = lp[j];
-          if (row == 0) s_m[wave][h] = m_own[j];
+          s_l[wave][h] = lp[j];
+          s_m[wave][h] = m_own[j];
         }
       }
     }
   }
   __syncthreads();
 
-  // Combine rows and waves: thread -> (head h, dim d) outputs.
+  // Combine the waves: thread -> (head h, dim d) outputs.
   for (int o = tid; o < G * D; o += 256) {
     const int h = o / D, d = o % D;
     float M = kNegInf;
@@ -587,14 +630,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
       for (int w = 0; w < kWaves; ++w) {
         const float mw = s_m[w][h];
         const float e = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-        float lw = 0.f, aw = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          lw += s_l[w][rr][h];
-          aw += s_acc[w][rr][h][d];
-        }
-        L += lw * e;
-        A += aw * e;
+        L += s_l[w][h] * e;
+        A += s_acc[w][h][d] * e;
       }
     }
     const int hq = g * G + h;
