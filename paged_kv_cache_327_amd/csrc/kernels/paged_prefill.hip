@@ -100,7 +100,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 template <int D, int HW, bool CAUSAL, bool BIG, bool F8>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
   constexpr int DB = D / 32;                 // 32-row blocks of head_dim in O^T
@@ -348,81 +348,88 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     return tile_off<D>(r, 4 * b + 2 * tr_g + (tr_a >> 1)) + 4 * (tr_a & 1);
   };
 
-  // One key tile from LDS tiles K / V.
-  auto compute = [&](const int t, const uint16_t* K, const uint16_t* V) __attribute__((always_inline)) {
-    // S^T[key][query] for the two 32-key halves of the tile and each query
-    // block.  The accumulations are independent: their MFMAs alternate, every
-    // K operand read from LDS feeds all query blocks, and the next k-step's K
-    // operands are read before this step's MFMAs issue.
-    f32x16_t s[kQB][2];
+  // S^T[key][query] of one key tile from LDS tile K, for the two 32-key
+  // halves of the tile and each query block.  The accumulations are
+  // independent: their MFMAs alternate, every K operand read from LDS feeds
+  // all query blocks, and the next k-step's K operands are read before this
+  // step's MFMAs issue.
+  auto qk = [&](const uint16_t* K, f32x16_t (&s)[kQB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
-    {
-      const uint16_t* krow0 = &K[col * D];
-      const uint16_t* krow1 = &K[(32 + col) * D];
-      auto kread = [&](const uint16_t* row, int ks) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(row + (kswz ^ (16 * ks)));
-      };
-      uint4 ka0 = kread(krow0, 0);
-      uint4 ka1 = kread(krow1, 0);
+    const uint16_t* krow0 = &K[col * D];
+    const uint16_t* krow1 = &K[(32 + col) * D];
+    auto kread = [&](const uint16_t* row, int ks) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(row + (kswz ^ (16 * ks)));
+    };
+    uint4 ka0 = kread(krow0, 0);
+    uint4 ka1 = kread(krow1, 0);
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks) {
-        uint4 kn0 = ka0, kn1 = ka1;
-        if (ks + 1 < DS) {
-          kn0 = kread(krow0, ks + 1);
-          kn1 = kread(krow1, ks + 1);
-        }
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          s[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka0), as_bf16x8(qreg[qb][ks]), s[qb][0], 0, 0, 0);
-          s[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka1), as_bf16x8(qreg[qb][ks]), s[qb][1], 0, 0, 0);
-        }
-        ka0 = kn0;
-        ka1 = kn1;
+    for (int ks = 0; ks < DS; ++ks) {
+      uint4 kn0 = ka0, kn1 = ka1;
+      if (ks + 1 < DS) {
+        kn0 = kread(krow0, ks + 1);
+        kn1 = kread(krow1, ks + 1);
       }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        s[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka0), as_bf16x8(qreg[qb][ks]), s[qb][0], 0, 0, 0);
+        s[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka1), as_bf16x8(qreg[qb][ks]), s[qb][1], 0, 0, 0);
+      }
+      ka0 = kn0;
+      ka1 = kn1;
     }
-    // mask and tile max on raw scores.  Register r of half kb holds key
-    // n0 + 32 kb + 8 (r / 4) + 4 hf + r % 4; a key is visible iff its offset
-    // 32 kb + 8 (r / 4) + r % 4 is at most `lim` (one compare per score, on
-    // tiles that reach past the query block's first query only).
+  };
+  // Mask and tile maximum (scaled, log2 units, both lane halves) of query
+  // block qb in tile t.  Register r of half kb holds key
+  // n0 + 32 kb + 8 (r / 4) + 4 hf + r % 4; a key is visible iff its offset
+  // 32 kb + 8 (r / 4) + r % 4 is at most `lim` (one compare per score, on
+  // tiles that reach past the query block's first query only; MASK = false
+  // asserts that no key of the tile needs it).
+  auto tile_max = [&](auto maskc, f32x16_t (&s)[kQB][2], const int t, const int qb) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
     const int n0 = t * kKeys;
-    uint32_t pb[kQB][2][2][4];
+    const int qpos = ctx + qw + 32 * qb + col;     // absolute position of the lane's query
+    const int lim = (CAUSAL ? qpos : kv_len - 1) - n0 - 4 * hf;
+    const bool need_mask = MASK && n0 + kKeys - 1 > (CAUSAL ? ctx + qw + 32 * qb : kv_len - 1);
+    float mt = kNegInf;
+    if (need_mask) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int qpos = ctx + qw + 32 * qb + col;     // absolute position of the lane's query
-      const int lim = (CAUSAL ? qpos : kv_len - 1) - n0 - 4 * hf;
-      const bool need_mask = n0 + kKeys - 1 > (CAUSAL ? ctx + qw + 32 * qb : kv_len - 1);
-      float mt = kNegInf;
-      if (need_mask) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) {
+          s[qb][kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[qb][kb][r] : kNegInf;
+          mt = fmaxf(mt, s[qb][kb][r]);
+        }
+    } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[qb][kb][r] = 32 * kb + 8 * (r >> 2) + (r & 3) <= lim ? s[qb][kb][r] : kNegInf;
-            mt = fmaxf(mt, s[qb][kb][r]);
-          }
-      } else {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
+    }
+    return fmaxf(mt, __shfl_xor(mt, 32)) * scale;
+  };
+  // The running maximum is raised only when the tile's exceeds it by more
+  // than kSlack; the sum and the output are rescaled then.
+  auto rescale = [&](const int qb, const float mt) __attribute__((always_inline)) {
+    if (mt > m[qb] + kSlack) {
+      const float alpha = fast_exp2(m[qb] - mt);
+      l[qb] *= alpha;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kb][r]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale;
-      if (mt > m[qb] + kSlack) {
-        const float alpha = fast_exp2(m[qb] - mt);
-        l[qb] *= alpha;
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+        for (int r = 0; r < 16; ++r) o[qb][b][r] *= alpha;
+      m[qb] = mt;
+    }
+  };
+  // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s;
+  // weights are exp2(score * scale - m), and their bf16 values are summed.
+  auto exp_pack = [&](const f32x16_t (&s)[kQB][2], uint32_t (&pb)[kQB][2][2][4]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][b][r] *= alpha;
-        m[qb] = mt;
-      }
-      // P^T in bf16: B operand slots s of lane half hf <-> registers 8 ks + s;
-      // weights are exp2(score * scale - m), and their bf16 values are summed.
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -435,12 +442,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
             pb[qb][kb][ks][w] = pk;
             l[qb] = dot2_bf16(pk, 0x3F803F80u, l[qb]);
           }
-    }
-    // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
-    // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.  The V^T
-    // operand (lane: d = 32 b + col) comes from row-major V with transposing
-    // reads: in each 16-lane group (d = dg .. dg + 15), lane a + 4 c points at
-    // V[key0 + c][dg + 4 a], which hands lane j the 4 keys of d = dg + j.
+  };
+  // O^T[d][query] += V^T[d][key] P^T[key][query]; slot s of lane half hf in
+  // step (kb, ks) is key 32 kb + 16 ks + 8 (s / 4) + 4 hf + s % 4.  The V^T
+  // operand (lane: d = 32 b + col) comes from row-major V with transposing
+  // reads: in each 16-lane group (d = dg .. dg + 15), lane a + 4 c points at
+  // V[key0 + c][dg + 4 a], which hands lane j the 4 keys of d = dg + j.
+  auto pv = [&](const uint16_t* V, const uint32_t (&pb)[kQB][2][2][4]) __attribute__((always_inline)) {
     auto read_vt = [&](int step, int b) __attribute__((always_inline)) {
       const int kb = step >> 1, ks = step & 1;
       const uint16_t* src = V + (32 * kb + 16 * ks) * D;
@@ -469,6 +477,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) va[b] = vn[b];
     }
+  };
+
+  // One key tile from LDS tiles K / V, its phases one after another.
+  auto compute = [&](const int t, const uint16_t* K, const uint16_t* V) __attribute__((always_inline)) {
+    f32x16_t s[kQB][2];
+    qk(K, s);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) rescale(qb, tile_max(std::true_type(), s, t, qb));
+    uint32_t pb[kQB][2][2][4];
+    exp_pack(s, pb);
+    pv(V, pb);
   };
 
   // Tile t from buffer BUF, the next one into the other buffer.  bf16: the
@@ -514,12 +533,103 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     load_tile(0, s_k0, s_v0);
     fetch_entries(1, ent);
   }
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
+
+  // Software-pipelined tiles (bf16, B >= 16): the leading tiles whose keys
+  // every query of the work-group sees need no mask, and for them step t
+  // runs the QK^T MFMAs of tile t + 1 beside the exponentials of tile t, and
+  // the PV MFMAs of tile t beside the maximum of tile t + 1, so that the
+  // matrix cores and the vector ALUs work at the same time.  K runs one tile
+  // ahead of V: step t reads K(t + 1) and V(t) and loads K(t + 2) and
+  // V(t + 1), each into the buffer of its own parity, which the previous
+  // step finished reading.  The remaining (masked) tiles take the plain
+  // steps above.
+  int t_first = 0;
+  if constexpr (BIG && !F8) {
+    static_assert(kQB == 1, "the pipelined steps hold one query block per wave");
+    const int n_pipe = ((CAUSAL ? ctx + q0 : kv_len - 1) + 1) / kKeys;  // tiles without a mask
+    if (n_pipe >= 2) {
+      // V(t) is loaded one step after K(t), from the same rows: the tile's
+      // row base and the last row that is a key (rows past it load the
+      // wave's first row) are kept from the K load.
+      struct Rows {
+        int64_t base;
+        int lim;
+      };
+      auto tile_rows = [&](int tile) __attribute__((always_inline)) {
+        const int kw = wave_key(tile);
+        const int blk = clamp_blk(__builtin_amdgcn_readlane(tab, tile - win));
+        return Rows{((int64_t)blk * bstride + (int64_t)(kw & Bmask) * row_elems) * 2, kv_end - 1 - kw};
+      };
+      auto load_rows = [&](const char* cache, const Rows r, uint16_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          load_to_lds16(cache + r.base + (KPI * j + kr0 <= r.lim ? voff[j] : voff0[j]), dst + (16 * wave + KPI * j) * D);
+      };
+      advance_window(1);
+      Rows vrows = tile_rows(1);           // rows of the tile whose V is loaded next
+      load_rows(kcb, vrows, s_k1);
+      __syncthreads();
+      f32x16_t sc[kQB][2];
+      qk(s_k0, sc);
+      rescale(0, tile_max(std::false_type(), sc, 0, 0));
+      __syncthreads();   // K(0) is read: its buffer takes K(2) next
+      // step t: K(t + 1) in buffer (t + 1) & 1, V(t) in buffer t & 1
+      auto pstep = [&](auto parc, const int t) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(parc)::value;   // t & 1
+        uint16_t* const k_next = PAR ? s_k0 : s_k1;  // holds K(t + 1)
+        uint16_t* const k_free = PAR ? s_k1 : s_k0;  // K(t) was read last step
+        uint16_t* const v_cur = PAR ? s_v1 : s_v0;   // holds V(t)
+        uint16_t* const v_free = PAR ? s_v0 : s_v1;  // V(t - 1) was read last step
+        load_rows(vcb, vrows, v_free);
+        if (t + 2 < n_tiles) {
+          advance_window(t + 2);
+          vrows = tile_rows(t + 2);
+          load_rows(kcb, vrows, k_free);
+        }
+        f32x16_t sn[kQB][2];
+        uint32_t pb[kQB][2][2][4];
+        qk(k_next, sn);
+        exp_pack(sc, pb);
+        pv(v_cur, pb);
+        const float mt = tile_max(std::false_type(), sn, t + 1, 0);
+        __syncthreads();
+        rescale(0, mt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[0][kb] = sn[0][kb];
+      };
+      int t = 0;
+      for (; t + 2 < n_pipe; t += 2) {
+        pstep(std::integral_constant<int, 0>(), t);
+        pstep(std::integral_constant<int, 1>(), t + 1);
+      }
+      if (t + 1 < n_pipe) {
+        pstep(std::integral_constant<int, 0>(), t);
+        ++t;
+      }
+      // last pipelined tile t = n_pipe - 1: K(t + 1) is loading (if any);
+      // its V goes to the buffer of V(t - 1), then the plain steps go on
+      // from t + 1 with tile t + 1 whole in buffer (t + 1) & 1
+      if (t + 1 < n_tiles) load_rows(vcb, vrows, (t & 1) ? s_v0 : s_v1);
+      uint32_t pb[kQB][2][2][4];
+      exp_pack(sc, pb);
+      pv((t & 1) ? s_v1 : s_v0, pb);
+      __syncthreads();
+      t_first = t + 1;
+    } else {
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();
+  }
+  int t = t_first;
+  if (t & 1) {
+    if (t < n_tiles) step(std::integral_constant<int, 1>(), t);
+    ++t;
+  }
+  for (; t < n_tiles; t += 2) {
     step(std::integral_constant<int, 0>(), t);
     if (t + 1 < n_tiles) step(std::integral_constant<int, 1>(), t + 1);
   }
-
   // normalise and write: in query block qb the lane owns query
   // qw + 32 qb + col, d = 32 b + 8 (r / 4) + 4 hf + r % 4
 #pragma unroll
