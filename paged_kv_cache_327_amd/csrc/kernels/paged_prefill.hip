@@ -268,38 +268,74 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  // byte offset of the piece that load j of `tile` fetches, from a cache's base
-  auto src_off = [&](int tile, int j) __attribute__((always_inline)) {
-    if constexpr (BIG) {
-      const int kw = wave_key(tile);
-      const int lim = kv_end - 1 - kw;       // rows 0 .. lim of the wave's 16 are keys
-      const int blk = clamp_blk(__builtin_amdgcn_readlane(tab, tile - win));
-      const int64_t base = ((int64_t)blk * bstride + (int64_t)(kw & Bmask) * row_elems) * (F8 ? 1 : 2);
-      return base + (KPI * j + kr0 <= lim ? voff[j] : voff0[j]);
-    } else {
-      int p = tile * kKeys + 16 * wave + KPI * j + kr0;
-      p = p < kv_end ? p : 0;
-      return ((int64_t)clamp_blk(ent[j]) * bstride + (int64_t)(p & Bmask) * row_elems) * (F8 ? 1 : 2) + voff0[j];
-    }
+  // B >= 16: a wave's 16 rows of a tile lie in one block, so their base is
+  // wave-uniform (a scalar address) and each lane adds a 32-bit offset;
+  // rows past `lim` (keys at or past kv_end) load the wave's first row.
+  struct Rows {
+    int64_t base;   // bytes from the cache's start
+    int lim;        // rows 0 .. lim of the wave's 16 are keys
+  };
+  auto tile_rows = [&](int tile) __attribute__((always_inline)) {
+    const int kw = wave_key(tile);
+    const int blk = clamp_blk(__builtin_amdgcn_readlane(tab, tile - win));
+    return Rows{((int64_t)blk * bstride + (int64_t)(kw & Bmask) * row_elems) * (F8 ? 1 : 2), kv_end - 1 - kw};
+  };
+  // (the empty asm keeps the offset a 32-bit register value, so that the
+  // address stays scalar base + lane offset instead of becoming a select
+  // between two 64-bit addresses)
+  auto row_off = [&](const Rows& r, int j, auto wholec) __attribute__((always_inline)) {
+    uint32_t off = decltype(wholec)::value || KPI * j + kr0 <= r.lim ? voff[j] : voff0[j];
+    asm("" : "+v"(off));
+    return off;
+  };
+  // B < 16: byte offset of the piece that load j of `tile` fetches (every
+  // key looks up its own block)
+  auto key_off = [&](int tile, int j) __attribute__((always_inline)) {
+    int p = tile * kKeys + 16 * wave + KPI * j + kr0;
+    p = p < kv_end ? p : 0;
+    return ((int64_t)clamp_blk(ent[j]) * bstride + (int64_t)(p & Bmask) * row_elems) * (F8 ? 1 : 2) + voff0[j];
   };
   const char* kcb = static_cast<const char*>(a.key_cache);
   const char* vcb = static_cast<const char*>(a.value_cache);
+  // bf16, B >= 16: the wave's rows of one tile of `cache` into LDS tile dst
+  // (WHOLE asserts that all 16 rows are keys)
+  auto load_rows = [&](const char* cache, const Rows r, uint16_t* dst, auto wholec) __attribute__((always_inline)) {
+    const char* base = cache + r.base;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) load_to_lds16(base + row_off(r, j, wholec), dst + (16 * wave + KPI * j) * D);
+  };
   // bf16: tile `tile` into LDS tiles kd / vd (rows 16 w .. 16 w + 15)
   auto load_tile = [&](int tile, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+    if constexpr (BIG) {
+      const Rows r = tile_rows(tile);
+      load_rows(kcb, r, kd, std::false_type());
+      load_rows(vcb, r, vd, std::false_type());
+    } else {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t off = src_off(tile, j);
-      load_to_lds16(kcb + off, kd + (16 * wave + KPI * j) * D);
-      load_to_lds16(vcb + off, vd + (16 * wave + KPI * j) * D);
+      for (int j = 0; j < NI; ++j) {
+        const int64_t off = key_off(tile, j);
+        load_to_lds16(kcb + off, kd + (16 * wave + KPI * j) * D);
+        load_to_lds16(vcb + off, vd + (16 * wave + KPI * j) * D);
+      }
     }
   };
   // E4M3: codes of tile `tile` into registers
   auto issue_loads = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (BIG) {
+      const Rows r = tile_rows(tile);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t off = src_off(tile, j);
-      kr[j] = *reinterpret_cast<const u32x4_t*>(kcb + off);
-      vr[j] = *reinterpret_cast<const u32x4_t*>(vcb + off);
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t off = row_off(r, j, std::false_type());
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kcb + r.base + off);
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vcb + r.base + off);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int64_t off = key_off(tile, j);
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kcb + off);
+        vr[j] = *reinterpret_cast<const u32x4_t*>(vcb + off);
+      }
     }
   };
   // 16 E4M3 codes (code chunk c of row `key`) -> bf16 chunks 2c and 2c + 1
@@ -534,7 +570,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     fetch_entries(1, ent);
   }
 
-  // Software-pipelined tiles (bf16, B >= 16): the leading tiles whose keys
+  // Software-pipelined tiles (bf16 caches): the leading tiles whose keys
   // every query of the work-group sees need no mask, and for them step t
   // runs the QK^T MFMAs of tile t + 1 beside the exponentials of tile t, and
   // the PV MFMAs of tile t beside the maximum of tile t + 1, so that the
@@ -544,30 +580,39 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   // step finished reading.  The remaining (masked) tiles take the plain
   // steps above.
   int t_first = 0;
-  if constexpr (BIG && !F8) {
+  if constexpr (!F8) {
     static_assert(kQB == 1, "the pipelined steps hold one query block per wave");
     const int n_pipe = ((CAUSAL ? ctx + q0 : kv_len - 1) + 1) / kKeys;  // tiles without a mask
     if (n_pipe >= 2) {
-      // V(t) is loaded one step after K(t), from the same rows: the tile's
-      // row base and the last row that is a key (rows past it load the
-      // wave's first row) are kept from the K load.
-      struct Rows {
-        int64_t base;
-        int lim;
+      // V(t) is loaded one step after K(t), from the same rows: B >= 16
+      // keeps the wave's row base, B < 16 the lanes' offsets (and `ent`
+      // holds the table entries of the tile whose K is loaded next).
+      struct KeyOffs {
+        int64_t off[NI];
       };
-      auto tile_rows = [&](int tile) __attribute__((always_inline)) {
-        const int kw = wave_key(tile);
-        const int blk = clamp_blk(__builtin_amdgcn_readlane(tab, tile - win));
-        return Rows{((int64_t)blk * bstride + (int64_t)(kw & Bmask) * row_elems) * 2, kv_end - 1 - kw};
-      };
-      auto load_rows = [&](const char* cache, const Rows r, uint16_t* dst) __attribute__((always_inline)) {
+      using Addr = typename std::conditional<BIG, Rows, KeyOffs>::type;
+      auto tile_addr = [&](int tile) __attribute__((always_inline)) {
+        if constexpr (BIG) {
+          return tile_rows(tile);
+        } else {
+          KeyOffs k;
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          load_to_lds16(cache + r.base + (KPI * j + kr0 <= r.lim ? voff[j] : voff0[j]), dst + (16 * wave + KPI * j) * D);
+          for (int j = 0; j < NI; ++j) k.off[j] = key_off(tile, j);
+          return k;
+        }
+      };
+      auto load_addr = [&](const char* cache, const Addr& ad, uint16_t* dst, auto wholec) __attribute__((always_inline)) {
+        if constexpr (BIG) {
+          load_rows(cache, ad, dst, wholec);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NI; ++j) load_to_lds16(cache + ad.off[j], dst + (16 * wave + KPI * j) * D);
+        }
       };
       advance_window(1);
-      Rows vrows = tile_rows(1);           // rows of the tile whose V is loaded next
-      load_rows(kcb, vrows, s_k1);
+      Addr vaddr = tile_addr(1);           // rows of the tile whose V is loaded next
+      load_addr(kcb, vaddr, s_k1, std::false_type());
+      fetch_entries(2, ent);
       __syncthreads();
       f32x16_t sc[kQB][2];
       qk(s_k0, sc);
@@ -580,12 +625,13 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         uint16_t* const k_free = PAR ? s_k1 : s_k0;  // K(t) was read last step
         uint16_t* const v_cur = PAR ? s_v1 : s_v0;   // holds V(t)
         uint16_t* const v_free = PAR ? s_v0 : s_v1;  // V(t - 1) was read last step
-        load_rows(vcb, vrows, v_free);
+        load_addr(vcb, vaddr, v_free, std::true_type());   // t + 1 < n_pipe: no key past the end
         if (t + 2 < n_tiles) {
           advance_window(t + 2);
-          vrows = tile_rows(t + 2);
-          load_rows(kcb, vrows, k_free);
+          vaddr = tile_addr(t + 2);
+          load_addr(kcb, vaddr, k_free, std::false_type());
         }
+        fetch_entries(t + 3, ent);
         f32x16_t sn[kQB][2];
         uint32_t pb[kQB][2][2][4];
         qk(k_next, sn);
@@ -608,8 +654,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
       }
       // last pipelined tile t = n_pipe - 1: K(t + 1) is loading (if any);
       // its V goes to the buffer of V(t - 1), then the plain steps go on
-      // from t + 1 with tile t + 1 whole in buffer (t + 1) & 1
-      if (t + 1 < n_tiles) load_rows(vcb, vrows, (t & 1) ? s_v0 : s_v1);
+      // from t + 1 with tile t + 1 whole in buffer (t + 1) & 1 (and, B < 16,
+      // the entries of tile t + 2 in `ent`)
+      if (t + 1 < n_tiles) load_addr(vcb, vaddr, (t & 1) ? s_v0 : s_v1, std::false_type());
       uint32_t pb[kQB][2][2][4];
       exp_pack(sc, pb);
       pv((t & 1) ? s_v1 : s_v0, pb);
