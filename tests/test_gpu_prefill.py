@@ -55,6 +55,25 @@ def test_prefill_non_causal(block_size):
     run_parity(wl, causal=False)
 
 
+@pytest.mark.parametrize("block_size", [1, 16])
+@pytest.mark.parametrize("gqa", [(32, 8), (16, 8)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_unmasked_leading_tiles(block_size, gqa, causal):
+    """Contexts that put the number of leading 64-key tiles no query of a
+    work-group masks at 2, 3 and 4, at the whole tile count (causal ctx 127
+    and 255 with one query; non-causal lengths 128 and 256), and past the
+    64-tile window of block-table entries (4200-token context), so that the
+    steps that overlap one tile's QK^T with the previous tile's softmax run
+    with every parity and hand over to the masked steps at every point."""
+    hq, hkv = gqa
+    ctx = [127, 128, 191, 192, 255, 4200]
+    q = [1, 1, 33, 64, 1, 40]
+    lens = [c + n for c, n in zip(ctx, q)]
+    wl = workloads.custom(f"prefill_lead_g{hq // hkv}_b{block_size}", 55, hq, hkv, 128, block_size, lens,
+                          q_lens=q)
+    run_parity(wl, causal=causal)
+
+
 def test_chunked_matches_one_shot():
     """Chunks of 256 + 256 queries over one 512-token sequence match one chunk
     of 512 (each chunk attends to everything written before it)."""
