@@ -4,7 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
-#include <unordered_set>
+#include <algorithm>
 #include <vector>
 
 #include "internal.hpp"
@@ -181,16 +181,25 @@ int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, i
   if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
   for (int32_t c = 0; c < n_caches; ++c)
     if (!caches[c] || !aligned(caches[c], 16)) return pa::fail(PA_ERR_INVALID, "%s: cache %d NULL or unaligned", fn, c);
-  std::unordered_set<int32_t> dsts, srcs;
+  // duplicate destinations and destinations that are also sources, found on
+  // sorted copies (no per-entry allocation: this runs once per step)
+  std::vector<int32_t> dsts(n_pairs), srcs(n_pairs);
   for (int32_t i = 0; i < n_pairs; ++i) {
     const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
     if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
       return pa::fail(PA_ERR_INVALID, "%s: pair %d (%d, %d) outside [0, %d)", fn, i, s, d, num_blocks);
-    if (!dsts.insert(d).second) return pa::fail(PA_ERR_INVALID, "%s: destination %d named twice", fn, d);
-    srcs.insert(s);
+    dsts[i] = d;
+    srcs[i] = s;
   }
-  for (int32_t d : dsts)
-    if (srcs.count(d)) return pa::fail(PA_ERR_INVALID, "%s: block %d is both a source and a destination", fn, d);
+  std::sort(dsts.begin(), dsts.end());
+  std::sort(srcs.begin(), srcs.end());
+  const auto dup = std::adjacent_find(dsts.begin(), dsts.end());
+  if (dup != dsts.end()) return pa::fail(PA_ERR_INVALID, "%s: destination %d named twice", fn, *dup);
+  for (size_t i = 0, j = 0; i < dsts.size() && j < srcs.size();) {
+    if (dsts[i] == srcs[j])
+      return pa::fail(PA_ERR_INVALID, "%s: block %d is both a source and a destination", fn, dsts[i]);
+    if (dsts[i] < srcs[j]) ++i; else ++j;
+  }
   return hip_status(fn, pa::launch_copy_blocks(caches, n_caches, block_bytes, stride_bytes, pairs, n_pairs, stream));
 }
 

@@ -307,6 +307,22 @@ def test_device_calls_validate_on_host():
         arr = np.array(pairs, dtype=np.int32)
         assert L.pa_copy_blocks(ptrs, 1, 4096, 4096, 4, arr.ctypes.data_as(B.P_i32), len(pairs) // 2,
                                 None) == B.PA_ERR_INVALID
+    # long pair lists of distinct blocks with one planted duplicate
+    # destination, or one destination that is also a source, anywhere in the
+    # list: refused on the host (valid lists are not tried here, they launch)
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        perm = rng.permutation(1000).astype(np.int32)
+        arr = np.stack([perm[:300], perm[300:600]], 1).copy()
+        i, j = rng.choice(300, 2, replace=False)
+        if trial % 2:
+            arr[i, 1] = arr[j, 1]
+            want = "named twice"
+        else:
+            arr[i, 1] = arr[j, 0]
+            want = "both a source and a destination"
+        rc = L.pa_copy_blocks(ptrs, 1, 4096, 4096, 1000, arr.ctypes.data_as(B.P_i32), 300, None)
+        assert rc == B.PA_ERR_INVALID and want in L.pa_last_error().decode()
     # decode: q heads not a multiple of kv heads; partition not a multiple of 64;
     # table too narrow for max_seq_len; missing workspace
     args = dict(hq=32, hkv=8, d=128, bs=16, msl=1000, part=512, bt=64, ws=None, wsb=0)
