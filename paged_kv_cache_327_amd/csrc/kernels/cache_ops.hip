@@ -158,11 +158,12 @@ __global__ void __launch_bounds__(256) slot_mapping_kernel(SlotArgs a) {
 }
 
 constexpr int kMaxCopyCaches = 64;
-constexpr int kMaxCopyPairs = 128;
+constexpr int kMaxCopyPairs = 256;
 constexpr int kCopyUnroll = 4;  // 16-byte vectors per thread per pass
 
-// Pairs and cache pointers travel in the kernel arguments (about 1.6 KiB), so
-// the host's pair list needs no staging buffer.
+// Pairs and cache pointers travel in the kernel arguments (about 2.5 KiB), so
+// the host's pair list needs no staging buffer; a step's copy-on-write pairs
+// (up to 256) and all 64 cache tensors of a 32-layer model take one launch.
 struct CopyBatch {
   char* caches[kMaxCopyCaches];
   int32_t pairs[2 * kMaxCopyPairs];
