@@ -265,22 +265,18 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
 
   // APP: the new token's K/V rows of this head in the input, and their copy
   // into the cache by the partition that holds the new position
+  // (lanes 0 .. 2 D / 8 - 1 of wave 0 copy one 16-byte piece each: the piece
+  // is loaded here and stored after the merge, so that the store neither
+  // waits for the load nor holds up the wave's first K/V loads)
   const T* new_k = nullptr;
   const T* new_v = nullptr;
+  bool app_copy = false;
+  uint4 app_piece = make_uint4(0, 0, 0, 0);
   if constexpr (APP) {
     new_k = static_cast<const T*>(a.new_key) + (int64_t)s * a.new_key_stride + g * D;
     new_v = static_cast<const T*>(a.new_value) + (int64_t)s * a.new_value_stride + g * D;
-    if (app && app_pos / P == part && wave == 0 && lane < 2 * (D / 8)) {
-      const int c = lane % (D / 8);
-      const int64_t dst = (int64_t)app_blk * bstride + (app_slot & Bmask) * row_elems + g * D + 8 * c;
-      T* cache = const_cast<T*>(lane < D / 8 ? kcache : vcache);
-      const T* src = lane < D / 8 ? new_k : new_v;
-      *reinterpret_cast<uint4*>(cache + dst) = *reinterpret_cast<const uint4*>(src + 8 * c);
-      if (g == 0 && lane == 0) {
-        if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
-        a.wr_lens[s] = app_pos + 1;
-      }
-    }
+    app_copy = app && app_pos / P == part && wave == 0 && lane < 2 * (D / 8);
+    if (app_copy) app_piece = *reinterpret_cast<const uint4*>((lane < D / 8 ? new_k : new_v) + 8 * (lane % (D / 8)));
   }
 
   float m_own[NSET], l_own[NSET], acc[G][PPL][8];
@@ -644,6 +640,21 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
     } else {
       a.ws_out[(orow * a.max_parts + part) * D + d] = val;
       if (d == 0) a.ws_lse[orow * a.max_parts + part] = lse2;
+    }
+  }
+
+  // APP: the new token's K/V rows of this head into its slot, and (head 0)
+  // the new position's table entry and the length
+  if constexpr (APP) {
+    if (app_copy) {
+      const int c = lane % (D / 8);
+      const int64_t dst = (int64_t)app_blk * bstride + (app_slot & Bmask) * row_elems + g * D + 8 * c;
+      T* cache = const_cast<T*>(lane < D / 8 ? kcache : vcache);
+      *reinterpret_cast<uint4*>(cache + dst) = app_piece;
+      if (g == 0 && lane == 0) {
+        if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
+        a.wr_lens[s] = app_pos + 1;
+      }
     }
   }
 }
