@@ -149,11 +149,9 @@ constexpr int kAppendRows = 256;
 struct AppendRows {
   int64_t slots[kAppendRows];
   int32_t pos[kAppendRows];
-  int32_t row0;
-  int32_t n;
 };
 struct NoAppend {
-  int32_t row0;
+  int32_t unused;
 };
 template <bool APP>
 using RowsOf = typename std::conditional<APP, AppendRows, NoAppend>::type;
@@ -173,7 +171,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   __shared__ float s_m[kWaves][G];
 
   static_assert(!(APP && F8), "appending decode takes bf16 caches");
-  const int part = blockIdx.x, g = blockIdx.y, s = APP ? rows.row0 + (int)blockIdx.z : (int)blockIdx.z;
+  // (an appending launch of rows r0 .. r0 + n - 1 gets every per-sequence
+  // array offset by r0 on the host, so that no address waits for a load)
+  const int part = blockIdx.x, g = blockIdx.y, s = (int)blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (SGPR) so that the tile loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,11 +204,12 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   const int app_j = app ? app_pos >> lgB : -1;
   const int app_blk = app ? (int)(app_slot >> lgB) : 0;
   // table entry j as the kernel sees it (APP: the new position's entry from
-  // the arguments)
-  auto entry = [&](int j) __attribute__((always_inline)) {
-    const int b = bt_row[j];
+  // the arguments).  Prefetched entries are loaded as they stand and fixed
+  // where they are used, so that their loads never wait for the position.
+  auto fix_entry = [&](int j, int b) __attribute__((always_inline)) {
     return APP && j == app_j ? app_blk : b;
   };
+  auto entry = [&](int j) __attribute__((always_inline)) { return fix_entry(j, bt_row[j]); };
 
   // Independent loads first: the length, the queries and (B < 16) the first
   // chunk's table entries, so that their latencies overlap.
@@ -246,10 +247,10 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf) {
         const int i = (tw + k * kWaves * kTile + hf * kHalf) >> lgB;
-        pre[k][hf] = entry(i < wmax ? i : wmax);
+        pre[k][hf] = bt_row[i < wmax ? i : wmax];
       }
     const int is = start >> lgB;
-    pre_start = entry(is < wmax ? is : wmax);
+    pre_start = bt_row[is < wmax ? is : wmax];
   }
 
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
@@ -312,7 +313,8 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
         for (int hf = 0; hf < NH; ++hf) {
           const int th = t0 + hf * kHalf;
           const int tc = th < c1 ? th : c0;          // wave-uniform
-          int blk = __builtin_amdgcn_readfirstlane(fetched ? (th < c1 ? pf[hf] : pre_start) : entry(tc >> lgB));
+          int blk = __builtin_amdgcn_readfirstlane(fetched ? fix_entry(tc >> lgB, th < c1 ? pf[hf] : pre_start)
+                                                           : entry(tc >> lgB));
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
           const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
           kb[hf] = kcache + base;
@@ -718,18 +720,34 @@ template <int D, int G>
 int launch_g_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, hipStream_t st) {
   const bool big = a.log2_block_size >= 4;
   for (int32_t r0 = 0; r0 < a.num_seqs; r0 += kAppendRows) {
+    const int32_t n = a.num_seqs - r0 < kAppendRows ? a.num_seqs - r0 : kAppendRows;
     AppendRows rows{};
-    rows.row0 = r0;
-    rows.n = a.num_seqs - r0 < kAppendRows ? a.num_seqs - r0 : kAppendRows;
-    for (int32_t i = 0; i < rows.n; ++i) {
+    for (int32_t i = 0; i < n; ++i) {
       rows.slots[i] = slots[r0 + i];
       rows.pos[i] = positions[r0 + i];
     }
-    const dim3 grid(a.max_parts, a.num_kv_heads, rows.n);
+    // rows r0 .. r0 + n - 1 are rows 0 .. n - 1 of this launch
+    DecodeArgs b = a;
+    const int64_t hq = a.num_q_heads;
+    b.num_seqs = n;
+    b.out = static_cast<uint16_t*>(a.out) + r0 * hq * D;
+    if (a.lse) b.lse = a.lse + r0 * hq;
+    b.q = static_cast<const uint16_t*>(a.q) + r0 * hq * D;
+    b.block_tables = a.block_tables + (int64_t)r0 * a.bt_stride;
+    b.seq_lens = a.seq_lens + r0;
+    if (a.ws_out) {
+      b.ws_out = a.ws_out + r0 * hq * a.max_parts * D;
+      b.ws_lse = a.ws_lse + r0 * hq * a.max_parts;
+    }
+    b.new_key = static_cast<const uint16_t*>(a.new_key) + r0 * a.new_key_stride;
+    b.new_value = static_cast<const uint16_t*>(a.new_value) + r0 * a.new_value_stride;
+    b.wr_tables = a.wr_tables + (int64_t)r0 * a.bt_stride;
+    b.wr_lens = a.wr_lens + r0;
+    const dim3 grid(a.max_parts, a.num_kv_heads, n);
     if (big)
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(256), 0, st, a, rows);
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(256), 0, st, b, rows);
     else
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false, true>), grid, dim3(256), 0, st, a, rows);
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false, true>), grid, dim3(256), 0, st, b, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
