@@ -25,6 +25,9 @@
 //     converted to bf16 on their way into LDS.
 //   * Each wave stages 16 keys of the tile.  With B >= 16 they lie in one
 //     block: the block id is a scalar load and the row base a scalar address.
+//     With B < 16 every key has its own block; when a cache's whole byte
+//     span fits in 32 bits the lanes' offsets are 32-bit (SMALL), so the
+//     loads take a scalar base and a 32-bit lane offset there too.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
 //     so the softmax max and sum are in-lane (plus one exchange between the
 //     two lane halves).
@@ -99,7 +102,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int D, int HW, bool CAUSAL, bool BIG, bool F8>
+template <int D, int HW, bool CAUSAL, bool BIG, bool F8, bool SMALL>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
@@ -293,8 +296,17 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   auto key_off = [&](int tile, int j) __attribute__((always_inline)) {
     int p = tile * kKeys + 16 * wave + KPI * j + kr0;
     p = p < kv_end ? p : 0;
-    return ((int64_t)clamp_blk(ent[j]) * bstride + (int64_t)(p & Bmask) * row_elems) * (F8 ? 1 : 2) + voff0[j];
+    if constexpr (SMALL) {
+      // every byte offset of the cache fits in 32 bits (checked on the host)
+      uint32_t off = (uint32_t)clamp_blk(ent[j]) * (uint32_t)(bstride * (F8 ? 1 : 2)) +
+                     (uint32_t)(p & Bmask) * (uint32_t)(row_elems * (F8 ? 1 : 2)) + voff0[j];
+      asm("" : "+v"(off));
+      return off;
+    } else {
+      return ((int64_t)clamp_blk(ent[j]) * bstride + (int64_t)(p & Bmask) * row_elems) * (F8 ? 1 : 2) + voff0[j];
+    }
   };
+  using KeyOff = decltype(key_off(0, 0));
   const char* kcb = static_cast<const char*>(a.key_cache);
   const char* vcb = static_cast<const char*>(a.value_cache);
   // bf16, B >= 16: the wave's rows of one tile of `cache` into LDS tile dst
@@ -313,7 +325,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int64_t off = key_off(tile, j);
+        const KeyOff off = key_off(tile, j);
         load_to_lds16(kcb + off, kd + (16 * wave + KPI * j) * D);
         load_to_lds16(vcb + off, vd + (16 * wave + KPI * j) * D);
       }
@@ -332,7 +344,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int64_t off = key_off(tile, j);
+        const KeyOff off = key_off(tile, j);
         kr[j] = *reinterpret_cast<const u32x4_t*>(kcb + off);
         vr[j] = *reinterpret_cast<const u32x4_t*>(vcb + off);
       }
@@ -588,7 +600,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
       // keeps the wave's row base, B < 16 the lanes' offsets (and `ent`
       // holds the table entries of the tile whose K is loaded next).
       struct KeyOffs {
-        int64_t off[NI];
+        KeyOff off[NI];
       };
       using Addr = typename std::conditional<BIG, Rows, KeyOffs>::type;
       auto tile_addr = [&](int tile) __attribute__((always_inline)) {
@@ -698,6 +710,20 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   }
 }
 
+template <int D, int HW, bool CAUSAL, bool BIG, bool F8>
+void launch_one(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (!BIG) {
+    // B < 16: 32-bit key offsets when every byte offset of a cache fits
+    // (num_blocks block strides; ids are clamped into [0, num_blocks))
+    const int64_t span = (int64_t)a.num_blocks * a.cache_block_stride * (F8 ? 1 : 2);
+    if (span <= 0xffffffffLL) {
+      hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, true>), grid, dim3(256), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, false>), grid, dim3(256), 0, st, a);
+}
+
 template <int D, int HW>
 int launch_hw(const PrefillArgs& a, hipStream_t st) {
   const int span = kQ * (4 / HW);
@@ -709,21 +735,21 @@ int launch_hw(const PrefillArgs& a, hipStream_t st) {
   const bool big = a.log2_block_size >= 4;
   if (a.fp8) {
     if (a.causal && big)
-      hipLaunchKernelGGL((prefill_kernel<D, HW, true, true, true>), grid, dim3(256), 0, st, a);
+      launch_one<D, HW, true, true, true>(a, grid, st);
     else if (a.causal)
-      hipLaunchKernelGGL((prefill_kernel<D, HW, true, false, true>), grid, dim3(256), 0, st, a);
+      launch_one<D, HW, true, false, true>(a, grid, st);
     else if (big)
-      hipLaunchKernelGGL((prefill_kernel<D, HW, false, true, true>), grid, dim3(256), 0, st, a);
+      launch_one<D, HW, false, true, true>(a, grid, st);
     else
-      hipLaunchKernelGGL((prefill_kernel<D, HW, false, false, true>), grid, dim3(256), 0, st, a);
+      launch_one<D, HW, false, false, true>(a, grid, st);
   } else if (a.causal && big)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, true, true, false>), grid, dim3(256), 0, st, a);
+    launch_one<D, HW, true, true, false>(a, grid, st);
   else if (a.causal)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, true, false, false>), grid, dim3(256), 0, st, a);
+    launch_one<D, HW, true, false, false>(a, grid, st);
   else if (big)
-    hipLaunchKernelGGL((prefill_kernel<D, HW, false, true, false>), grid, dim3(256), 0, st, a);
+    launch_one<D, HW, false, true, false>(a, grid, st);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, HW, false, false, false>), grid, dim3(256), 0, st, a);
+    launch_one<D, HW, false, false, false>(a, grid, st);
   return (int)hipGetLastError();
 }
 

@@ -92,6 +92,28 @@ def test_prefill_placement_and_block_size_do_not_change_a_bit():
         assert torch.equal(out, outs[0])
 
 
+def test_prefill_per_key_offsets_past_4gib():
+    """B = 1 keeps 32-bit per-key offsets when a cache's byte span fits in 32
+    bits and 64-bit ones otherwise: the same requests over a small pool and
+    over one of 2.2 M blocks (4.5 GiB per cache, blocks scattered over it)
+    give identical bits, and the small pool matches the oracle."""
+    ctx = [300, 1000, 0]
+    q = [64, 33, 70]
+    lens = [c + n for c, n in zip(ctx, q)]
+    outs = []
+    for extra in (3, 2_200_000):
+        wl = workloads.custom("prefill_span", 57, 32, 8, 128, 1, lens, q_lens=q, extra_blocks=extra)
+        print(f"[prefill] B=1 pool of {wl.num_blocks} blocks", flush=True)
+        if extra == 3:
+            run_parity(wl)
+        h = HipStep(wl)
+        seqs = list(range(wl.num_seqs))
+        outs.append(h.prefill(q_rows(wl, seqs), seqs).cpu())
+        del h
+        torch.cuda.empty_cache()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_chunked_matches_one_shot():
     """Chunks of 256 + 256 queries over one 512-token sequence match one chunk
     of 512 (each chunk attends to everything written before it)."""
