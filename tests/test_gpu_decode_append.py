@@ -174,10 +174,12 @@ def test_fused_decode_append_rejects_bad_positions():
 
 
 def test_fused_decode_append_over_more_than_one_launch_of_rows():
-    """300 sequences (two launches of rows, 256 + 44): the same bits as the
-    separate write and decode, and the oracle's attention."""
+    """300 sequences (two launches of rows, 256 + 44, the second seeing its
+    rows' arrays from row 256 on), split into partitions of 64 tokens: the
+    same bits (outputs, lse, tables, lengths) as the separate write and
+    decode, and the oracle's attention."""
     rng = np.random.default_rng(31)
-    lens = rng.integers(1, 60, size=300).tolist()
+    lens = rng.integers(1, 200, size=300).tolist()
     wl = workloads.custom("fused_300", 81, 8, 2, 64, 16, lens, q_lens=[0] * 300, extra_blocks=400)
     print("[fused append] 300 rows", flush=True)
     S = wl.num_seqs
@@ -201,12 +203,16 @@ def test_fused_decode_append_over_more_than_one_launch_of_rows():
     q = workloads.normal_bf16(rng, (S, wl.num_q_heads, wl.head_dim))
     kd, vd, qd = to_device(k), to_device(v), to_device(q)
     o1, o2 = torch.empty_like(qd), torch.empty_like(qd)
+    lse1 = torch.empty((S, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    lse2 = torch.empty_like(lse1)
     B.pa_decode_append(kd, vd, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, slots, pos)
-    B.pa_paged_decode(o1, qd, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, msl, wl.scale, partition_size=64)
+    B.pa_paged_decode(o1, qd, h1.kc, h1.vc, h1.table_dev, h1.seq_lens_dev, msl, wl.scale, partition_size=64,
+                      lse=lse1)
     B.pa_paged_decode_append(o2, qd, h2.kc, h2.vc, h2.table_dev, h2.seq_lens_dev, msl, wl.scale, kd, vd, slots, pos,
-                             partition_size=64)
+                             partition_size=64, lse=lse2)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse1, lse2)
     assert torch.equal(h1.table_dev, h2.table_dev) and torch.equal(h1.seq_lens_dev, h2.seq_lens_dev)
     o_table = o.table.astype(np.int64).copy()
     o_lens = o.seq_lens.astype(np.int64).copy()
