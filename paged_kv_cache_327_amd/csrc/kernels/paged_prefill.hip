@@ -40,6 +40,11 @@
 //   * The next key tile's K/V loads are in flight while the current tile is
 //     computed (double-buffered LDS, one barrier per tile); block-table
 //     entries are fetched one further tile ahead.
+//   * bf16 caches: the leading tiles that no query of the work-group masks
+//     are software-pipelined (the QK^T MFMAs of tile t + 1 issued between
+//     the exponentials of tile t, the PV MFMAs of tile t beside the maximum
+//     of tile t + 1), with K loaded one tile ahead of V; the masked tiles at
+//     the diagonal take the plain steps.
 #include <type_traits>
 
 #include "../internal.hpp"
