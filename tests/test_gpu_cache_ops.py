@@ -137,3 +137,22 @@ def test_slot_mapping_edge_cases_match_oracle():
     want = cache_ops.slot_mapping(bt, qsl, lens, Bs, T)
     assert np.array_equal(got, want)
     assert (got == -1).any() and (got >= 0).any()
+
+
+def test_slot_mapping_with_more_requests_than_staged():
+    """2,500 requests (more query_start_loc entries than a work-group stages
+    in LDS, so the search reads global memory), some empty: equal to the
+    oracle."""
+    rng = np.random.default_rng(6)
+    S, W, Bs = 2500, 4, 16
+    bt = rng.integers(0, 10000, size=(S, W)).astype(np.int32)
+    q = rng.integers(0, 4, size=S)
+    qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    lens = rng.integers(0, W * Bs, size=S).astype(np.int32)
+    T = int(qsl[-1]) + 3
+    got = B.pa_slot_mapping(torch.from_numpy(bt).cuda(), torch.from_numpy(qsl).cuda(),
+                            torch.from_numpy(lens).cuda(), Bs, T).cpu().numpy()
+    want = cache_ops.slot_mapping(bt, qsl, lens, Bs, T)
+    assert np.array_equal(got, want)
+    assert (got >= 0).sum() > 1000
+
