@@ -68,21 +68,23 @@ int launch_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_byte
                        int64_t stride_bytes, const int32_t* pairs, int32_t n_pairs,
                        void* stream);
 
+// The fields the decode prologue's first loads need come first, so that the
+// kernel reads them with its first argument loads.
 struct DecodeArgs {
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const void* q;
+  int32_t bt_stride;
+  int32_t log2_block_size;
+  int32_t max_seq_len;
+  int32_t partition_size;  // > 0, multiple of 64 and of the block size
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
   void* out;
   float* lse;
-  const void* q;
   const void* key_cache;
   const void* value_cache;
   int64_t cache_block_stride;
   int32_t num_blocks;
-  const int32_t* block_tables;
-  int32_t bt_stride;
-  const int32_t* seq_lens;
-  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
-  int32_t log2_block_size;
-  int32_t max_seq_len;
-  int32_t partition_size;  // > 0, multiple of 64 and of the block size
   int32_t max_parts;
   float scale;     // softmax scale (times k_scale for E4M3 caches)
   float v_scale;   // 1 for bf16 caches
