@@ -313,3 +313,13 @@ def pool_ops_cached(seed: int, n_ops: int = 200, max_seqs: int = 10, max_append:
     for t in transfers:
         ops.append(("unpin", t))
     return ops
+
+
+def device_rows(seed: int, tag: int, shape, device="cuda"):
+    """bf16 device tensor of `shape` drawn N(0, 1) by a torch generator seeded
+    per (seed, tag): step inputs (new K/V rows, queries) of the large
+    workloads.  A check copies the tensor back; it never redraws it."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 2_000_003 + tag * 613 + 17) % (2**63 - 1))
+    return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)

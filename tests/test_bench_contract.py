@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused():
 @pytest.mark.timeout(300)
 def test_short_run_prints_one_complete_json_line():
     print("[bench] short run: 3 steps, no extra workloads", flush=True)
-    r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "1", "--kernel-reps", "8",
+    r = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "1", "--kernel-reps", "1",
                         "--no-configs", "--no-prefill", "--no-cpu-baseline"],
                        capture_output=True, text=True, timeout=280)
     assert r.returncode == 0, r.stderr[-2000:]
@@ -37,7 +37,7 @@ def test_short_run_prints_one_complete_json_line():
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["unit"] == "GB/s"
     assert d["higher_is_better"] is True and d["scaling"] in ("weak", "strong")
-    assert d["config"]["workload"] == "llama3_8b_decode"
+    assert d["config"]["workload"] == "long_context_decode" and d["config"]["layers"] == 32
     roof = d["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key

@@ -119,33 +119,6 @@ def test_mixed_step_decode_sampled(block_size):
     check_sampled(h, q, out, lse, rows, sample, what=wl.name)
 
 
-def test_long_context_32_layer_pool():
-    """Long-context decode over the 32-layer pool (26,785 blocks of 16
-    tokens per layer, 52.3 GiB of K/V, layer-major [layer][K|V][block]):
-    8 sequences of U{16384..32768} tokens, partitions of 512 tokens and the
-    log-sum-exp merge.  Every layer is decoded; the oracle checks all 8
-    sequences of layers 0 and 31 and one sequence of layer 13."""
-    wl = workloads.long_context()
-    print(f"[decode] {wl.name}: 32-layer pool", flush=True)
-    L = wl.num_layers
-    kv = torch.full((L, 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), float("nan"),
-                    dtype=torch.bfloat16, device="cuda")
-    layers = [(l, kv[l, 0], kv[l, 1]) for l in range(L)]
-    h = HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]), layers=layers)
-    rows = list(range(wl.num_seqs))
-    for l in range(L):
-        q = workloads.query_bits(wl.seed, wl.num_seqs, wl.num_q_heads, wl.head_dim, layer=l)
-        out, lse = h.decode(q, partition_size=512, caches=(kv[l, 0], kv[l, 1]))
-        if l in (0, 31):
-            check_sampled(h, q, out, lse, rows, rows, layer=l, what=f"layer {l}")
-        elif l == 13:
-            check_sampled(h, q, out, lse, rows, [5], layer=l, what=f"layer {l}")
-        else:
-            assert torch.isfinite(out.float()).all()
-    del kv, layers, h
-    torch.cuda.empty_cache()
-
-
 def test_split_workspace_reuse_is_deterministic():
     """A split-K call reused with the same workspace, call after call, gives
     the same complete result each time (the partials are rewritten, nothing
