@@ -412,6 +412,28 @@ int pa_paged_decode(void* out, float* lse, const void* q,
                     int32_t partition_size, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_paged_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and result, without the workspace.  The split-K partials
+ * go to a scratch array of PA_STATIC_SCRATCH_BYTES (64 MiB) that the library
+ * keeps in device memory; every GPU the library runs on holds its own copy
+ * until the process ends.  The call itself allocates nothing.  All calls on
+ * one GPU share that GPU's scratch: calls that overlap in time on one GPU
+ * (different streams, no ordering between them) race; calls ordered on one
+ * stream do not.  Nothing carries over between calls (each call writes every
+ * partial it reads), so the scratch needs no clearing.
+ * Errors as pa_paged_decode, plus PA_ERR_INVALID when the call needs more
+ * partials than the scratch holds (pa_paged_decode_workspace_size above
+ * PA_STATIC_SCRATCH_BYTES); nothing is launched then. */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_paged_decode_noalloc(void* out, float* lse, const void* q,
+                            const void* key_cache, const void* value_cache,
+                            int64_t cache_block_stride, int32_t num_blocks,
+                            const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                            int32_t partition_size, float scale, void* stream);
+
 /* pa_decode_append followed by pa_paged_decode, in one launch per 256
  * sequences: row s's new token (K/V rows = row s of key/value, slot
  * slots[s], position positions[s]) is written to the cache, block_tables[s]

@@ -79,6 +79,8 @@ _SIGS = {
     "pa_paged_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_paged_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_sz, c_vp]),
+    "pa_paged_decode_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
+                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp]),
     "pa_paged_decode_append": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
                                        c_vp, c_i64, c_vp, c_i64, P_i64, P_i32, c_vp, c_sz, c_vp]),
@@ -468,6 +470,14 @@ def pa_paged_decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_
             workspace, stream, False, 1.0, 1.0)
 
 
+def pa_paged_decode_noalloc(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale,
+                            partition_size=512, lse=None, stream=None):
+    """pa_paged_decode with the split-K partials in the library's static
+    device scratch (no workspace; nothing is allocated)."""
+    _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
+            None, stream, False, 1.0, 1.0, noalloc=True)
+
+
 def pa_paged_decode_fp8(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale,
                         k_scale=1.0, v_scale=1.0, partition_size=512, lse=None, workspace=None, stream=None):
     """pa_paged_decode over E4M3 caches (uint8 or float8_e4m3fn) with
@@ -496,7 +506,7 @@ def pa_paged_decode_append(out, q, key_cache, value_cache, block_tables, seq_len
 
 
 def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len, scale, partition_size, lse,
-            workspace, stream, fp8, k_scale, v_scale, append=None):
+            workspace, stream, fp8, k_scale, v_scale, append=None, noalloc=False):
     import torch
     nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache, fp8)
     _bf16(q, "q")
@@ -511,14 +521,17 @@ def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len,
         raise InvalidArgument(PA_ERR_INVALID, "seq_lens must be contiguous int32 [S]")
     if lse is not None and (lse.dtype != torch.float32 or lse.shape != (S, hq) or not lse.is_contiguous()):
         raise InvalidArgument(PA_ERR_INVALID, "lse must be contiguous fp32 [S, Hq]")
+    args = (out.data_ptr(), lse.data_ptr() if lse is not None else None, q.data_ptr(), key_cache.data_ptr(),
+            value_cache.data_ptr(), bstride, nb, block_tables.data_ptr(), block_tables.stride(0),
+            seq_lens.data_ptr(), S, hq, hkv, d, bs, max_seq_len, partition_size, scale)
+    if noalloc:
+        _check(lib().pa_paged_decode_noalloc(*args, _stream(q, stream)))
+        return
     need = pa_paged_decode_workspace_size(S, hq, d, max_seq_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    args = (out.data_ptr(), lse.data_ptr() if lse is not None else None, q.data_ptr(), key_cache.data_ptr(),
-            value_cache.data_ptr(), bstride, nb, block_tables.data_ptr(), block_tables.stride(0),
-            seq_lens.data_ptr(), S, hq, hkv, d, bs, max_seq_len, partition_size, scale)
     if append is not None:
         k, v, sl, pos = append
         _check(lib().pa_paged_decode_append(*args, k.data_ptr(), k.stride(0), v.data_ptr(), v.stride(0), _i64p(sl),

@@ -332,6 +332,31 @@ int pa_paged_decode(void* out, float* lse, const void* q, const void* key_cache,
                      max_seq_len, partition_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
 }
 
+int pa_paged_decode_noalloc(void* out, float* lse, const void* q, const void* key_cache, const void* value_cache,
+                            int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
+                            int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                            int32_t partition_size, float scale, void* stream) {
+  static_assert(pa::kStaticScratchBytes == PA_STATIC_SCRATCH_BYTES, "scratch size differs from the header's");
+  const char* fn = "paged_decode_noalloc";
+  pa::clear_error();
+  const size_t need = num_seqs > 0 && partition_size > 0
+                          ? pa_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len,
+                                                           partition_size)
+                          : 0;
+  if (need > pa::kStaticScratchBytes)
+    return pa::fail(PA_ERR_INVALID,
+                    "%s: the call needs %zu bytes of split-K partials, more than the %zu-byte static scratch "
+                    "(use a larger partition_size, or pa_paged_decode with a workspace)",
+                    fn, need, pa::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0)
+    if (int e = pa::static_decode_scratch(&ws)) return hip_status(fn, e);
+  return decode_impl(fn, out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks, block_tables, bt_stride,
+                     seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len, partition_size,
+                     scale, false, 1.f, 1.f, ws, need > 0 ? pa::kStaticScratchBytes : 0, stream);
+}
+
 int pa_paged_decode_append(void* out, float* lse, const void* q, void* key_cache, void* value_cache,
                            int64_t cache_block_stride, int32_t num_blocks, int32_t* block_tables, int32_t bt_stride,
                            int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

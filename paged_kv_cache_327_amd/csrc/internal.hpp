@@ -101,6 +101,10 @@ struct DecodeArgs {
   int32_t* wr_lens;
 };
 int launch_paged_decode(const DecodeArgs& a, void* stream);
+// The allocation-free entry point's scratch: its device address on the
+// current GPU (looked up once per device), kStaticScratchBytes long.
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+int static_decode_scratch(void** ptr);
 // slots, positions: host arrays of num_seqs entries (kernel arguments)
 int launch_paged_decode_append(const DecodeArgs& a, const int64_t* slots, const int32_t* positions, void* stream);
 

@@ -43,6 +43,7 @@
 //    sequence with one partition writes its bf16 output directly; otherwise
 //    partials (normalised output, log2 lse) go to the workspace for the merge
 //    pass.
+#include <mutex>
 #include <type_traits>
 
 #include "../internal.hpp"
@@ -785,6 +786,33 @@ int launch_d_append(const DecodeArgs& a, const int64_t* slots, const int32_t* po
 }
 
 }  // namespace
+
+// Split-K scratch of the allocation-free decode entry point: a file-scope
+// device array (each GPU the library runs on holds its own copy until the
+// process ends).  In host code `scratch` only stands for the symbol; its
+// device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+int static_decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return 0;
+}
 
 int launch_paged_decode(const DecodeArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
