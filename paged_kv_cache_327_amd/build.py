@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -36,16 +37,94 @@ def sources():
             sorted(glob.glob(os.path.join(CSRC, "kernels", "*.hip"))))
 
 
+# Resource budgets the kernels' designs rest on, checked on every build from
+# the compiler's resource-usage remarks (a compiler that places registers
+# differently -- e.g. without the VGPR-form MFMA option above -- fails the
+# build instead of silently changing occupancy or spilling):
+#   kernel, template-argument predicate -> (max arch VGPRs, max AGPRs,
+#   max scratch bytes per lane, min waves per SIMD)
+# * prefill, head_dim 128: 256 VGPRs, no AGPRs, two waves per SIMD; only the
+#   bf16 B < 16 variant with 64-bit key offsets spills 12 bytes per lane
+#   (around its step loop).
+# * prefill, head_dim 64: two waves per SIMD, no scratch.
+# * decode partition pass, up to 4 query heads per KV head: two waves per
+#   SIMD, no scratch; 5-8 heads: one wave per SIMD, no scratch.
+# * every other kernel: no scratch.
+def _budget(name, targs):
+    if name == "prefill_kernel":
+        d, causal_, big, f8, small = targs[0], targs[2], targs[3], targs[4], targs[5]
+        if d == 128:
+            spill = 12 if (not big and not f8 and not small) else 0
+            return 256, 0, spill, 2
+        return 256, 0, 0, 2
+    if name == "decode_partition_kernel":
+        return (512, 256, 0, 2) if targs[1] <= 4 else (512, 256, 0, 1)
+    return 512, 256, 0, 1
+
+
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]):\s*(\S+)")
+
+
+def kernel_name(mangled):
+    """(unqualified name, integer/bool template arguments) of a mangled
+    kernel name such as _ZN2pa12_GLOBAL__N_114prefill_kernelILi128ELb1E...E."""
+    i = mangled.find("_ZN")
+    name, pos = "", i + 3
+    while 0 <= i and pos < len(mangled) and mangled[pos].isdigit():
+        j = pos
+        while mangled[j].isdigit():
+            j += 1
+        n = int(mangled[pos:j])
+        name, pos = mangled[j:j + n], j + n
+    targs = []
+    if mangled[pos:pos + 1] == "I":
+        for m in re.finditer(r"L[ib](\d+)E", mangled[pos + 1:]):
+            if m.start() != 0 and not mangled[pos + 1:][:m.start()].endswith("E"):
+                break
+            targs.append(int(m.group(1)))
+    return name, targs
+
+
+def resource_usage(text):
+    """[(kernel name, template args, {field: value})] from the compiler's
+    kernel-resource-usage remarks."""
+    out = []
+    for m in _REMARK.finditer(text):
+        field, val = m.group(1), m.group(2)
+        if field == "Function Name":
+            name, targs = kernel_name(val)
+            out.append((name, targs, {"mangled": val}))
+        elif out:
+            out[-1][2][field.split(" ")[0]] = int(val)
+    return out
+
+
+def check_budgets(usage):
+    bad = []
+    for name, targs, r in usage:
+        vg, ag, scratch, occ = _budget(name, targs)
+        if r.get("VGPRs", 0) > vg or r.get("AGPRs", 0) > ag or r.get("ScratchSize", 0) > scratch \
+                or r.get("Occupancy", 99) < occ:
+            bad.append(f"{name}<{', '.join(map(str, targs))}>: {r} exceeds budget "
+                       f"(VGPRs <= {vg}, AGPRs <= {ag}, scratch <= {scratch}, waves/SIMD >= {occ})")
+    if bad:
+        raise RuntimeError("kernel resource budgets exceeded:\n" + "\n".join(bad))
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in line)
+    text = r.stdout + r.stderr
+    err = "\n".join(line for line in text.splitlines()
+                    if "packed-fp32-ops" not in line and "remark" not in line and "|" not in line
+                    and not line.strip().startswith("^") and line.strip())
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err)
+    return text
 
 
 def build(verbose: bool = False) -> str:
@@ -60,10 +139,15 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in hip:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        list(ex.map(lambda c: _run(c, verbose), jobs))
+        texts = list(ex.map(lambda c: _run(c, verbose), jobs))
+    usage = [u for t in texts for u in resource_usage(t)]
+    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+        for name, targs, r in usage:
+            f.write(f"{name}<{', '.join(map(str, targs))}> {r}\n")
+    check_budgets(usage)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
