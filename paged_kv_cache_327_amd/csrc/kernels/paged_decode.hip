@@ -664,6 +664,12 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
 
 // out[s, h] = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M) over the
 // sequence's partitions (log-sum-exp identity); lse = (M + log2 W) ln 2.
+// One wave per (sequence, query head): lane p holds partition p's log2 lse
+// (64 partitions per pass), the wave takes their maximum, and the partial
+// outputs are loaded kMergeBatch partitions at a time before any is summed,
+// so a merge costs a few round trips to memory instead of one per partition.
+// The sums run in partition order.
+constexpr int kMergeBatch = 16;
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
@@ -675,18 +681,36 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
   const float* lse2 = a.ws_lse + row * a.max_parts;
   const float* po = a.ws_out + row * a.max_parts * D;
   float M = kNegInf;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, lse2[p]);
+  for (int p0 = 0; p0 < nparts; p0 += 64) M = fmaxf(M, p0 + lane < nparts ? lse2[p0 + lane] : kNegInf);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float W = 0.f, o[D / 64];
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = fast_exp2(lse2[p] - M);
-    W += w;
+  for (int k = 0; k < D / 64; ++k) o[k] = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int n = nparts - p0 < 64 ? nparts - p0 : 64;
+    const float w = lane < n ? fast_exp2(lse2[p0 + lane] - M) : 0.f;
+    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+      float v[kMergeBatch][D / 64];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] += w * po[p * D + lane + 64 * i];
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int i = i0 + j < n ? i0 + j : n - 1;     // a valid partial; its weight is not used
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) v[j][k] = po[(int64_t)(p0 + i) * D + lane + 64 * k];
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        if (i0 + j < n) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i0 + j));
+          W += wj;
+#pragma unroll
+          for (int k = 0; k < D / 64; ++k) o[k] += wj * v[j][k];
+        }
+      }
+    }
   }
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i) static_cast<uint16_t*>(a.out)[row * D + lane + 64 * i] = to_bf16(o[i] / W);
+  for (int k = 0; k < D / 64; ++k) static_cast<uint16_t*>(a.out)[row * D + lane + 64 * k] = to_bf16(o[k] / W);
   if (a.lse && lane == 0) a.lse[row] = (M + fast_log2(W)) * kLn2;
 }
 
