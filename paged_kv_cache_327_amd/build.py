@@ -47,8 +47,8 @@ def sources():
 #   bf16 B < 16 variant with 64-bit key offsets spills 12 bytes per lane
 #   (around its step loop).
 # * prefill, head_dim 64: two waves per SIMD, no scratch.
-# * decode partition pass, up to 4 query heads per KV head: two waves per
-#   SIMD, no scratch; 5-8 heads: one wave per SIMD, no scratch.
+# * decode partition pass: no AGPRs and no scratch; three waves per SIMD up
+#   to 4 query heads per KV head, two for 5-8.
 # * every other kernel: no scratch.
 def _budget(name, targs):
     if name == "prefill_kernel":
@@ -58,7 +58,7 @@ def _budget(name, targs):
             return 256, 0, spill, 2
         return 256, 0, 0, 2
     if name == "decode_partition_kernel":
-        return (512, 256, 0, 2) if targs[1] <= 4 else (512, 256, 0, 1)
+        return (512, 0, 0, 3) if targs[1] <= 4 else (512, 0, 0, 2)
     return 512, 256, 0, 1
 
 

@@ -43,6 +43,8 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppBcast0 = 0x00;      // quad_perm [0, 0, 0, 0]
 constexpr int kDppBcast2 = 0xAA;      // quad_perm [2, 2, 2, 2]
 constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15 - i
+constexpr int kDppRowBcast0 = 0x150;  // + n: lane n of each 16-lane row to the whole row
 constexpr int kDppRor8 = 0x128;
 
 template <int CTRL>

@@ -10,39 +10,40 @@
 // below is ours.
 //
 // Partition pass: one work-group (4 waves) per (partition, KV head g, seq s).
-//  * Lanes form groups of 8.  A group owns one token at a time; its 8 lanes
-//    split head_dim into 16-byte pieces (lane i holds d = 8i..8i+7 and, for
-//    D = 128, d = 64+8i..64+8i+7), so every K/V row load is a coalesced
-//    16-byte-per-lane access of the token's contiguous row.  A wave handles
-//    16-token tiles (2 tokens per group) and keeps the next tile's loads in
-//    flight while it computes the current one.
-//  * E4M3 caches (one byte per element): lane i holds d = (D/8) i ..
-//    (D/8) i + D/8 - 1 of a token in one 16- (or 8-) byte load; the codes
-//    become bf16 pairs exactly (v_cvt_scalef32_pk_bf16_fp8 at scale 1) and
-//    the rest is the bf16 path; k_scale is folded into the logit scale and
-//    v_scale into the output.
+//  * A token's K (or V) row of head g is held by D / 8 lanes, 8 elements
+//    each (one 16-byte piece of bf16, or 8 one-byte E4M3 codes), so every
+//    row load is a coalesced access of the row's contiguous bytes.  With
+//    D = 128 a wave's four 16-lane rows hold 4 consecutive tokens per load
+//    instruction, with D = 64 its eight 8-lane groups hold 8.  A wave works
+//    on 16-token tiles and keeps the next tile's loads in flight while it
+//    computes the current one.  Eight elements per lane keep a lane's
+//    queries (G x 4 registers) and accumulators (G x 8) small enough for
+//    three waves per SIMD at D = 128 and G = 4.
+//  * E4M3 caches: the codes become bf16 pairs exactly
+//    (v_cvt_scalef32_pk_bf16_fp8 at scale 1) and the rest is the bf16 path;
+//    k_scale is folded into the logit scale and v_scale into the output.
 //  * Block lookup: with B >= 16 a tile lies inside one block, whose id is a
 //    scalar load from the table row and whose base address is scalar; with
 //    B < 16 the partition's table entries are staged in LDS and each token
 //    looks its block up there.  Ids are clamped into [0, num_blocks).
 //  * The G = Hq/Hkv query heads of KV head g all use the same K/V registers
-//    (the GQA sharing).  q.k partial sums (v_dot2_f32_bf16) are
-//    reduce-scattered over the 8 lanes of a group, so each lane finishes one
-//    (head, token) score and takes one exponential; the bf16 weights are
-//    paired per head and broadcast back to the group with DPP, and p.v runs
-//    on token pairs with v_dot2_f32_bf16 into fp32 accumulators.
+//    (the GQA sharing).  q.k partial sums (v_dot2_f32_bf16) of 4 heads x the
+//    group's tokens are reduce-scattered over the group's lanes with DPP, so
+//    each lane finishes one (head, token) score and takes one exponential;
+//    the bf16 weights are paired over tokens and broadcast back to the group
+//    with DPP, and p.v runs on token pairs with v_dot2_f32_bf16 into fp32
+//    accumulators.
 //  * Online softmax in log2 units with one running maximum per head shared by
 //    the whole wave.  It is raised only when a score exceeds it by more than
 //    8 (weights stay <= 2^8): a ballot sends the wave to a rare slow path, so
 //    the fast path has no per-lane branches and the lane groups never need
 //    rescaling against each other.
-//  * Merge: the two groups of each 16-lane row are summed with DPP, the four
-//    rows with gfx950's lane swaps (v_permlane32_swap, v_permlane16_swap),
-//    and the waves go through LDS and are combined with the log-sum-exp
-//    identity.  A
-//    sequence with one partition writes its bf16 output directly; otherwise
-//    partials (normalised output, log2 lse) go to the workspace for the merge
-//    pass.
+//  * Merge: the lane groups' sums add directly (shared maxima): the four
+//    16-lane rows in registers with gfx950's lane swaps (v_permlane32_swap,
+//    v_permlane16_swap), the waves through LDS with the log-sum-exp
+//    identity.  A sequence with one partition writes its bf16 output
+//    directly; otherwise partials (normalised output, log2 lse) go to the
+//    workspace for the merge pass.
 #include <mutex>
 #include <type_traits>
 
@@ -53,87 +54,112 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kHalf = 16;     // tokens of a half tile: two per lane group, inside one block when B >= 16
+constexpr int kHalf = 16;     // tokens of a half tile, inside one block when B >= 16
 constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
-constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1).  Two halves
-                              // (a tile's loads as large as with bf16 rows) measured 3%
-                              // faster on 16K-32K-token sequences but 8% slower on the
-                              // 600-token batch, so one half is kept
+constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1)
 constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
-// A lane's share of the K and V rows of its group's NT tokens (two per half
-// tile): D / 8 elements each, bf16 in 16-byte pieces (element e is d =
-// 64 (e / 8) + 8 li + e % 8), or E4M3 codes in one 16- or 8-byte piece
-// (element e is d = (D / 8) li + e).  Either way a group's 8 lanes read a
-// row's contiguous bytes.
-template <int D, bool F8, int NT>
-struct KV {
-  static constexpr int kPieces = D / 64;  // 16-byte bf16 pieces per lane per token
-  uint4 k[NT][kPieces];
-  uint4 v[NT][kPieces];
-};
-template <int D, int NT>
-struct KV<D, true, NT> {
-  using Piece = typename std::conditional<D == 128, uint4, uint2>::type;
-  Piece k[NT];
-  Piece v[NT];
+// Lane layout.  A token's K (or V) row of one KV head is held by LPT = D / 8
+// lanes, 8 elements each (lane li = lane % LPT holds d = 8 li .. 8 li + 7:
+// one 16-byte piece of bf16, or 8 E4M3 codes), so a lane group reads the
+// row's contiguous bytes.  The NG = 64 / LPT groups of a wave hold NG
+// consecutive tokens per load instruction; a half tile's 16 tokens take
+// TPL = 16 / NG loads, token u of group grp being t0 + grp + NG u.
+template <int D>
+struct Layout {
+  static constexpr int LPT = D / 8;
+  static constexpr int NG = 64 / LPT;
+  static constexpr int TPL = kHalf / NG;
 };
 
-// Element index e = 8 k + i of a lane -> dimension d.
-template <int D, bool F8>
-__device__ __forceinline__ int lane_dim(int k, int i, int li) {
-  return F8 ? (D / 8) * li + 8 * k + i : 64 * k + 8 * li + i;
+template <bool F8>
+using PieceOf = typename std::conditional<F8, uint2, uint4>::type;
+
+// A lane's pieces of the K and V rows of its NT tokens.
+template <bool F8, int NT>
+struct KV {
+  PieceOf<F8> k[NT];
+  PieceOf<F8> v[NT];
+};
+
+// The 8 elements of a piece as 4 packed bf16 pairs in element order (E4M3
+// codes are converted exactly).
+template <bool F8>
+__device__ __forceinline__ void bf16_words(const PieceOf<F8>& piece, uint32_t (&w)[4]) {
+  if constexpr (F8) {
+    w[0] = e4m3x2_to_bf16x2<false>(piece.x);
+    w[1] = e4m3x2_to_bf16x2<true>(piece.x);
+    w[2] = e4m3x2_to_bf16x2<false>(piece.y);
+    w[3] = e4m3x2_to_bf16x2<true>(piece.y);
+  } else {
+    w[0] = piece.x;
+    w[1] = piece.y;
+    w[2] = piece.z;
+    w[3] = piece.w;
+  }
 }
 
-// The lane's D / 8 elements of one token as D / 16 packed bf16 pairs, in
-// element order (E4M3 codes are converted exactly).
-template <int D, bool F8, typename P>
-__device__ __forceinline__ void bf16_words(const P& piece, uint32_t (&w)[D / 16]) {
-  const uint32_t* raw = reinterpret_cast<const uint32_t*>(&piece);
-  if constexpr (F8) {
+// One reduce-scatter step over lane pairs that differ in one bit of li:
+// a lane whose bit is set keeps the upper half of its values, its partner
+// the lower half, and each adds the partner's copy of the half it keeps.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_step(const float (&v)[N], float (&w)[N / 2], bool bit) {
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      w[2 * j] = e4m3x2_to_bf16x2<false>(raw[j]);
-      w[2 * j + 1] = e4m3x2_to_bf16x2<true>(raw[j]);
-    }
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = bit ? v[k] : v[k + N / 2];
+    const float keep = bit ? v[k + N / 2] : v[k];
+    w[k] = keep + dpp<CTRL>(send);
+  }
+}
+
+// Sum of LPT per-lane values over the LPT lanes of a group, scattered: lane
+// li of the group ends with the total of value li.  The partner of each step
+// flips one bit of li: the row mirror (li <-> 15 - li) bit 3, the half-row
+// mirror (li <-> li ^ 7) bit 2, then xor 2 and xor 1.
+template <int LPT>
+__device__ __forceinline__ float reduce_scatter(const float (&v)[LPT], int li) {
+  float w8[8];
+  if constexpr (LPT == 16) {
+    rs_step<kDppRowMirror>(v, w8, (li & 8) != 0);
   } else {
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) w[j] = raw[j];
+    for (int k = 0; k < 8; ++k) w8[k] = v[k];
   }
+  float w4[4], w2[2], w1[1];
+  rs_step<kDppHalfMirror>(w8, w4, (li & 4) != 0);
+  rs_step<kDppXor2>(w4, w2, (li & 2) != 0);
+  rs_step<kDppXor1>(w2, w1, (li & 1) != 0);
+  return w1[0];
 }
 
-// Sum of 8 per-lane values over the 8 lanes of a group, scattered: lane i
-// of the group ends with the total of value i.  Pairs are (i, 7 - i), then
-// (i, i ^ 2), then (i, i ^ 1); each step keeps half and adds the partner's.
-__device__ __forceinline__ float reduce_scatter8(const float (&v)[8], bool up4, bool b1, bool b0) {
-  float w[4], z[2];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float send = up4 ? v[k] : v[k + 4];
-    const float keep = up4 ? v[k + 4] : v[k];
-    w[k] = keep + dpp<kDppHalfMirror>(send);
+// Each head of a set of four holds one value per token pair in the lanes of
+// that pair (group lanes TPL h + 2 q and TPL h + 2 q + 1, q < TPL / 2); every
+// lane of the group gets all of them: out[h][q].
+template <int TPL>
+__device__ __forceinline__ void broadcast_pairs(uint32_t x, int li, uint32_t (&out)[4][TPL / 2]) {
+  if constexpr (TPL == 4) {
+    // a group is a 16-lane row: broadcast lanes 0, 2, 4, ..., 14 of the row
+    out[0][0] = dpp<kDppRowBcast0 + 0>(x);
+    out[0][1] = dpp<kDppRowBcast0 + 2>(x);
+    out[1][0] = dpp<kDppRowBcast0 + 4>(x);
+    out[1][1] = dpp<kDppRowBcast0 + 6>(x);
+    out[2][0] = dpp<kDppRowBcast0 + 8>(x);
+    out[2][1] = dpp<kDppRowBcast0 + 10>(x);
+    out[3][0] = dpp<kDppRowBcast0 + 12>(x);
+    out[3][1] = dpp<kDppRowBcast0 + 14>(x);
+  } else {
+    // a group is half a row (lanes 2h, 2h + 1 hold head h): quad broadcasts
+    // give heads 0-1 of this quad, the half-row mirror those of the other
+    const bool up4 = (li & 4) != 0;
+    const uint32_t a = dpp<kDppBcast0>(x), b = dpp<kDppBcast2>(x);
+    const uint32_t a2 = dpp<kDppHalfMirror>(a), b2 = dpp<kDppHalfMirror>(b);
+    out[0][0] = up4 ? a2 : a;
+    out[1][0] = up4 ? b2 : b;
+    out[2][0] = up4 ? a : a2;
+    out[3][0] = up4 ? b : b2;
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float send = b1 ? w[k] : w[k + 2];
-    const float keep = b1 ? w[k + 2] : w[k];
-    z[k] = keep + dpp<kDppXor2>(send);
-  }
-  const float send = b0 ? z[0] : z[1];
-  const float keep = b0 ? z[1] : z[0];
-  return keep + dpp<kDppXor1>(send);
-}
-
-// Lanes 2h and 2h+1 of a group hold value h (h = 0..3); every lane gets all four.
-__device__ __forceinline__ void broadcast4(uint32_t x, bool up4, uint32_t (&out)[4]) {
-  const uint32_t a = dpp<kDppBcast0>(x), b = dpp<kDppBcast2>(x);
-  const uint32_t a2 = dpp<kDppHalfMirror>(a), b2 = dpp<kDppHalfMirror>(b);
-  out[0] = up4 ? a2 : a;
-  out[1] = up4 ? b2 : b;
-  out[2] = up4 ? a : a2;
-  out[3] = up4 ? b : b2;
 }
 
 // Appending decode (APP): one new token per sequence of the launch, its slot
@@ -160,29 +186,32 @@ using RowsOf = typename std::conditional<APP, AppendRows, NoAppend>::type;
 template <int D, int G, bool BIG, bool F8, bool APP>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, RowsOf<APP> rows) {
   using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
-  constexpr int PPL = D / 64;   // groups of 8 elements per lane per token
-  constexpr int NW = D / 16;    // packed bf16 pairs per lane per token
+  using Lay = Layout<D>;
+  constexpr int LPT = Lay::LPT, NG = Lay::NG, TPL = Lay::TPL;
   constexpr int NH = F8 ? kHalves8 : 1;   // half tiles per tile
   constexpr int kTile = kHalf * NH;       // tokens per wave iteration
-  using KVt = KV<D, F8, 2 * NH>;
-  constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score slot per lane per set
+  using KVt = KV<F8, TPL * NH>;
+  using P = PieceOf<F8>;
+  constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score per lane per set
   __shared__ int32_t s_bt[BIG ? 1 : kChunk];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][D];
   __shared__ float s_l[kWaves][G];
   __shared__ float s_m[kWaves][G];
 
   static_assert(!(APP && F8), "appending decode takes bf16 caches");
+  static_assert(LPT == 4 * TPL, "a group reduces 4 heads x TPL tokens, one value per lane");
   // (an appending launch of rows r0 .. r0 + n - 1 gets every per-sequence
   // array offset by r0 on the host, so that no address waits for a load)
   const int part = blockIdx.x, g = blockIdx.y, s = (int)blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (SGPR) so that the tile loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane >> 3, li = lane & 7, row = lane >> 4;
-  const bool up4 = (li & 4) != 0, b1 = (li & 2) != 0, b0 = (li & 1) != 0;
+  const int grp = lane / LPT, li = lane % LPT, row = lane >> 4;
+  const bool b0 = (li & 1) != 0;
+  const int my_h = li / TPL, my_u = li % TPL;   // the (head in set, token) whose score this lane finishes
 
-  const int P = a.partition_size;
-  const int start = part * P;
+  const int P_ = a.partition_size;
+  const int start = part * P_;
   const int lgB = a.log2_block_size;
   const int Bmask = (1 << lgB) - 1;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
@@ -216,14 +245,11 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   // chunk's table entries, so that their latencies overlap.
   int len = a.seq_lens[s];
   if (app) len = app_pos + 1;
-  uint4 qr[G][PPL];
+  uint4 qr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int k = 0; k < PPL; ++k)
-      qr[h][k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                                 ((int64_t)s * a.num_q_heads + g * G + h) * D +
-                                                 lane_dim<D, F8>(k, 0, li));
+    qr[h] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                            ((int64_t)s * a.num_q_heads + g * G + h) * D + 8 * li);
   auto stage_table = [&](int c0) {
     const int j0 = c0 >> lgB;
     int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
@@ -258,12 +284,11 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   // A partition past the sequence's last one gets an empty range and returns
   // before the merge; there is no early exit here, which would let the
   // compiler move the table loads above behind it.
-  const bool live = part * P < len || part == 0;
-  const int end = !live ? start : (start + P < len ? start + P : len);
+  const bool live = part * P_ < len || part == 0;
+  const int end = !live ? start : (start + P_ < len ? start + P_ : len);
 
-  // per-lane constant part of a K/V element offset (BIG: tokens grp, grp + 8
-  // of the tile relative to its first token)
-  const int lane_off = g * D + lane_dim<D, F8>(0, 0, li);
+  // per-lane constant part of a K/V element offset
+  const int lane_off = g * D + 8 * li;
 
   // APP: the new token's K/V rows of this head in the input, and their copy
   // into the cache by the partition that holds the new position
@@ -277,11 +302,11 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   if constexpr (APP) {
     new_k = static_cast<const T*>(a.new_key) + (int64_t)s * a.new_key_stride + g * D;
     new_v = static_cast<const T*>(a.new_value) + (int64_t)s * a.new_value_stride + g * D;
-    app_copy = app && app_pos / P == part && wave == 0 && lane < 2 * (D / 8);
+    app_copy = app && app_pos / P_ == part && wave == 0 && lane < 2 * (D / 8);
     if (app_copy) app_piece = *reinterpret_cast<const uint4*>((lane < D / 8 ? new_k : new_v) + 8 * (lane % (D / 8)));
   }
 
-  float m_own[NSET], l_own[NSET], acc[G][PPL][8];
+  float m_own[NSET], l_own[NSET], acc[G][8];
 #pragma unroll
   for (int j = 0; j < NSET; ++j) {
     m_own[j] = kNegInf;
@@ -290,9 +315,7 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int k = 0; k < PPL; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][k][i] = 0.f;
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
 
   // Tokens c0 .. c1 - 1 (B < 16: their table entries are in LDS from j0 on).
   auto range = [&](const int c0, const int c1, const int j0) __attribute__((always_inline)) {
@@ -305,11 +328,9 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
     // (with `fetched`, the block ids are `pf`, fetched early for tile t0, or
     // pre_start for a half past c1)
     auto load = [&](int t0, KVt& r, bool fetched = false, const int* pf = nullptr) __attribute__((always_inline)) {
+      const T* kp[NH * TPL];
+      const T* vp[NH * TPL];
       if (BIG) {
-        const T* kb[NH];
-        const T* vb[NH];
-        int64_t roff[NH][2];
-        bool isnew[NH][2] = {};
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) {
           const int th = t0 + hf * kHalf;
@@ -318,175 +339,131 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
                                                            : entry(tc >> lgB));
           blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
           const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
-          kb[hf] = kcache + base;
-          vb[hf] = vcache + base;
           // tokens past c1 read the half's first token (valid): their slots
           // may hold anything, and a zero weight times a NaN is NaN
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-            roff[hf][u] = (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) * row_elems + lane_off;
-          if constexpr (APP) {
-            // the token a lane loads is tc + its row offset; the new one comes
-            // from the input
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              isnew[hf][u] = app && tc + (tc + grp + 8 * u < c1 ? grp + 8 * u : 0) == app_pos;
+          for (int u = 0; u < TPL; ++u) {
+            const int r_ = tc + grp + NG * u < c1 ? grp + NG * u : 0;
+            const int64_t off = r_ * row_elems + lane_off;
+            const bool isnew = APP && app && tc + r_ == app_pos;
+            kp[hf * TPL + u] = isnew ? new_k + 8 * li : kcache + base + off;
+            vp[hf * TPL + u] = isnew ? new_v + 8 * li : vcache + base + off;
           }
-        }
-        if constexpr (F8) {
-          using P = typename KVt::Piece;
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) r.k[2 * hf + u] = *reinterpret_cast<const P*>(kb[hf] + roff[hf][u]);
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) r.v[2 * hf + u] = *reinterpret_cast<const P*>(vb[hf] + roff[hf][u]);
-        } else {
-          const T* kp[NH][2];
-          const T* vp[NH][2];
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              kp[hf][u] = APP && isnew[hf][u] ? new_k + lane_dim<D, F8>(0, 0, li) : kb[hf] + roff[hf][u];
-              vp[hf][u] = APP && isnew[hf][u] ? new_v + lane_dim<D, F8>(0, 0, li) : vb[hf] + roff[hf][u];
-            }
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int k = 0; k < PPL; ++k)
-                r.k[2 * hf + u][k] = *reinterpret_cast<const uint4*>(kp[hf][u] + 64 * k);
-#pragma unroll
-          for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-              for (int k = 0; k < PPL; ++k)
-                r.v[2 * hf + u][k] = *reinterpret_cast<const uint4*>(vp[hf][u] + 64 * k);
         }
       } else {
-        int64_t off[2 * NH];
-        bool isnew[2 * NH] = {};
 #pragma unroll
-        for (int u = 0; u < 2 * NH; ++u) {
-          int t = t0 + (u >> 1) * kHalf + grp + 8 * (u & 1);
+        for (int i = 0; i < NH * TPL; ++i) {
+          int t = t0 + (i / TPL) * kHalf + grp + NG * (i % TPL);
           t = t < c1 ? t : c0;
           const int64_t blk = s_bt[(t >> lgB) - j0];
-          off[u] = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
-          if constexpr (APP) isnew[u] = app && t == app_pos;
-        }
-        if constexpr (F8) {
-          using P = typename KVt::Piece;
-#pragma unroll
-          for (int u = 0; u < 2 * NH; ++u) r.k[u] = *reinterpret_cast<const P*>(kcache + off[u]);
-#pragma unroll
-          for (int u = 0; u < 2 * NH; ++u) r.v[u] = *reinterpret_cast<const P*>(vcache + off[u]);
-        } else {
-          const T* kp[2 * NH];
-          const T* vp[2 * NH];
-#pragma unroll
-          for (int u = 0; u < 2 * NH; ++u) {
-            kp[u] = APP && isnew[u] ? new_k + lane_dim<D, F8>(0, 0, li) : kcache + off[u];
-            vp[u] = APP && isnew[u] ? new_v + lane_dim<D, F8>(0, 0, li) : vcache + off[u];
-          }
-#pragma unroll
-          for (int u = 0; u < 2 * NH; ++u)
-#pragma unroll
-            for (int k = 0; k < PPL; ++k) r.k[u][k] = *reinterpret_cast<const uint4*>(kp[u] + 64 * k);
-#pragma unroll
-          for (int u = 0; u < 2 * NH; ++u)
-#pragma unroll
-            for (int k = 0; k < PPL; ++k) r.v[u][k] = *reinterpret_cast<const uint4*>(vp[u] + 64 * k);
+          const int64_t off = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
+          const bool isnew = APP && app && t == app_pos;
+          kp[i] = isnew ? new_k + 8 * li : kcache + off;
+          vp[i] = isnew ? new_v + 8 * li : vcache + off;
         }
       }
+#pragma unroll
+      for (int i = 0; i < NH * TPL; ++i) r.k[i] = *reinterpret_cast<const P*>(kp[i]);
+#pragma unroll
+      for (int i = 0; i < NH * TPL; ++i) r.v[i] = *reinterpret_cast<const P*>(vp[i]);
     };
 
-    // One half tile: tokens t0 + grp and t0 + grp + 8 of each group, held in
-    // r.k / r.v [2 hf] and [2 hf + 1].
+    // One half tile: tokens t0 + grp + NG u of each group, held in
+    // r.k / r.v [TPL hf + u].
     auto compute = [&](int t0, const KVt& r, const int hf) __attribute__((always_inline)) {
-      const bool valid0 = t0 + grp < c1;
-      const bool valid1 = t0 + grp + 8 < c1;
-      uint32_t kw[2][NW];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) bf16_words<D, F8>(r.k[2 * hf + u], kw[u]);
-      // partial dots: slot v of set j is head 4 j + v / 2, token v % 2
+      const bool valid = t0 + grp + NG * my_u < c1;   // the token of this lane's score
+      // partial dots: value h TPL + u of set j is head 4 j + h, token u
       float x[NSET];
+      {
+        uint32_t kw[TPL][4];
 #pragma unroll
-      for (int j = 0; j < NSET; ++j) {
-        float w[8];
+        for (int u = 0; u < TPL; ++u) bf16_words<F8>(r.k[TPL * hf + u], kw[u]);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int h = 4 * j + (v >> 1), u = v & 1;
-          float d = 0.f;
-          if (h < G) {
-            const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h][0]);
+        for (int j = 0; j < NSET; ++j) {
+          float w[LPT];
 #pragma unroll
-            for (int jw = 0; jw < NW; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
-          }
-          w[v] = d;
+          for (int h4 = 0; h4 < 4; ++h4)
+#pragma unroll
+            for (int u = 0; u < TPL; ++u) {
+              const int h = 4 * j + h4;
+              float d = 0.f;
+              if (h < G) {
+                const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h]);
+#pragma unroll
+                for (int jw = 0; jw < 4; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
+              }
+              w[h4 * TPL + u] = d;
+            }
+          // the reduction is a cross-lane operation: every lane must take
+          // part, so it runs unconditionally and invalid slots are masked
+          // afterwards
+          const float xs = reduce_scatter<LPT>(w, li) * scale;
+          const bool ok = (4 * j + my_h < G) && valid;
+          x[j] = ok ? xs : kNegInf;
         }
-        // the reduction is a cross-lane operation: every lane must take part,
-        // so it runs unconditionally and invalid slots are masked afterwards
-        const float xs = reduce_scatter8(w, up4, b1, b0) * scale;
-        const bool ok = (4 * j + (li >> 1) < G) && (b0 ? valid1 : valid0);
-        x[j] = ok ? xs : kNegInf;
       }
       // rare slow path: raise the wave's running maxima
       bool need = false;
 #pragma unroll
       for (int j = 0; j < NSET; ++j) need |= x[j] > m_own[j] + kRescaleSlack;
       if (__any(need)) {
-        uint32_t al[NSET][4];
+        uint32_t al[NSET][4][1];
 #pragma unroll
         for (int j = 0; j < NSET; ++j) {
+          // maximum over the lanes holding the same head: its tokens in the
+          // group, then the groups of the wave
           float mx = x[j];
           mx = fmaxf(mx, dpp<kDppXor1>(mx));
-          mx = fmaxf(mx, dpp<kDppRor8>(mx));
+          if constexpr (TPL == 4) {
+            mx = fmaxf(mx, dpp<kDppXor2>(mx));
+          } else {
+            mx = fmaxf(mx, dpp<kDppRor8>(mx));
+          }
           mx = fmaxf(mx, __shfl_xor(mx, 16));
           mx = fmaxf(mx, __shfl_xor(mx, 32));
           const float mn = fmaxf(m_own[j], mx);
           const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own[j] - mn);
           l_own[j] *= alpha;
           m_own[j] = mn;
-          broadcast4(__float_as_uint(alpha), up4, al[j]);
+          uint32_t al2[4][TPL / 2];
+          broadcast_pairs<TPL>(__float_as_uint(alpha), li, al2);
+#pragma unroll
+          for (int h4 = 0; h4 < 4; ++h4) al[j][h4][0] = al2[h4][0];
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float alpha = __uint_as_float(al[h >> 2][h & 3]);
+          const float alpha = __uint_as_float(al[h >> 2][h & 3][0]);
 #pragma unroll
-          for (int k = 0; k < PPL; ++k)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[h][k][i] *= alpha;
+          for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
         }
       }
-      // weights: one exponential per lane, paired per head, broadcast to the group
-      uint32_t pp[NSET][4];
+      // weights: one exponential per lane, paired over tokens (u, u + 1) of a
+      // head, broadcast to the group
+      uint32_t pp[NSET][4][TPL / 2];
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
         const float p = x[j] == kNegInf ? 0.f : fast_exp2(x[j] - m_own[j]);
         const float other = dpp<kDppXor1>(p);
         const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
         l_own[j] += b0 ? bf16_hi(pk) : bf16_lo(pk);
-        broadcast4(pk, up4, pp[j]);
+        broadcast_pairs<TPL>(pk, li, pp[j]);
       }
-      // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs.
-      uint32_t v0[NW], v1[NW];
-      bf16_words<D, F8>(r.v[2 * hf], v0);
-      bf16_words<D, F8>(r.v[2 * hf + 1], v1);
+      // V rows of each token pair interleaved per d: (v0[d], v1[d]) pairs.
 #pragma unroll
-      for (int jw = 0; jw < NW; ++jw) {
-        const int k = jw >> 2, i = jw & 3;
-        const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
+      for (int q2 = 0; q2 < TPL / 2; ++q2) {
+        uint32_t v0[4], v1[4];
+        bf16_words<F8>(r.v[TPL * hf + 2 * q2], v0);
+        bf16_words<F8>(r.v[TPL * hf + 2 * q2 + 1], v1);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint32_t w = pp[h >> 2][h & 3];
-          acc[h][k][2 * i] = dot2_bf16(w, lo, acc[h][k][2 * i]);
-          acc[h][k][2 * i + 1] = dot2_bf16(w, hi, acc[h][k][2 * i + 1]);
+        for (int jw = 0; jw < 4; ++jw) {
+          const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t w = pp[h >> 2][h & 3][q2];
+            acc[h][2 * jw] = dot2_bf16(w, lo, acc[h][2 * jw]);
+            acc[h][2 * jw + 1] = dot2_bf16(w, hi, acc[h][2 * jw + 1]);
+          }
         }
       }
     };
@@ -539,26 +516,24 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
   }
 
   if (!live) return;
-  const int nparts = len > 0 ? (len + P - 1) / P : 1;
+  const int nparts = len > 0 ? (len + P_ - 1) / P_ : 1;
 
   // Merge.  All lane groups of a wave share the running maxima, so their
-  // partial sums add directly: the two groups of each 16-lane row with DPP,
-  // the four rows in registers with gfx950's lane swaps, the four waves
-  // through LDS.  permlane32_swap(x, y) exchanges lanes 32..63 of x with
-  // lanes 0..31 of y, permlane16_swap(x, y) the odd 16-lane rows of x with
-  // the even rows of y; adding the two results of a swap sums rows (0, 2)
-  // and (1, 3), then rows 0 and 1.  With the lane's NV sums flattened as
-  // v = (h PPL + k) 8 + i and paired as below, row r ends with the totals of
-  // v = r Q .. r Q + Q - 1 in its lanes 0..7 (lanes 8..15 hold copies).
-  constexpr int NV = G * PPL * 8;
+  // partial sums add directly: (D = 64) the two groups of each 16-lane row
+  // with DPP, then the four rows in registers with gfx950's lane swaps, then
+  // the four waves through LDS.  permlane32_swap(x, y) exchanges lanes 32..63
+  // of x with lanes 0..31 of y, permlane16_swap(x, y) the odd 16-lane rows of
+  // x with the even rows of y; adding the two results of a swap sums rows
+  // (0, 2) and (1, 3), then rows 0 and 1.  With the lane's NV sums flattened
+  // as v = 8 h + i and paired as below, row r ends with the totals of
+  // v = r Q .. r Q + Q - 1 (D = 64: in lanes 0..7 of the row, copies in 8..15).
+  constexpr int NV = G * 8;
   constexpr int Q = NV / 4;
   float xs[NV];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int k = 0; k < PPL; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs[(h * PPL + k) * 8 + i] = acc[h][k][i] + dpp<kDppRor8>(acc[h][k][i]);
+    for (int i = 0; i < 8; ++i) xs[h * 8 + i] = LPT == 16 ? acc[h][i] : acc[h][i] + dpp<kDppRor8>(acc[h][i]);
   auto swap_add32 = [](float x, float y) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -574,25 +549,30 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
     // the 32-lane step each holds its first value in rows 0-1 and its second
     // in rows 2-3; the 16-lane step then puts v m, Q + m, 2Q + m, 3Q + m in
     // rows 0, 1, 2, 3
-    const float a = swap_add32(xs[m], xs[2 * Q + m]);
-    const float b = swap_add32(xs[Q + m], xs[3 * Q + m]);
-    tot[m] = swap_add16(a, b);
+    const float a_ = swap_add32(xs[m], xs[2 * Q + m]);
+    const float b_ = swap_add32(xs[Q + m], xs[3 * Q + m]);
+    tot[m] = swap_add16(a_, b_);
   }
+  // l: the lanes of a head in a group (its tokens), then the rows
   float lp[NSET];
 #pragma unroll
   for (int j = 0; j < NSET; ++j) {
     lp[j] = l_own[j] + dpp<kDppXor1>(l_own[j]);
-    lp[j] += dpp<kDppRor8>(lp[j]);
+    if constexpr (TPL == 4) {
+      lp[j] += dpp<kDppXor2>(lp[j]);
+    } else {
+      lp[j] += dpp<kDppRor8>(lp[j]);
+    }
     lp[j] = swap_add32(lp[j], lp[j]);
     lp[j] = swap_add16(lp[j], lp[j]);
   }
-  if ((lane & 8) == 0) {
+  if (LPT == 16 || (lane & 8) == 0) {
     if constexpr (Q % 8 == 0) {
-      // row r: (h, k) pairs r Q / 8 + c, 8 consecutive elements each
+      // row r: heads r Q / 8 + c, 8 consecutive elements each
 #pragma unroll
       for (int c = 0; c < Q / 8; ++c) {
-        const int hk = row * (Q / 8) + c;
-        float* dst = &s_acc[wave][hk / PPL][lane_dim<D, F8>(hk % PPL, 0, li)];
+        const int h = row * (Q / 8) + c;
+        float* dst = &s_acc[wave][h][8 * li];
         *reinterpret_cast<float4*>(dst) = make_float4(tot[8 * c], tot[8 * c + 1], tot[8 * c + 2], tot[8 * c + 3]);
         *reinterpret_cast<float4*>(dst + 4) =
             make_float4(tot[8 * c + 4], tot[8 * c + 5], tot[8 * c + 6], tot[8 * c + 7]);
@@ -600,14 +580,14 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
     } else {
 #pragma unroll
       for (int m = 0; m < Q; ++m) {
-        const int v = row * Q + m, hk = v >> 3;
-        s_acc[wave][hk / PPL][lane_dim<D, F8>(hk % PPL, v & 7, li)] = tot[m];
+        const int v = row * Q + m;
+        s_acc[wave][v >> 3][8 * li + (v & 7)] = tot[m];
       }
     }
-    if (row == 0 && !b0) {
+    if (row == 0 && my_u == 0) {
 #pragma unroll
       for (int j = 0; j < NSET; ++j) {
-        const int h = 4 * j + (li >> 1);
+        const int h = 4 * j + my_h;
         if (h < G) {
           s_l[wave][h] = lp[j];
           s_m[wave][h] = m_own[j];
