@@ -522,6 +522,51 @@ int pa_paged_prefill_fp8(void* out, const void* q,
                          int32_t block_size, float scale, float k_scale, float v_scale,
                          int32_t causal, void* stream);
 
+/* Bytes of workspace pa_paged_attention needs for a batch: that of
+ * pa_paged_decode for the batch's decode rows (the leading requests with one
+ * query each, found from query_start_loc_host); 0 when none is split. */
+size_t pa_paged_attention_workspace_size(const int32_t* query_start_loc_host, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                                         int32_t partition_size);
+
+/* A whole step's attention -- prefill chunks and decode rows of a mixed batch
+ * -- in one launch (plus the merge pass of decode rows split into
+ * partitions).  One metadata set describes every request, as in the
+ * attention-metadata section of "PagedAttention: fragmentation, blocks,
+ * block tables": request i's queries are rows query_start_loc[i] ..
+ * query_start_loc[i+1]-1 of q, the last q_i of its seq_lens[i] tokens (all
+ * written to the cache), and query j attends to keys 0 .. c_i + j (causal,
+ * c_i = seq_lens[i] - q_i) or to all seq_lens[i] keys, gathered by walking
+ * row i of the block table; a decode is a request with one query.
+ * The leading requests with one query each (the decode rows; with the usual
+ * decode-first batch order, all of them) run the pa_paged_decode partition
+ * pass with partition_size; the others run the pa_paged_prefill body; both
+ * kinds' work-groups share one grid, so the HBM-bound decode and the
+ * MFMA-bound prefill run side by side.  Results are bit for bit those of
+ * pa_paged_decode and pa_paged_prefill on the two parts.  (With head_dim
+ * 128 and more than 5 query heads per KV head the two parts are launched one
+ * after the other.)
+ * q, out: device bf16 [total_q][num_q_heads][head_dim], contiguous.
+ * query_start_loc: device int32 [num_seqs + 1]; query_start_loc_host: the
+ * same values in host memory (the metadata's CPU copy; the launch splits the
+ * batch with it).  seq_lens: device int32 [num_seqs].  Every q_i must be at
+ * most max_query_len; seq_lens[i] <= max_seq_len; ceil(max_seq_len / B)
+ * must not exceed bt_stride.  workspace: at least
+ * pa_paged_attention_workspace_size(...) bytes, 256-byte aligned.
+ * bf16 caches only.
+ * Errors: PA_ERR_INVALID for a query_start_loc_host that does not start at 0
+ * or decreases, a request with more than max_query_len queries, and the
+ * errors of pa_paged_decode and pa_paged_prefill; nothing is launched then. */
+int pa_paged_attention(void* out, const void* q,
+                       const void* key_cache, const void* value_cache,
+                       int64_t cache_block_stride, int32_t num_blocks,
+                       const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* query_start_loc, const int32_t* query_start_loc_host,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+                       int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t partition_size, float scale,
+                       int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

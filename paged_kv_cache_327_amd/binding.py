@@ -90,6 +90,10 @@ _SIGS = {
     "pa_paged_prefill_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                      c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_f32,
                                      c_i32, c_vp]),
+    "pa_paged_attention_workspace_size": (c_sz, [P_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_paged_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, P_i32, c_vp,
+                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
+                                   c_vp, c_sz, c_vp]),
     "pa_paged_prefill": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
 }
@@ -582,3 +586,44 @@ def _prefill(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_
         _check(lib().pa_paged_prefill(*args, int(bool(causal)), _stream(q, stream)))
     else:
         _check(lib().pa_paged_prefill_fp8(*args, fp8[0], fp8[1], int(bool(causal)), _stream(q, stream)))
+
+
+def pa_paged_attention_workspace_size(query_start_loc_host, num_q_heads, head_dim, max_seq_len, partition_size):
+    qsl = np.ascontiguousarray(query_start_loc_host, dtype=np.int32)
+    return lib().pa_paged_attention_workspace_size(_i32p(qsl), len(qsl) - 1, num_q_heads, head_dim, max_seq_len,
+                                                   partition_size)
+
+
+def pa_paged_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, query_start_loc_host, seq_lens,
+                       max_query_len, max_seq_len, scale, partition_size=512, causal=True, workspace=None,
+                       stream=None):
+    """A mixed batch (decode rows first, then prefill chunks) in one launch:
+    out/q [Tq, Hq, D] bf16 contiguous; query_start_loc int32 [S+1] on the
+    device and query_start_loc_host the same values on the host; seq_lens
+    int32 [S]; block_tables int32 [S, W]; workspace a uint8 device tensor
+    (allocated here if None)."""
+    import torch
+    nb, bs, hkv, d, bstride = _cache_geometry(key_cache, value_cache)
+    _bf16(q, "q")
+    _bf16(out, "out")
+    hq = q.shape[1]
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or not q.is_contiguous() \
+            or not out.is_contiguous():
+        raise InvalidArgument(PA_ERR_INVALID, "q and out must be contiguous [Tq, Hq, D]")
+    S = seq_lens.shape[0]
+    qsl_h = np.ascontiguousarray(query_start_loc_host, dtype=np.int32)
+    if query_start_loc.dtype != torch.int32 or query_start_loc.shape != (S + 1,) or qsl_h.shape != (S + 1,) \
+            or seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise InvalidArgument(PA_ERR_INVALID, "query_start_loc int32 [S+1] (device and host) and seq_lens int32 [S]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1 \
+            or block_tables.shape[0] != S:
+        raise InvalidArgument(PA_ERR_INVALID, "block_tables must be int32 [S, W] with unit column stride")
+    need = lib().pa_paged_attention_workspace_size(_i32p(qsl_h), S, hq, d, max_seq_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_paged_attention(out.data_ptr(), q.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), bstride,
+                                    nb, block_tables.data_ptr(), block_tables.stride(0), query_start_loc.data_ptr(),
+                                    _i32p(qsl_h), seq_lens.data_ptr(), S, max_query_len, max_seq_len, hq, hkv, d, bs,
+                                    partition_size, scale, int(bool(causal)), ws_ptr, ws_bytes, _stream(q, stream)))

@@ -49,6 +49,10 @@ def sources():
 # * prefill, head_dim 64: two waves per SIMD, no scratch.
 # * decode partition pass: no AGPRs and no scratch; three waves per SIMD up
 #   to 4 query heads per KV head, two for 5-8.
+# * mixed-batch kernel (prefill and decode bodies in one kernel): 256
+#   VGPRs, no AGPRs, two waves per SIMD; with B < 16 at head_dim 128 up to
+#   32 bytes per lane of scratch (prefill's per-key offsets beside the
+#   decode body's registers).
 # * every other kernel: no scratch.
 def _budget(name, targs):
     if name == "prefill_kernel":
@@ -57,6 +61,9 @@ def _budget(name, targs):
             spill = 12 if (not big and not f8 and not small) else 0
             return 256, 0, spill, 2
         return 256, 0, 0, 2
+    if name == "varlen_kernel":
+        d, big = targs[0], targs[4]
+        return (256, 0, 0 if (d == 64 or big) else 32, 2)
     if name == "decode_partition_kernel":
         return (512, 0, 0, 3) if targs[1] <= 4 else (512, 0, 0, 2)
     return 512, 256, 0, 1

@@ -227,13 +227,15 @@ struct NewTokens {
   const int32_t* positions = nullptr;
 };
 
-int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* key_cache,
-                const void* value_cache, int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
-                int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
-                int32_t partition_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
-                size_t workspace_bytes, void* stream, const NewTokens& nt = NewTokens()) {
-  pa::clear_error();
+// Validate a decode call's arguments and fill `a` (a.num_seqs = 0: nothing
+// to launch).
+int make_decode_args(const char* fn, void* out, float* lse, const void* q, const void* key_cache,
+                     const void* value_cache, int64_t cache_block_stride, int32_t num_blocks,
+                     const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_seq_len, int32_t partition_size, float scale, bool fp8, float k_scale, float v_scale,
+                     void* workspace, size_t workspace_bytes, const NewTokens& nt, pa::DecodeArgs& a) {
+  a = pa::DecodeArgs{};
   if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
@@ -279,7 +281,6 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
                         nt.positions[i]);
     }
   }
-  pa::DecodeArgs a{};
   a.out = out;
   a.lse = lse;
   a.q = q;
@@ -313,8 +314,25 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     a.new_value_stride = nt.value_row_stride;
     a.wr_tables = const_cast<int32_t*>(block_tables);
     a.wr_lens = const_cast<int32_t*>(seq_lens);
-    return hip_status(fn, pa::launch_paged_decode_append(a, nt.slots, nt.positions, stream));
   }
+  return PA_OK;
+}
+
+int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* key_cache,
+                const void* value_cache, int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables,
+                int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_seq_len,
+                int32_t partition_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                size_t workspace_bytes, void* stream, const NewTokens& nt = NewTokens()) {
+  pa::clear_error();
+  pa::DecodeArgs a;
+  if (int rc = make_decode_args(fn, out, lse, q, key_cache, value_cache, cache_block_stride, num_blocks, block_tables,
+                                bt_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_seq_len, partition_size, scale, fp8, k_scale, v_scale, workspace, workspace_bytes,
+                                nt, a))
+    return rc;
+  if (a.num_seqs == 0) return PA_OK;
+  if (nt.slots) return hip_status(fn, pa::launch_paged_decode_append(a, nt.slots, nt.positions, stream));
   return hip_status(fn, pa::launch_paged_decode(a, stream));
 }
 
@@ -395,13 +413,15 @@ int pa_paged_decode_fp8(void* out, float* lse, const void* q, const void* key_ca
 
 namespace {
 
-int prefill_impl(const char* fn, void* out, const void* q, const void* key_cache, const void* value_cache,
-                 int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
-                 const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
-                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                 int32_t block_size, float scale, int32_t causal, bool fp8, float k_scale, float v_scale,
-                 void* stream) {
-  pa::clear_error();
+// Validate a prefill call's arguments and fill `a` (a.num_seqs = 0: nothing
+// to launch).
+int make_prefill_args(const char* fn, void* out, const void* q, const void* key_cache, const void* value_cache,
+                      int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, float scale, int32_t causal, bool fp8, float k_scale,
+                      float v_scale, pa::PrefillArgs& a) {
+  a = pa::PrefillArgs{};
   if (int rc = check_heads(fn, num_q_heads, num_kv_heads, head_dim, block_size)) return rc;
   const int64_t row = (int64_t)num_kv_heads * head_dim;
   if (int rc = check_cache(fn, key_cache, value_cache, cache_block_stride, num_blocks, block_size, row)) return rc;
@@ -420,7 +440,6 @@ int prefill_impl(const char* fn, void* out, const void* q, const void* key_cache
   if (((int64_t)max_seq_len + block_size - 1) / block_size > bt_stride)
     return pa::fail(PA_ERR_INVALID, "%s: ceil(max_seq_len / B) exceeds bt_stride %d", fn, bt_stride);
   if (!(scale == scale)) return pa::fail(PA_ERR_INVALID, "%s: scale is NaN", fn);
-  pa::PrefillArgs a{};
   a.out = out;
   a.q = q;
   a.key_cache = key_cache;
@@ -442,7 +461,42 @@ int prefill_impl(const char* fn, void* out, const void* q, const void* key_cache
   a.causal = causal;
   a.fp8 = fp8 ? 1 : 0;
   a.v_scale = fp8 ? v_scale : 1.f;
+  return PA_OK;
+}
+
+int prefill_impl(const char* fn, void* out, const void* q, const void* key_cache, const void* value_cache,
+                 int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                 const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+                 int32_t max_seq_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, float scale, int32_t causal, bool fp8, float k_scale, float v_scale,
+                 void* stream) {
+  pa::clear_error();
+  pa::PrefillArgs a;
+  if (int rc = make_prefill_args(fn, out, q, key_cache, value_cache, cache_block_stride, num_blocks, block_tables,
+                                 bt_stride, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len,
+                                 num_q_heads, num_kv_heads, head_dim, block_size, scale, causal, fp8, k_scale,
+                                 v_scale, a))
+    return rc;
+  if (a.num_seqs == 0) return PA_OK;
   return hip_status(fn, pa::launch_paged_prefill(a, stream));
+}
+
+// Requests 0 .. n - 1 with one query each (the decode rows of a mixed batch):
+// the leading run of query_start_loc_host steps of 1.  -1 if
+// query_start_loc_host is not a non-decreasing sequence from 0.
+int32_t leading_decodes(const int32_t* qsl, int32_t num_seqs) {
+  if (qsl[0] != 0) return -1;
+  int32_t n = 0;
+  bool run = true;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t ql = qsl[i + 1] - qsl[i];
+    if (ql < 0) return -1;
+    if (run && ql == 1)
+      ++n;
+    else
+      run = false;
+  }
+  return n;
 }
 
 }  // namespace
@@ -468,6 +522,65 @@ int pa_paged_prefill_fp8(void* out, const void* q, const void* key_cache, const 
   return prefill_impl("paged_prefill_fp8", out, q, key_cache, value_cache, cache_block_stride, num_blocks,
                       block_tables, bt_stride, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len,
                       num_q_heads, num_kv_heads, head_dim, block_size, scale, causal, true, k_scale, v_scale, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t pa_paged_attention_workspace_size(const int32_t* query_start_loc_host, int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t head_dim, int32_t max_seq_len, int32_t partition_size) {
+  if (!query_start_loc_host || num_seqs <= 0) return 0;
+  const int32_t nd = leading_decodes(query_start_loc_host, num_seqs);
+  return nd > 0 ? pa_paged_decode_workspace_size(nd, num_q_heads, head_dim, max_seq_len, partition_size) : 0;
+}
+
+int pa_paged_attention(void* out, const void* q, const void* key_cache, const void* value_cache,
+                       int64_t cache_block_stride, int32_t num_blocks, const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* query_start_loc, const int32_t* query_start_loc_host, const int32_t* seq_lens,
+                       int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t partition_size,
+                       float scale, int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "paged_attention";
+  pa::clear_error();
+  if (num_seqs < 0) return pa::fail(PA_ERR_INVALID, "%s: num_seqs < 0", fn);
+  if (num_seqs == 0) return PA_OK;
+  if (!query_start_loc_host || !query_start_loc || !block_tables || !seq_lens)
+    return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  const int32_t nd = leading_decodes(query_start_loc_host, num_seqs);
+  if (nd < 0)
+    return pa::fail(PA_ERR_INVALID, "%s: query_start_loc_host must start at 0 and not decrease", fn);
+  // the prefill requests' longest query (every request's must fit max_query_len)
+  int32_t pre_max_q = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t ql = query_start_loc_host[i + 1] - query_start_loc_host[i];
+    if (ql > max_query_len)
+      return pa::fail(PA_ERR_INVALID, "%s: request %d has %d queries, more than max_query_len %d", fn, i, ql,
+                      max_query_len);
+    if (i >= nd && ql > pre_max_q) pre_max_q = ql;
+  }
+  if (bt_stride < 1) return pa::fail(PA_ERR_INVALID, "%s: bt_stride must be positive", fn);
+  pa::DecodeArgs d;
+  if (int rc = make_decode_args(fn, out, nullptr, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                                block_tables, bt_stride, seq_lens, nd, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_seq_len, partition_size, scale, false, 1.f, 1.f, workspace, workspace_bytes,
+                                NewTokens(), d))
+    return rc;
+  pa::PrefillArgs p;
+  if (int rc = make_prefill_args(fn, out, q, key_cache, value_cache, cache_block_stride, num_blocks,
+                                 block_tables + (int64_t)nd * bt_stride, bt_stride, query_start_loc + nd, seq_lens + nd,
+                                 num_seqs - nd, pre_max_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, scale, causal, false, 1.f, 1.f, p))
+    return rc;
+  if (d.num_seqs == 0 && p.num_seqs == 0) return PA_OK;
+  // fields the fused launch reads from the other kind's arguments
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.log2_block_size = ilog2(block_size);
+  p.num_blocks = num_blocks;
+  p.cache_block_stride = cache_block_stride;
+  return hip_status(fn, pa::launch_paged_varlen(p, d, stream));
 }
 
 }  // extern "C"

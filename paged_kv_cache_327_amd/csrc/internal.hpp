@@ -128,6 +128,13 @@ struct PrefillArgs {
   float v_scale;   // 1 for bf16 caches
 };
 int launch_paged_prefill(const PrefillArgs& a, void* stream);
+// Work-groups of a prefill launch (0 when a.num_seqs is 0; -1 when too many).
+int64_t prefill_grid_size(const PrefillArgs& a);
+// The decode's log-sum-exp merge pass alone (nothing when a.max_parts <= 1).
+int launch_decode_merge(const DecodeArgs& a, void* stream);
+// A mixed batch in one launch: prefill requests p and decode rows d (either
+// may have num_seqs 0), then the decode rows' merge pass.
+int launch_paged_varlen(const PrefillArgs& p, const DecodeArgs& d, void* stream);
 
 const char* hip_error_string(int err);
 

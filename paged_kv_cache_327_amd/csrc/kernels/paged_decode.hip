@@ -49,597 +49,16 @@
 
 #include "../internal.hpp"
 #include "common.hpp"
+#include "decode_body.hpp"
 
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kHalf = 16;     // tokens of a half tile, inside one block when B >= 16
-constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
-constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1)
-constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kRescaleSlack = 8.0f;  // log2 units
-
-// Lane layout.  A token's K (or V) row of one KV head is held by LPT = D / 8
-// lanes, 8 elements each (lane li = lane % LPT holds d = 8 li .. 8 li + 7:
-// one 16-byte piece of bf16, or 8 E4M3 codes), so a lane group reads the
-// row's contiguous bytes.  The NG = 64 / LPT groups of a wave hold NG
-// consecutive tokens per load instruction; a half tile's 16 tokens take
-// TPL = 16 / NG loads, token u of group grp being t0 + grp + NG u.
-template <int D>
-struct Layout {
-  static constexpr int LPT = D / 8;
-  static constexpr int NG = 64 / LPT;
-  static constexpr int TPL = kHalf / NG;
-};
-
-template <bool F8>
-using PieceOf = typename std::conditional<F8, uint2, uint4>::type;
-
-// A lane's pieces of the K and V rows of its NT tokens.
-template <bool F8, int NT>
-struct KV {
-  PieceOf<F8> k[NT];
-  PieceOf<F8> v[NT];
-};
-
-// The 8 elements of a piece as 4 packed bf16 pairs in element order (E4M3
-// codes are converted exactly).
-template <bool F8>
-__device__ __forceinline__ void bf16_words(const PieceOf<F8>& piece, uint32_t (&w)[4]) {
-  if constexpr (F8) {
-    w[0] = e4m3x2_to_bf16x2<false>(piece.x);
-    w[1] = e4m3x2_to_bf16x2<true>(piece.x);
-    w[2] = e4m3x2_to_bf16x2<false>(piece.y);
-    w[3] = e4m3x2_to_bf16x2<true>(piece.y);
-  } else {
-    w[0] = piece.x;
-    w[1] = piece.y;
-    w[2] = piece.z;
-    w[3] = piece.w;
-  }
-}
-
-// One reduce-scatter step over lane pairs that differ in one bit of li:
-// a lane whose bit is set keeps the upper half of its values, its partner
-// the lower half, and each adds the partner's copy of the half it keeps.
-template <int CTRL, int N>
-__device__ __forceinline__ void rs_step(const float (&v)[N], float (&w)[N / 2], bool bit) {
-#pragma unroll
-  for (int k = 0; k < N / 2; ++k) {
-    const float send = bit ? v[k] : v[k + N / 2];
-    const float keep = bit ? v[k + N / 2] : v[k];
-    w[k] = keep + dpp<CTRL>(send);
-  }
-}
-
-// Sum of LPT per-lane values over the LPT lanes of a group, scattered: lane
-// li of the group ends with the total of value li.  The partner of each step
-// flips one bit of li: the row mirror (li <-> 15 - li) bit 3, the half-row
-// mirror (li <-> li ^ 7) bit 2, then xor 2 and xor 1.
-template <int LPT>
-__device__ __forceinline__ float reduce_scatter(const float (&v)[LPT], int li) {
-  float w8[8];
-  if constexpr (LPT == 16) {
-    rs_step<kDppRowMirror>(v, w8, (li & 8) != 0);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w8[k] = v[k];
-  }
-  float w4[4], w2[2], w1[1];
-  rs_step<kDppHalfMirror>(w8, w4, (li & 4) != 0);
-  rs_step<kDppXor2>(w4, w2, (li & 2) != 0);
-  rs_step<kDppXor1>(w2, w1, (li & 1) != 0);
-  return w1[0];
-}
-
-// Each head of a set of four holds one value per token pair in the lanes of
-// that pair (group lanes TPL h + 2 q and TPL h + 2 q + 1, q < TPL / 2); every
-// lane of the group gets all of them: out[h][q].
-template <int TPL>
-__device__ __forceinline__ void broadcast_pairs(uint32_t x, int li, uint32_t (&out)[4][TPL / 2]) {
-  if constexpr (TPL == 4) {
-    // a group is a 16-lane row: broadcast lanes 0, 2, 4, ..., 14 of the row
-    out[0][0] = dpp<kDppRowBcast0 + 0>(x);
-    out[0][1] = dpp<kDppRowBcast0 + 2>(x);
-    out[1][0] = dpp<kDppRowBcast0 + 4>(x);
-    out[1][1] = dpp<kDppRowBcast0 + 6>(x);
-    out[2][0] = dpp<kDppRowBcast0 + 8>(x);
-    out[2][1] = dpp<kDppRowBcast0 + 10>(x);
-    out[3][0] = dpp<kDppRowBcast0 + 12>(x);
-    out[3][1] = dpp<kDppRowBcast0 + 14>(x);
-  } else {
-    // a group is half a row (lanes 2h, 2h + 1 hold head h): quad broadcasts
-    // give heads 0-1 of this quad, the half-row mirror those of the other
-    const bool up4 = (li & 4) != 0;
-    const uint32_t a = dpp<kDppBcast0>(x), b = dpp<kDppBcast2>(x);
-    const uint32_t a2 = dpp<kDppHalfMirror>(a), b2 = dpp<kDppHalfMirror>(b);
-    out[0][0] = up4 ? a2 : a;
-    out[1][0] = up4 ? b2 : b;
-    out[2][0] = up4 ? a : a2;
-    out[3][0] = up4 ? b : b2;
-  }
-}
-
-// Appending decode (APP): one new token per sequence of the launch, its slot
-// and position in the kernel arguments (up to kAppendRows sequences per
-// launch).  Every work-group of sequence s takes the sequence's length
-// (position + 1) and the block of the new position's table entry (slot / B)
-// from these arguments and reads the new token's K/V from the input rows, so
-// it never reads a table entry, length or cache row that this launch writes;
-// the work-group of the partition holding the new token writes its head's
-// K/V rows to the slot, and the one of head 0 also the table entry and the
-// length.  The result is that of the cache write with the table update
-// followed by decode, in one launch.
-constexpr int kAppendRows = 256;
-struct AppendRows {
-  int64_t slots[kAppendRows];
-  int32_t pos[kAppendRows];
-};
-struct NoAppend {
-  int32_t unused;
-};
-template <bool APP>
-using RowsOf = typename std::conditional<APP, AppendRows, NoAppend>::type;
+using namespace decode_body;
 
 template <int D, int G, bool BIG, bool F8, bool APP>
 __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, RowsOf<APP> rows) {
-  using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
-  using Lay = Layout<D>;
-  constexpr int LPT = Lay::LPT, NG = Lay::NG, TPL = Lay::TPL;
-  constexpr int NH = F8 ? kHalves8 : 1;   // half tiles per tile
-  constexpr int kTile = kHalf * NH;       // tokens per wave iteration
-  using KVt = KV<F8, TPL * NH>;
-  using P = PieceOf<F8>;
-  constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score per lane per set
-  __shared__ int32_t s_bt[BIG ? 1 : kChunk];
-  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][D];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_m[kWaves][G];
-
-  static_assert(!(APP && F8), "appending decode takes bf16 caches");
-  static_assert(LPT == 4 * TPL, "a group reduces 4 heads x TPL tokens, one value per lane");
-  // (an appending launch of rows r0 .. r0 + n - 1 gets every per-sequence
-  // array offset by r0 on the host, so that no address waits for a load)
-  const int part = blockIdx.x, g = blockIdx.y, s = (int)blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform (SGPR) so that the tile loop below branches on scalars
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane / LPT, li = lane % LPT, row = lane >> 4;
-  const bool b0 = (li & 1) != 0;
-  const int my_h = li / TPL, my_u = li % TPL;   // the (head in set, token) whose score this lane finishes
-
-  const int P_ = a.partition_size;
-  const int start = part * P_;
-  const int lgB = a.log2_block_size;
-  const int Bmask = (1 << lgB) - 1;
-  const int64_t row_elems = (int64_t)a.num_kv_heads * D;
-  const int64_t bstride = a.cache_block_stride;
-  const T* kcache = static_cast<const T*>(a.key_cache);
-  const T* vcache = static_cast<const T*>(a.value_cache);
-  const int32_t* bt_row = a.block_tables + (int64_t)s * a.bt_stride;
-  const int width = (a.max_seq_len + Bmask) >> lgB;   // table entries that may be read
-  const float scale = a.scale * kLog2e;
-
-  // APP: this sequence's new token (position, slot) and the block its
-  // position's table entry names after the append
-  int64_t app_slot = -1;
-  int app_pos = -1;
-  if constexpr (APP) {
-    app_slot = rows.slots[blockIdx.z];
-    app_pos = rows.pos[blockIdx.z];
-  }
-  const bool app = APP && app_slot >= 0;
-  const int app_j = app ? app_pos >> lgB : -1;
-  const int app_blk = app ? (int)(app_slot >> lgB) : 0;
-  // table entry j as the kernel sees it (APP: the new position's entry from
-  // the arguments).  Prefetched entries are loaded as they stand and fixed
-  // where they are used, so that their loads never wait for the position.
-  auto fix_entry = [&](int j, int b) __attribute__((always_inline)) {
-    return APP && j == app_j ? app_blk : b;
-  };
-  auto entry = [&](int j) __attribute__((always_inline)) { return fix_entry(j, bt_row[j]); };
-
-  // Independent loads first: the length, the queries and (B < 16) the first
-  // chunk's table entries, so that their latencies overlap.
-  int len = a.seq_lens[s];
-  if (app) len = app_pos + 1;
-  uint4 qr[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qr[h] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                            ((int64_t)s * a.num_q_heads + g * G + h) * D + 8 * li);
-  auto stage_table = [&](int c0) {
-    const int j0 = c0 >> lgB;
-    int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
-    nj = nj < width - j0 ? nj : width - j0;
-    for (int i = tid; i < nj; i += 256) {
-      int b = entry(j0 + i);
-      b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-      s_bt[i] = b;
-    }
-  };
-  if (!BIG) stage_table(start);
-  // BIG: the table entries of the halves of this wave's first two tiles and
-  // of the partition's first token, fetched before the length is known
-  // (indexes are kept inside the row), so that the first K/V loads wait for
-  // one round trip instead of two.
-  int pre[2][NH] = {}, pre_start = 0;
-  if constexpr (BIG) {
-    const int wmax = width - 1;
-    const int tw = start + wave * kTile;
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) {
-        const int i = (tw + k * kWaves * kTile + hf * kHalf) >> lgB;
-        pre[k][hf] = bt_row[i < wmax ? i : wmax];
-      }
-    const int is = start >> lgB;
-    pre_start = bt_row[is < wmax ? is : wmax];
-  }
-
-  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
-  // A partition past the sequence's last one gets an empty range and returns
-  // before the merge; there is no early exit here, which would let the
-  // compiler move the table loads above behind it.
-  const bool live = part * P_ < len || part == 0;
-  const int end = !live ? start : (start + P_ < len ? start + P_ : len);
-
-  // per-lane constant part of a K/V element offset
-  const int lane_off = g * D + 8 * li;
-
-  // APP: the new token's K/V rows of this head in the input, and their copy
-  // into the cache by the partition that holds the new position
-  // (lanes 0 .. 2 D / 8 - 1 of wave 0 copy one 16-byte piece each: the piece
-  // is loaded here and stored after the merge, so that the store neither
-  // waits for the load nor holds up the wave's first K/V loads)
-  const T* new_k = nullptr;
-  const T* new_v = nullptr;
-  bool app_copy = false;
-  uint4 app_piece = make_uint4(0, 0, 0, 0);
-  if constexpr (APP) {
-    new_k = static_cast<const T*>(a.new_key) + (int64_t)s * a.new_key_stride + g * D;
-    new_v = static_cast<const T*>(a.new_value) + (int64_t)s * a.new_value_stride + g * D;
-    app_copy = app && app_pos / P_ == part && wave == 0 && lane < 2 * (D / 8);
-    if (app_copy) app_piece = *reinterpret_cast<const uint4*>((lane < D / 8 ? new_k : new_v) + 8 * (lane % (D / 8)));
-  }
-
-  float m_own[NSET], l_own[NSET], acc[G][8];
-#pragma unroll
-  for (int j = 0; j < NSET; ++j) {
-    m_own[j] = kNegInf;
-    l_own[j] = 0.f;
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-
-  // Tokens c0 .. c1 - 1 (B < 16: their table entries are in LDS from j0 on).
-  auto range = [&](const int c0, const int c1, const int j0) __attribute__((always_inline)) {
-
-    // Tokens past c1 read token c0 (always valid), so every load stays inside
-    // the cache and can be issued unconditionally: with no branch around the
-    // prefetches the compiler's wait counts stay exact and the next tiles'
-    // loads remain in flight while this one is computed.  All K loads are
-    // issued before the V loads so q.k can start first.
-    // (with `fetched`, the block ids are `pf`, fetched early for tile t0, or
-    // pre_start for a half past c1)
-    auto load = [&](int t0, KVt& r, bool fetched = false, const int* pf = nullptr) __attribute__((always_inline)) {
-      const T* kp[NH * TPL];
-      const T* vp[NH * TPL];
-      if (BIG) {
-#pragma unroll
-        for (int hf = 0; hf < NH; ++hf) {
-          const int th = t0 + hf * kHalf;
-          const int tc = th < c1 ? th : c0;          // wave-uniform
-          int blk = __builtin_amdgcn_readfirstlane(fetched ? fix_entry(tc >> lgB, th < c1 ? pf[hf] : pre_start)
-                                                           : entry(tc >> lgB));
-          blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-          const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems;
-          // tokens past c1 read the half's first token (valid): their slots
-          // may hold anything, and a zero weight times a NaN is NaN
-#pragma unroll
-          for (int u = 0; u < TPL; ++u) {
-            const int r_ = tc + grp + NG * u < c1 ? grp + NG * u : 0;
-            const int64_t off = r_ * row_elems + lane_off;
-            const bool isnew = APP && app && tc + r_ == app_pos;
-            kp[hf * TPL + u] = isnew ? new_k + 8 * li : kcache + base + off;
-            vp[hf * TPL + u] = isnew ? new_v + 8 * li : vcache + base + off;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NH * TPL; ++i) {
-          int t = t0 + (i / TPL) * kHalf + grp + NG * (i % TPL);
-          t = t < c1 ? t : c0;
-          const int64_t blk = s_bt[(t >> lgB) - j0];
-          const int64_t off = blk * bstride + (int64_t)(t & Bmask) * row_elems + lane_off;
-          const bool isnew = APP && app && t == app_pos;
-          kp[i] = isnew ? new_k + 8 * li : kcache + off;
-          vp[i] = isnew ? new_v + 8 * li : vcache + off;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NH * TPL; ++i) r.k[i] = *reinterpret_cast<const P*>(kp[i]);
-#pragma unroll
-      for (int i = 0; i < NH * TPL; ++i) r.v[i] = *reinterpret_cast<const P*>(vp[i]);
-    };
-
-    // One half tile: tokens t0 + grp + NG u of each group, held in
-    // r.k / r.v [TPL hf + u].
-    auto compute = [&](int t0, const KVt& r, const int hf) __attribute__((always_inline)) {
-      const bool valid = t0 + grp + NG * my_u < c1;   // the token of this lane's score
-      // partial dots: value h TPL + u of set j is head 4 j + h, token u
-      float x[NSET];
-      {
-        uint32_t kw[TPL][4];
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) bf16_words<F8>(r.k[TPL * hf + u], kw[u]);
-#pragma unroll
-        for (int j = 0; j < NSET; ++j) {
-          float w[LPT];
-#pragma unroll
-          for (int h4 = 0; h4 < 4; ++h4)
-#pragma unroll
-            for (int u = 0; u < TPL; ++u) {
-              const int h = 4 * j + h4;
-              float d = 0.f;
-              if (h < G) {
-                const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h]);
-#pragma unroll
-                for (int jw = 0; jw < 4; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
-              }
-              w[h4 * TPL + u] = d;
-            }
-          // the reduction is a cross-lane operation: every lane must take
-          // part, so it runs unconditionally and invalid slots are masked
-          // afterwards
-          const float xs = reduce_scatter<LPT>(w, li) * scale;
-          const bool ok = (4 * j + my_h < G) && valid;
-          x[j] = ok ? xs : kNegInf;
-        }
-      }
-      // rare slow path: raise the wave's running maxima
-      bool need = false;
-#pragma unroll
-      for (int j = 0; j < NSET; ++j) need |= x[j] > m_own[j] + kRescaleSlack;
-      if (__any(need)) {
-        uint32_t al[NSET][4][1];
-#pragma unroll
-        for (int j = 0; j < NSET; ++j) {
-          // maximum over the lanes holding the same head: its tokens in the
-          // group, then the groups of the wave
-          float mx = x[j];
-          mx = fmaxf(mx, dpp<kDppXor1>(mx));
-          if constexpr (TPL == 4) {
-            mx = fmaxf(mx, dpp<kDppXor2>(mx));
-          } else {
-            mx = fmaxf(mx, dpp<kDppRor8>(mx));
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(m_own[j], mx);
-          const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own[j] - mn);
-          l_own[j] *= alpha;
-          m_own[j] = mn;
-          uint32_t al2[4][TPL / 2];
-          broadcast_pairs<TPL>(__float_as_uint(alpha), li, al2);
-#pragma unroll
-          for (int h4 = 0; h4 < 4; ++h4) al[j][h4][0] = al2[h4][0];
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float alpha = __uint_as_float(al[h >> 2][h & 3][0]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
-        }
-      }
-      // weights: one exponential per lane, paired over tokens (u, u + 1) of a
-      // head, broadcast to the group
-      uint32_t pp[NSET][4][TPL / 2];
-#pragma unroll
-      for (int j = 0; j < NSET; ++j) {
-        const float p = x[j] == kNegInf ? 0.f : fast_exp2(x[j] - m_own[j]);
-        const float other = dpp<kDppXor1>(p);
-        const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
-        l_own[j] += b0 ? bf16_hi(pk) : bf16_lo(pk);
-        broadcast_pairs<TPL>(pk, li, pp[j]);
-      }
-      // V rows of each token pair interleaved per d: (v0[d], v1[d]) pairs.
-#pragma unroll
-      for (int q2 = 0; q2 < TPL / 2; ++q2) {
-        uint32_t v0[4], v1[4];
-        bf16_words<F8>(r.v[TPL * hf + 2 * q2], v0);
-        bf16_words<F8>(r.v[TPL * hf + 2 * q2 + 1], v1);
-#pragma unroll
-        for (int jw = 0; jw < 4; ++jw) {
-          const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t w = pp[h >> 2][h & 3][q2];
-            acc[h][2 * jw] = dot2_bf16(w, lo, acc[h][2 * jw]);
-            acc[h][2 * jw + 1] = dot2_bf16(w, hi, acc[h][2 * jw + 1]);
-          }
-        }
-      }
-    };
-
-    // kBuffers register buffers: while tile t is computed, the next
-    // kBuffers - 1 tiles of the wave are in flight.  The loop runs whole
-    // rounds of kBuffers tiles and has a single, bottom-tested exit (an exit
-    // in the middle gives the compiler a path back into the loop with loads
-    // pending, and it then drains every load at the top); the last tiles are
-    // computed after it from buffers already loaded.  All branches here are
-    // wave-uniform.  The first loads are issued whatever n_tiles is (they
-    // stay inside the cache), so nothing delays them.
-    constexpr int kStep = kWaves * kTile;
-    constexpr int NB = kBuffers;
-    int t = c0 + wave * kTile;
-    const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
-    KVt r[NB];
-#pragma unroll
-    for (int k = 0; k + 1 < NB; ++k) load(t + k * kStep, r[k], BIG && k < 2, pre[k < 2 ? k : 0]);
-    int i = 0;
-    for (; i + NB <= n_tiles; i += NB) {
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        load(t + (NB - 1) * kStep, r[(k + NB - 1) % NB]);
-#pragma unroll
-        for (int hf = 0; hf < NH; ++hf) compute(t + hf * kHalf, r[k], hf);
-        t += kStep;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k + 1 < NB; ++k)
-      if (n_tiles - i > k) {
-#pragma unroll
-        for (int hf = 0; hf < NH; ++hf) compute(t + k * kStep + hf * kHalf, r[k], hf);
-      }
-  };
-  if constexpr (BIG) {
-    // one range: no outer loop, whose header would drain the query loads
-    // before the first K/V loads are issued
-    range(start, end, start >> lgB);
-  } else {
-    for (int c0 = start; c0 < end; c0 += kChunk) {
-      if (c0 != start) {
-        __syncthreads();
-        stage_table(c0);
-      }
-      __syncthreads();
-      range(c0, c0 + kChunk < end ? c0 + kChunk : end, c0 >> lgB);
-    }
-  }
-
-  if (!live) return;
-  const int nparts = len > 0 ? (len + P_ - 1) / P_ : 1;
-
-  // Merge.  All lane groups of a wave share the running maxima, so their
-  // partial sums add directly: (D = 64) the two groups of each 16-lane row
-  // with DPP, then the four rows in registers with gfx950's lane swaps, then
-  // the four waves through LDS.  permlane32_swap(x, y) exchanges lanes 32..63
-  // of x with lanes 0..31 of y, permlane16_swap(x, y) the odd 16-lane rows of
-  // x with the even rows of y; adding the two results of a swap sums rows
-  // (0, 2) and (1, 3), then rows 0 and 1.  With the lane's NV sums flattened
-  // as v = 8 h + i and paired as below, row r ends with the totals of
-  // v = r Q .. r Q + Q - 1 (D = 64: in lanes 0..7 of the row, copies in 8..15).
-  constexpr int NV = G * 8;
-  constexpr int Q = NV / 4;
-  float xs[NV];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xs[h * 8 + i] = LPT == 16 ? acc[h][i] : acc[h][i] + dpp<kDppRor8>(acc[h][i]);
-  auto swap_add32 = [](float x, float y) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  };
-  auto swap_add16 = [](float x, float y) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  };
-  float tot[Q];
-#pragma unroll
-  for (int m = 0; m < Q; ++m) {
-    // pair 2m = (v m, v 2Q + m) and pair 2m + 1 = (v Q + m, v 3Q + m): after
-    // the 32-lane step each holds its first value in rows 0-1 and its second
-    // in rows 2-3; the 16-lane step then puts v m, Q + m, 2Q + m, 3Q + m in
-    // rows 0, 1, 2, 3
-    const float a_ = swap_add32(xs[m], xs[2 * Q + m]);
-    const float b_ = swap_add32(xs[Q + m], xs[3 * Q + m]);
-    tot[m] = swap_add16(a_, b_);
-  }
-  // l: the lanes of a head in a group (its tokens), then the rows
-  float lp[NSET];
-#pragma unroll
-  for (int j = 0; j < NSET; ++j) {
-    lp[j] = l_own[j] + dpp<kDppXor1>(l_own[j]);
-    if constexpr (TPL == 4) {
-      lp[j] += dpp<kDppXor2>(lp[j]);
-    } else {
-      lp[j] += dpp<kDppRor8>(lp[j]);
-    }
-    lp[j] = swap_add32(lp[j], lp[j]);
-    lp[j] = swap_add16(lp[j], lp[j]);
-  }
-  if (LPT == 16 || (lane & 8) == 0) {
-    if constexpr (Q % 8 == 0) {
-      // row r: heads r Q / 8 + c, 8 consecutive elements each
-#pragma unroll
-      for (int c = 0; c < Q / 8; ++c) {
-        const int h = row * (Q / 8) + c;
-        float* dst = &s_acc[wave][h][8 * li];
-        *reinterpret_cast<float4*>(dst) = make_float4(tot[8 * c], tot[8 * c + 1], tot[8 * c + 2], tot[8 * c + 3]);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(tot[8 * c + 4], tot[8 * c + 5], tot[8 * c + 6], tot[8 * c + 7]);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < Q; ++m) {
-        const int v = row * Q + m;
-        s_acc[wave][v >> 3][8 * li + (v & 7)] = tot[m];
-      }
-    }
-    if (row == 0 && my_u == 0) {
-#pragma unroll
-      for (int j = 0; j < NSET; ++j) {
-        const int h = 4 * j + my_h;
-        if (h < G) {
-          s_l[wave][h] = lp[j];
-          s_m[wave][h] = m_own[j];
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // Combine the waves: thread -> (head h, dim d) outputs.
-  for (int o = tid; o < G * D; o += 256) {
-    const int h = o / D, d = o % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, A = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][h];
-        const float e = mw == kNegInf ? 0.f : fast_exp2(mw - M);
-        L += s_l[w][h] * e;
-        A += s_acc[w][h][d] * e;
-      }
-    }
-    const int hq = g * G + h;
-    const int64_t orow = (int64_t)s * a.num_q_heads + hq;
-    const float val = L > 0.f ? A / L * a.v_scale : 0.f;
-    const float lse2 = L > 0.f ? M + fast_log2(L) : kNegInf;
-    if (nparts == 1) {
-      static_cast<uint16_t*>(a.out)[orow * D + d] = to_bf16(val);
-      if (a.lse && d == 0) a.lse[orow] = lse2 * kLn2;
-    } else {
-      a.ws_out[(orow * a.max_parts + part) * D + d] = val;
-      if (d == 0) a.ws_lse[orow * a.max_parts + part] = lse2;
-    }
-  }
-
-  // APP: the new token's K/V rows of this head into its slot, and (head 0)
-  // the new position's table entry and the length
-  if constexpr (APP) {
-    if (app_copy) {
-      const int c = lane % (D / 8);
-      const int64_t dst = (int64_t)app_blk * bstride + (app_slot & Bmask) * row_elems + g * D + 8 * c;
-      T* cache = const_cast<T*>(lane < D / 8 ? kcache : vcache);
-      *reinterpret_cast<uint4*>(cache + dst) = app_piece;
-      if (g == 0 && lane == 0) {
-        if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
-        a.wr_lens[s] = app_pos + 1;
-      }
-    }
-  }
+  decode_partition<D, G, BIG, F8, APP>(a, rows, blockIdx.x, blockIdx.y, (int)blockIdx.z);
 }
 
 // out[s, h] = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M) over the
@@ -816,6 +235,11 @@ int static_decode_scratch(void** ptr) {
   }
   *ptr = per_device[dev];
   return 0;
+}
+
+int launch_decode_merge(const DecodeArgs& a, void* stream) {
+  const hipStream_t st = (hipStream_t)stream;
+  return a.head_dim == 64 ? launch_merge<64>(a, st) : launch_merge<128>(a, st);
 }
 
 int launch_paged_decode(const DecodeArgs& a, void* stream) {

@@ -15,7 +15,8 @@
   cache write) bit-exact against the oracle scatter with nothing else
   changed, its prefill (sampled rows) and its decode (partitions of 2048,
   sampled sequences) against the oracle, and the step with the decode on a
-  second stream bitwise equal to the one-stream step.
+  second stream, and the step with the attention as one mixed-batch launch,
+  bitwise equal to the one-stream step.
 """
 
 import numpy as np
@@ -277,6 +278,15 @@ def test_mixed_step_writes_prefill_decode_and_two_streams(block_size):
     assert torch.equal(m.op.view(torch.int16), op.view(torch.int16))
     assert torch.equal(m.od.view(torch.int16), od.view(torch.int16))
     assert torch.equal(m.lsed, lsed)
+    assert torch.equal(h.kc.view(torch.int16), kc1.view(torch.int16))
+    # (5) the step's attention as one mixed batch (pa_paged_attention, decode
+    # rows first): the same bits as the separate prefill and decode calls
+    m.ov.zero_()
+    m.step_varlen()
+    torch.cuda.synchronize()
+    nd = len(m.dec)
+    assert torch.equal(m.ov[:nd].view(torch.int16), od.view(torch.int16))
+    assert torch.equal(m.ov[nd:].view(torch.int16), op.view(torch.int16))
     assert torch.equal(h.kc.view(torch.int16), kc1.view(torch.int16))
     del kc1
     m.close()
