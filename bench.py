@@ -61,7 +61,7 @@ PLAIN_KERNEL = "decode_partition_kernel<128, 4, true, false, false>"
 MERGE_KERNEL = "decode_merge_kernel<128>"
 # head_dim, query heads per work-group, causal, block size >= 16, E4M3 caches, 32-bit key offsets
 PREFILL_KERNEL = "prefill_kernel<128, 4, true, true, false, false>"
-HEADLINE_PARTITION = 2048
+HEADLINE_PARTITION = 1024
 COUNTERS = {
     "long_context": os.path.join(ROOT, "profiles", "decode_append_long_context_traffic.txt"),
     "decode": os.path.join(ROOT, "profiles", "decode_append_llama3_8b_traffic.txt"),

@@ -11,8 +11,9 @@
  * Conventions
  *   - Every call returns int status: PA_OK, PA_ERR_INVALID (bad argument, shape,
  *     pointer, id or duplicate), PA_ERR_NO_SPACE (the pool cannot supply the
- *     blocks: the allocate-returns-None case of the slot-allocation section) or
- *     PA_ERR_HIP (a HIP launch failed).  pa_last_error() describes the most
+ *     blocks: the allocate-returns-None case of the slot-allocation section),
+ *     PA_ERR_HIP (a HIP launch failed) or PA_ERR_NO_MEMORY (the pool could
+ *     not allocate host memory for its own bookkeeping; the pool is unchanged).  pa_last_error() describes the most
  *     recent failure on the calling thread.
  *   - Pool calls are all-or-nothing: on any error the pool is unchanged (CPU
  *     reference allocator section: a failed allocation leaves the sequence
@@ -62,7 +63,8 @@ enum {
   PA_OK = 0,
   PA_ERR_INVALID = -1,
   PA_ERR_NO_SPACE = -2,
-  PA_ERR_HIP = -3
+  PA_ERR_HIP = -3,
+  PA_ERR_NO_MEMORY = -4
 };
 
 /* Text of the most recent error on this thread ("" if none).  The pointer
@@ -169,9 +171,9 @@ int pa_pool_append_batch(pa_pool* pool, const int64_t* seq_ids, const int32_t* n
  * and the hashed ones to its tail (reused last, still matchable by a prefix
  * lookup until popped).
  * ("PagedAttention: fragmentation, blocks, block tables", 1. The block pool:
- * free_blocks takes blocks ordered by eviction priority, first evicted first;
- * non-cached blocks go to the front, cached ones to the back; a request frees
- * its blocks in reverse.)
+ * free_blocks receives the blocks in the order they should be reused,
+ * puts uncached ones at the front of the queue and cached ones at the back,
+ * and a request hands in its blocks tail first.)
  * Errors: PA_ERR_INVALID if seq_id is unknown. */
 int pa_pool_free_seq(pa_pool* pool, int64_t seq_id);
 
@@ -215,8 +217,9 @@ int pa_pool_block_table(const pa_pool* pool, const int64_t* seq_ids, int32_t n_s
  * ceil(len_i / block_size) * k entries; slots are unchanged by the view.
  * ("PagedAttention: fragmentation, blocks, block tables", the block-table
  * append with hybrid blocks, and the paragraph on decoupling the allocation
- * block from the kernel block: a 32-token allocation block can feed a kernel
- * that wants 16-token pages.)
+ * block from the kernel block: the allocator's block size and the one an
+ * attention kernel is tuned for need not be equal when the first is a
+ * multiple of the second.)
  * Errors: PA_ERR_INVALID if kernel_block_size does not divide block_size, a
  * row does not fit bt_stride, num_blocks * k exceeds INT32_MAX or a sequence
  * is unknown (nothing written). */
@@ -375,6 +378,19 @@ int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes,
                    int64_t cache_block_stride_bytes, int32_t num_blocks,
                    const int32_t* pairs, int32_t n_pairs, void* stream);
 
+/* pa_copy_blocks with the pairs in device memory, for launches captured once
+ * and replayed with new pairs (a HIP graph): pairs is a device int32
+ * [n_pairs][2] (src, dst) array read by the kernel; a pair with an id outside
+ * [0, num_blocks) is skipped, so -1 pads a list to a fixed n_pairs.  The
+ * pairs cannot be checked on the host: a destination named twice, or a
+ * destination that is also a source, gives an unspecified result (every
+ * access still stays inside the listed caches).  Every byte of each block is
+ * copied, as by pa_copy_blocks.  Errors: PA_ERR_INVALID for NULL or
+ * unaligned pointers and bad sizes (as pa_copy_blocks). */
+int pa_copy_blocks_device(void* const* caches, int32_t n_caches, int64_t block_bytes,
+                          int64_t cache_block_stride_bytes, int32_t num_blocks,
+                          const int32_t* pairs, int32_t n_pairs, void* stream);
+
 /* Bytes of workspace pa_paged_decode needs (0 when one partition covers
  * max_seq_len, i.e. no split). */
 size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -394,9 +410,12 @@ size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * log-sum-exp identity.)
  * q, out: device bf16 [num_seqs][num_q_heads][head_dim], contiguous.
  * lse: device fp32 [num_seqs][num_q_heads] or NULL.
- * seq_lens: device int32 [num_seqs]; each must be <= max_seq_len (longer
- * sequences are truncated to max_seq_len); a length of 0 yields out = 0 and
- * lse = -inf.  ceil(max_seq_len / B) must not exceed bt_stride.
+ * seq_lens: device int32 [num_seqs]; each must be <= max_seq_len.  The
+ * lengths live on the device, so the call cannot check them: a longer
+ * sequence is attended over its first max_seq_len tokens only (and a
+ * negative length counts as 0), which keeps every read inside the table and
+ * the cache but is a wrong answer for that row.  A length of 0 yields out = 0
+ * and lse = -inf.  ceil(max_seq_len / B) must not exceed bt_stride.
  * partition_size: 0 = one partition per sequence; otherwise a multiple of 64
  * and of block_size.  workspace: device buffer of at least
  * pa_paged_decode_workspace_size(...) bytes (may be NULL when that is 0),
@@ -492,7 +511,13 @@ int pa_paged_decode_fp8(void* out, float* lse, const void* q,
  * total_q = query_start_loc[num_seqs].  query_start_loc: device int32
  * [num_seqs + 1], non-decreasing, starting at 0; seq_lens: device int32
  * [num_seqs] with q_i <= seq_lens[i] <= max_seq_len; max_query_len bounds
- * every q_i.  ceil(max_seq_len / B) must not exceed bt_stride.
+ * every q_i.  ceil(max_seq_len / B) must not exceed bt_stride.  These
+ * device arrays cannot be checked by the call; when they break the bounds,
+ * no read leaves the table or the cache, but rows go unwritten: the queries
+ * of a request past its first max_query_len, and every query of a request
+ * with q_i > seq_lens[i] (lengths above max_seq_len are cut to it first).
+ * pa_paged_attention, which also takes the host copy of query_start_loc,
+ * rejects a q_i above max_query_len.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; softmax weights are
  * rounded to bf16 before the PV product. */
 int pa_paged_prefill(void* out, const void* q,

@@ -12,9 +12,9 @@ Sources
     counts the computed tokens; query_start_loc delimits each request's
     queries) and the VM-analogy paragraph (a straight gather, lookup per
     query).
-  * "The pantry of pigeonholes", "The mechanism": the kernel walks a
-    sequence's physical blocks in logical order and reads K and V as if
-    they were contiguous.
+  * "The pantry of pigeonholes", "The mechanism": the attention kernel
+    visits a sequence's physical blocks in logical order, so the gathered
+    K and V behave like one contiguous sequence.
   * "Memory management", Concept: the kernel follows the block table to
     gather keys and values.
 

@@ -78,8 +78,8 @@ def map_to_kernel_blocks(block_ids, blocks_per_alloc: int) -> np.ndarray:
     "PagedAttention: fragmentation, blocks, block tables", the block-table
     append (the hybrid-blocks branch) and the decoupling paragraph: an
     allocation block of B_alloc tokens is split into k = B_alloc / B_kernel
-    kernel blocks, so a 32-token allocation block can feed a kernel that
-    wants 16-token pages.  Reading: allocation block b is the same memory as
+    kernel blocks, so the allocator and the attention kernel may use
+    different block sizes.  Reading: allocation block b is the same memory as
     kernel blocks b*k .. b*k + k - 1 of the cache viewed with B_kernel-token
     blocks, and every allocation id of a row expands, in order, to its k
     kernel ids (so a row of n ids becomes n*k ids).

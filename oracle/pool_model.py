@@ -9,9 +9,9 @@ Sources
         free queue), get_new_blocks (pop from the head, ref 0 -> 1, an
         error when more blocks are asked for than are free) and
         free_blocks (ref -= 1; a block reaching zero goes back to the
-        *front* of the queue; the list is ordered by eviction priority,
-        first evicted first, and a request frees its blocks in reverse so
-        the tail of the sequence is reused first).
+        *front* of the queue; the blocks handed in are ordered so that the
+        one to be reused soonest comes first, and a request hands in its
+        blocks tail first, so its tail block is the next one reused).
       - 2. The block table: position p lives in block table[p // B] at
         offset p % B.
       - 3. The slot mapping: slot = table[p // B] * B + p % B.

@@ -13,7 +13,7 @@ import re
 
 import numpy as np
 
-PA_OK, PA_ERR_INVALID, PA_ERR_NO_SPACE, PA_ERR_HIP = 0, -1, -2, -3
+PA_OK, PA_ERR_INVALID, PA_ERR_NO_SPACE, PA_ERR_HIP, PA_ERR_NO_MEMORY = 0, -1, -2, -3, -4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
@@ -38,7 +38,11 @@ class HipError(PagedAttnError):
     pass
 
 
-_ERRORS = {PA_ERR_INVALID: InvalidArgument, PA_ERR_NO_SPACE: NoSpace, PA_ERR_HIP: HipError}
+class NoMemory(PagedAttnError):
+    pass
+
+
+_ERRORS = {PA_ERR_INVALID: InvalidArgument, PA_ERR_NO_SPACE: NoSpace, PA_ERR_HIP: HipError, PA_ERR_NO_MEMORY: NoMemory}
 
 c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_i32, P_i64 = ctypes.POINTER(c_i32), ctypes.POINTER(c_i64)
@@ -75,6 +79,7 @@ _SIGS = {
                                          c_i32, c_i32, c_i32, c_i32, c_f32, c_f32, c_vp]),
     "pa_decode_append": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp, P_i64,
                                  P_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pa_copy_blocks_device": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp]),
     "pa_copy_blocks": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i64, c_i64, c_i32, P_i32, c_i32, c_vp]),
     "pa_paged_decode_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_paged_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_i32, c_vp,
@@ -336,6 +341,18 @@ def _bf16(t, name):
         raise InvalidArgument(PA_ERR_INVALID, f"{name} must be a bf16 device tensor")
 
 
+def _scratch(nbytes, device, stream):
+    """A workspace allocated here for a launch on `stream`: marked as used on
+    that stream, so the caching allocator does not hand its memory to other
+    work before the launch's kernels have finished with it."""
+    import torch
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+        ws.record_stream(s)
+    return ws
+
+
 def _cache_geometry(kc, vc, fp8=False):
     """[NB, B, Hkv, D] views whose inner three dims are contiguous (bf16, or
     one-byte E4M3 codes as uint8 / float8_e4m3fn with fp8); returns
@@ -461,6 +478,27 @@ def pa_copy_blocks(caches, pairs, stream=None):
                                 _stream(c0, stream)))
 
 
+def pa_copy_blocks_device(caches, pairs, stream=None):
+    """caches: list of device tensors whose dim 0 indexes blocks; pairs: a
+    device int32 tensor [n, 2] (src, dst), ids outside the pool skipped."""
+    import torch
+    if not caches:
+        return
+    c0 = caches[0]
+    for c in caches:
+        if c.shape != c0.shape or c.stride() != c0.stride() or c.dtype != c0.dtype or not c.is_cuda:
+            raise InvalidArgument(PA_ERR_INVALID, "caches must share shape, strides and dtype")
+        if not c[0].is_contiguous():
+            raise InvalidArgument(PA_ERR_INVALID, "each block of a cache must be contiguous")
+    if pairs.dtype != torch.int32 or not pairs.is_cuda or pairs.dim() != 2 or pairs.shape[1] != 2 \
+            or not pairs.is_contiguous():
+        raise InvalidArgument(PA_ERR_INVALID, "pairs must be a contiguous device int32 [n, 2] tensor")
+    ptrs = (c_vp * len(caches))(*[c.data_ptr() for c in caches])
+    _check(lib().pa_copy_blocks_device(ptrs, len(caches), c0[0].numel() * c0.element_size(),
+                                       c0.stride(0) * c0.element_size(), c0.shape[0], pairs.data_ptr(),
+                                       pairs.shape[0], _stream(c0, stream)))
+
+
 def pa_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size):
     return lib().pa_paged_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
 
@@ -533,7 +571,7 @@ def _decode(out, q, key_cache, value_cache, block_tables, seq_lens, max_seq_len,
         return
     need = pa_paged_decode_workspace_size(S, hq, d, max_seq_len, partition_size)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if append is not None:
@@ -620,7 +658,7 @@ def pa_paged_attention(out, q, key_cache, value_cache, block_tables, query_start
         raise InvalidArgument(PA_ERR_INVALID, "block_tables must be int32 [S, W] with unit column stride")
     need = lib().pa_paged_attention_workspace_size(_i32p(qsl_h), S, hq, d, max_seq_len, partition_size)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().pa_paged_attention(out.data_ptr(), q.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), bstride,

@@ -203,6 +203,24 @@ int pa_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes, i
   return hip_status(fn, pa::launch_copy_blocks(caches, n_caches, block_bytes, stride_bytes, pairs, n_pairs, stream));
 }
 
+int pa_copy_blocks_device(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
+                          int32_t num_blocks, const int32_t* pairs, int32_t n_pairs, void* stream) {
+  pa::clear_error();
+  const char* fn = "copy_blocks_device";
+  if (n_pairs < 0 || n_caches < 0) return pa::fail(PA_ERR_INVALID, "%s: negative count", fn);
+  if (n_pairs == 0 || n_caches == 0) return PA_OK;
+  if (!caches || !pairs) return pa::fail(PA_ERR_INVALID, "%s: NULL argument", fn);
+  if (!aligned(pairs, 4)) return pa::fail(PA_ERR_INVALID, "%s: pairs must be 4-byte aligned", fn);
+  if (block_bytes <= 0 || block_bytes % 16 || stride_bytes < block_bytes || stride_bytes % 16)
+    return pa::fail(PA_ERR_INVALID, "%s: block_bytes %lld must be a positive multiple of 16 <= stride %lld", fn,
+                    (long long)block_bytes, (long long)stride_bytes);
+  if (num_blocks <= 0) return pa::fail(PA_ERR_INVALID, "%s: num_blocks must be positive", fn);
+  for (int32_t c = 0; c < n_caches; ++c)
+    if (!caches[c] || !aligned(caches[c], 16)) return pa::fail(PA_ERR_INVALID, "%s: cache %d NULL or unaligned", fn, c);
+  return hip_status(fn, pa::launch_copy_blocks_device(caches, n_caches, block_bytes, stride_bytes, num_blocks, pairs,
+                                                      n_pairs, stream));
+}
+
 size_t pa_paged_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
                                       int32_t partition_size) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 || partition_size <= 0) return 0;

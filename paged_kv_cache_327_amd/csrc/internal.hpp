@@ -67,6 +67,10 @@ int launch_slot_mapping(const SlotArgs& a, void* stream);
 int launch_copy_blocks(void* const* caches, int32_t n_caches, int64_t block_bytes,
                        int64_t stride_bytes, const int32_t* pairs, int32_t n_pairs,
                        void* stream);
+// pairs: device int32 [n_pairs][2]; pairs with an id outside [0, num_blocks)
+// are skipped
+int launch_copy_blocks_device(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
+                              int32_t num_blocks, const int32_t* pairs, int32_t n_pairs, void* stream);
 
 // The fields the decode prologue's first loads need come first, so that the
 // kernel reads them with its first argument loads.

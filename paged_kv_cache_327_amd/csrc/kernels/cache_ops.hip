@@ -196,7 +196,62 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(CopyBatch b) {
   }
 }
 
+// The same copy with the pairs read from device memory (so a captured launch
+// can take new pairs on every replay): pair `pair` of the array, skipped when
+// either id lies outside [0, num_blocks) -- -1 pads a list to a fixed count.
+struct CopyDevBatch {
+  char* caches[kMaxCopyCaches];
+  const int32_t* pairs;
+  int32_t num_blocks;
+  int64_t block_bytes;
+  int64_t stride_bytes;
+};
+
+__global__ void __launch_bounds__(256) copy_blocks_dev_kernel(CopyDevBatch b, int32_t pair0) {
+  const int pair = pair0 + blockIdx.y, cache = blockIdx.z;
+  const int32_t src = b.pairs[2 * pair], dst = b.pairs[2 * pair + 1];
+  if (src < 0 || src >= b.num_blocks || dst < 0 || dst >= b.num_blocks) return;
+  const uint4* s = reinterpret_cast<const uint4*>(b.caches[cache] + (int64_t)src * b.stride_bytes);
+  uint4* d = reinterpret_cast<uint4*>(b.caches[cache] + (int64_t)dst * b.stride_bytes);
+  const int64_t nvec = b.block_bytes >> 4;
+  const int64_t base = (int64_t)blockIdx.x * (256 * kCopyUnroll) + threadIdx.x;
+  uint4 v[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < nvec) v[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < nvec) d[i] = v[u];
+  }
+}
+
 }  // namespace
+
+int launch_copy_blocks_device(void* const* caches, int32_t n_caches, int64_t block_bytes, int64_t stride_bytes,
+                              int32_t num_blocks, const int32_t* pairs, int32_t n_pairs, void* stream) {
+  const int64_t nvec = block_bytes >> 4;
+  const unsigned chunks = (unsigned)((nvec + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll));
+  for (int32_t c0 = 0; c0 < n_caches; c0 += kMaxCopyCaches) {
+    const int32_t nc = n_caches - c0 < kMaxCopyCaches ? n_caches - c0 : kMaxCopyCaches;
+    CopyDevBatch b{};
+    for (int32_t i = 0; i < nc; ++i) b.caches[i] = static_cast<char*>(caches[c0 + i]);
+    b.pairs = pairs;
+    b.num_blocks = num_blocks;
+    b.block_bytes = block_bytes;
+    b.stride_bytes = stride_bytes;
+    for (int32_t p0 = 0; p0 < n_pairs; p0 += 65535) {
+      const int32_t np = n_pairs - p0 < 65535 ? n_pairs - p0 : 65535;
+      hipLaunchKernelGGL(copy_blocks_dev_kernel, dim3(chunks, (unsigned)np, (unsigned)nc), dim3(256), 0,
+                         (hipStream_t)stream, b, p0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return (int)e;
+    }
+  }
+  return 0;
+}
 
 int launch_reshape_and_cache(const ReshapeArgs& a, void* stream) {
   const unsigned grid = (unsigned)((a.num_tokens + 3) / 4);

@@ -5,9 +5,9 @@
 // attention-metadata section; "The pantry of pigeonholes", "The mechanism"):
 // for sequence s, the kernel walks row s of the block table in logical order
 // for ceil(seq_lens[s] / B) entries and attends one query per head over the
-// gathered K/V.  The split into partitions is named on the first page
-// ("the tiling, the split-K, the paged gather") without detail; the design
-// below is ours.
+// gathered K/V.  The first page names splitting a sequence's keys across
+// work-groups (split-K) among the kernel's concerns but gives no design; the
+// design below is ours.
 //
 // Partition pass: one work-group (4 waves) per (partition, KV head g, seq s).
 //  * A token's K (or V) row of head g is held by D / 8 lanes, 8 elements

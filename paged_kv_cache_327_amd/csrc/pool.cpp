@@ -157,7 +157,7 @@ int append_one(pa_pool* p, int64_t seq_id, int32_t n, int64_t* slots, int32_t* p
     s.blocks.reserve(s.blocks.size() + (size_t)needed);
     if (cow) p->pending.reserve(p->pending.size() + 1);
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "append: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "append: out of host memory");
   }
   pair[0] = -1;
   pair[1] = -1;
@@ -198,7 +198,7 @@ int pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
     return pa::fail(PA_ERR_INVALID, "pool_create: num_blocks (%d) and block_size (%d) must be positive",
                     num_blocks, block_size);
   pa_pool* p = new (std::nothrow) pa_pool();
-  if (!p) return pa::fail(PA_ERR_INVALID, "pool_create: out of host memory");
+  if (!p) return pa::fail(PA_ERR_NO_MEMORY, "pool_create: out of host memory");
   const size_t N = (size_t)num_blocks;
   try {
     p->prev.assign(N, -1);
@@ -211,7 +211,7 @@ int pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* order,
     p->hash.assign(N, 0);
   } catch (const std::bad_alloc&) {
     delete p;
-    return pa::fail(PA_ERR_INVALID, "pool_create: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "pool_create: out of host memory");
   }
   p->num_blocks = num_blocks;
   p->block_size = block_size;
@@ -242,7 +242,7 @@ int pa_pool_add_seq(pa_pool* p, int64_t seq_id) {
   try {
     p->seqs.emplace(seq_id, pa_pool::Seq());
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "add_seq: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "add_seq: out of host memory");
   }
   return PA_OK;
 }
@@ -271,7 +271,7 @@ int pa_pool_add_seq_cached(pa_pool* p, int64_t seq_id, const int32_t* tokens, in
     s.len = (int64_t)hits.size() * B;
     p->seqs.emplace(seq_id, std::move(s));
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "add_seq_cached: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "add_seq_cached: out of host memory");
   }
   for (int32_t b : hits) p->touch(b);
   *hit_tokens = (int64_t)hits.size() * B;
@@ -294,7 +294,7 @@ int pa_pool_cache_blocks(pa_pool* p, int64_t seq_id, const int32_t* tokens, int6
     chain.reserve((size_t)(n_tokens / B));
     p->cached.reserve(p->cached.size() + (size_t)(n_tokens / B));
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "cache_blocks: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "cache_blocks: out of host memory");
   }
   uint64_t h = 0;
   for (int64_t j = 0; (j + 1) * B <= n_tokens; ++j) {
@@ -325,7 +325,7 @@ int pa_pool_fork(pa_pool* p, int64_t src_seq, int64_t dst_seq) {
     pa_pool::Seq copy = it->second;
     p->seqs.emplace(dst_seq, std::move(copy));
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "fork: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "fork: out of host memory");
   }
   for (int32_t b : p->seqs[dst_seq].blocks) p->ref[(size_t)b] += 1;
   return PA_OK;
@@ -364,7 +364,7 @@ int pa_pool_free_seq(pa_pool* p, int64_t seq_id) {
   try {
     released.reserve(blocks.size());
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "free_seq: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "free_seq: out of host memory");
   }
   for (auto b = blocks.rbegin(); b != blocks.rend(); ++b) {
     p->ref[(size_t)*b] -= 1;
@@ -390,7 +390,7 @@ int pa_pool_pin(pa_pool* p, int64_t seq_id, int64_t transfer_id, int32_t* blocks
   try {
     p->transfers.emplace(transfer_id, blocks);
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "pin: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "pin: out of host memory");
   }
   for (size_t i = 0; i < blocks.size(); ++i) {
     p->pins[(size_t)blocks[i]] += 1;
@@ -409,7 +409,7 @@ int pa_pool_unpin(pa_pool* p, int64_t transfer_id) {
   try {
     released.reserve(it->second.size());
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "unpin: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "unpin: out of host memory");
   }
   for (auto b = it->second.rbegin(); b != it->second.rend(); ++b) {
     p->pins[(size_t)*b] -= 1;
@@ -427,7 +427,7 @@ int pa_pool_copies_done(pa_pool* p) {
   try {
     released.reserve(2 * p->pending.size());
   } catch (const std::bad_alloc&) {
-    return pa::fail(PA_ERR_INVALID, "copies_done: out of host memory");
+    return pa::fail(PA_ERR_NO_MEMORY, "copies_done: out of host memory");
   }
   for (const auto& sd : p->pending)
     for (int32_t b : {sd.first, sd.second}) {

@@ -1,12 +1,12 @@
 """GPU parity of the exact steps bench.py times, against the fp64 oracle.
 
 * The headline: the 32-layer long-context step (host pool append, then one
-  pa_paged_decode_append call per layer with partitions of 2048 tokens and
+  pa_paged_decode_append call per layer with bench.py's partition size and
   the merge) over consecutive steps -- outputs and lse of every sequence of
   layers 0 and 31 (and sampled sequences of other layers), the device block
   tables and lengths against the host pool, and the step's cache writes bit
   for bit against the oracle's scatter; plain decode of the same pool at
-  partitions of 512 and 2048 tokens.
+  partitions of 512, 1024 and 2048 tokens.
 * The Llama-3-8B batch of 64 (512 + U{0..100} tokens): bench.py's appending
   step (one partition per sequence) over consecutive steps, every output
   row and lse after each step, tables and lengths against the pool, and the
@@ -82,7 +82,8 @@ class LongContext:
 
     def __init__(self):
         print("[bench steps] 32-layer long-context pool set-up", flush=True)
-        self.st = bench.LongContextStep(torch, B, hip_side, workloads, partition_size=2048, max_steps=8, lse=True)
+        self.st = bench.LongContextStep(torch, B, hip_side, workloads, partition_size=bench.HEADLINE_PARTITION,
+                                        max_steps=8, lse=True)
         self.wl = self.st.wl
         self.ctx = {}
         self.rows_k, self.rows_v = [], []       # per step: [L, S, Hkv, D] bits
@@ -109,13 +110,13 @@ def lc():
     del c
 
 
-def test_long_context_plain_decode_at_512_and_2048(lc):
+def test_long_context_plain_decode_at_512_1024_2048(lc):
     """Plain decode of the 52.3 GiB pool, layers 0 and 31, all 8 sequences,
-    split into partitions of 512 and of 2048 tokens (32-64 and 8-16
-    partitions per sequence) and merged."""
+    split into partitions of 512, 1024 and 2048 tokens (32-64, 16-32 and
+    8-16 partitions per sequence) and merged."""
     st, wl = lc.st, lc.wl
     S = st.S
-    for P in (512, 2048):
+    for P in (512, 1024, 2048):
         ws = torch.empty(B.pa_paged_decode_workspace_size(S, 32, 128, st.max_seq_len, P), dtype=torch.uint8,
                          device="cuda")
         for l in lc.CHECK:

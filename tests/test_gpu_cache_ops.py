@@ -156,3 +156,24 @@ def test_slot_mapping_with_more_requests_than_staged():
     assert np.array_equal(got, want)
     assert (got >= 0).sum() > 1000
 
+
+def test_copy_blocks_with_device_pairs_and_padding():
+    """pa_copy_blocks_device: the pairs are read on the device; pairs padded
+    with -1, or naming a block past the pool, are skipped; the rest copy
+    every byte, bit-exact against the oracle's copy of the valid pairs, over
+    two calls with different pairs."""
+    nb, row = 40, 4 * 2 * 64
+    rng = np.random.default_rng(12)
+    host = [rng.integers(0, 2**16, size=(nb, row), dtype=np.uint16) for _ in range(3)]
+    dev = [torch.from_numpy(h.view(np.int16)).cuda() for h in host]
+    for rnd in range(2):
+        perm = rng.permutation(nb)
+        valid = np.stack([perm[:6], perm[6:12]], axis=1)
+        pairs = np.concatenate([valid, [[-1, -1], [3, nb], [nb + 5, 2]]]).astype(np.int32)
+        dp = torch.from_numpy(pairs).cuda()
+        B.pa_copy_blocks_device(dev, dp)
+        for h in host:
+            cache_ops.copy_blocks([h], valid.tolist(), nb)
+        torch.cuda.synchronize()
+        for h, t in zip(host, dev):
+            assert np.array_equal(t.cpu().numpy().view(np.uint16), h), rnd
