@@ -56,18 +56,23 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s; prefill TFLOP/s"
 # template arguments: head_dim, query heads per KV head, block size >= 16, E4M3 caches, appending
-APPEND_KERNEL = "decode_partition_kernel<128, 4, true, false, true>"
-PLAIN_KERNEL = "decode_partition_kernel<128, 4, true, false, false>"
+# the long-context step's appending decode (row layout: explicit partitions
+# of up to 1024 tokens) and the Llama batch's (head layout: one partition
+# per sequence)
+APPEND_KERNEL = "decode_rows_kernel<4, true, true>"
+LLAMA_APPEND_KERNEL = "decode_partition_kernel<128, 4, true, false, true>"
+LLAMA_PLAIN_KERNEL = "decode_partition_kernel<128, 4, true, false, false>"
 MERGE_KERNEL = "decode_merge_kernel<128>"
 # head_dim, query heads per work-group, causal, block size >= 16, E4M3 caches, 32-bit key offsets
 PREFILL_KERNEL = "prefill_kernel<128, 4, true, true, false, false>"
-HEADLINE_PARTITION = 1024
+HEADLINE_PARTITION = 512
 COUNTERS = {
     "long_context": os.path.join(ROOT, "profiles", "decode_append_long_context_traffic.txt"),
     "decode": os.path.join(ROOT, "profiles", "decode_append_llama3_8b_traffic.txt"),
 }
 COPY_CALIBRATION_BYTES = 512 << 20
 DECODE_SOURCES = ("paged_kv_cache_327_amd/csrc/kernels/paged_decode.hip",
+                  "paged_kv_cache_327_amd/csrc/kernels/decode_body.hpp",
                   "paged_kv_cache_327_amd/csrc/kernels/common.hpp",
                   "paged_kv_cache_327_amd/csrc/internal.hpp",
                   "paged_kv_cache_327_amd/csrc/api.cpp",
@@ -586,11 +591,11 @@ def measure_llama_decode(torch, B, hip_side, workloads, steps=40, warmup=4, inst
                        f"8192-block pools, {instances} pools used in turn",
            "steps": steps, "ms_per_step": round(ms, 4), "step_gbps": round(kv / ms / 1e6, 1),
            "step_hbm_frac": hbm(kv / ms / 1e6), "seqs_per_s": round(S / ms * 1e3, 1),
-           "roofline": {"bound": "hbm", "kernel": APPEND_KERNEL, "achieved": round(alg / t_app / 1e9, 2),
+           "roofline": {"bound": "hbm", "kernel": LLAMA_APPEND_KERNEL, "achieved": round(alg / t_app / 1e9, 2),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm(alg / t_app / 1e9),
                         "traffic": traffic_from_counters("decode"), "algorithmic_bytes_per_launch": int(alg),
                         "launch_us": round(t_app * 1e6, 2)},
-           "plain_kernel": {"kernel": PLAIN_KERNEL, "us": round(t_plain * 1e6, 2),
+           "plain_kernel": {"kernel": LLAMA_PLAIN_KERNEL, "us": round(t_plain * 1e6, 2),
                             "gbps": round(alg / t_plain / 1e9, 1), "hbm_frac": hbm(alg / t_plain / 1e9),
                             "seqs_per_s": round(S / t_plain, 1)},
            "reshape_64_tokens_us": round(t_w * 1e6, 2)}
@@ -653,10 +658,11 @@ def measure_tiny(torch, B, hip_side, workloads, reps=200):
     return {"workload": "4 sequences of 1, 17, 33, 100 tokens, 8/2 heads, d 64, B 16", "decode_us": round(sec * 1e6, 2)}
 
 
-def measure_long_context_partitions(torch, B, hip_side, workloads, sizes=(512, 2048), reps=3):
+def measure_long_context_partitions(torch, B, hip_side, workloads, sizes=(256, 1024, 2048), reps=3):
     """Plain decode over the 32-layer pool (no token write) at several
-    partition sizes: every layer with its own queries, per layer and per
-    32-layer pass."""
+    partition sizes (up to 1024 tokens the row layout, above it the head
+    layout): every layer with its own queries, per layer and per 32-layer
+    pass."""
     st = LongContextStep(torch, B, hip_side, workloads, sizes[0], max_steps=2)
     wl = st.wl
     L, S = st.L, st.S
@@ -673,7 +679,8 @@ def measure_long_context_partitions(torch, B, hip_side, workloads, sizes=(512, 2
                 B.pa_paged_decode(st.out[l], st.q[0, l], st.kv[l, 0], st.kv[l, 1], st.h.table_dev,
                                   st.h.seq_lens_dev, msl, wl.scale, partition_size=P, workspace=ws)
         sec = time_launches(torch, one_pass, reps)
-        res[f"plain_p{P}"] = {"pass_ms": round(sec * 1e3, 3), "layer_us": round(sec / L * 1e6, 1),
+        res[f"plain_p{P}"] = {"layout": "rows" if P <= 1024 else "heads",
+                              "pass_ms": round(sec * 1e3, 3), "layer_us": round(sec / L * 1e6, 1),
                               "gbps": round(per_layer * L / sec / 1e9, 1),
                               "hbm_frac": hbm(per_layer * L / sec / 1e9), "seqs_per_s": round(S / sec, 1)}
         del ws
@@ -1117,8 +1124,9 @@ def counter_summary(kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
     ff, wf = kib / copy_f, kib / copy_w
     fr, wr = _read_counter_csv(fetch_dir), _read_counter_csv(write_dir)
     # every appending launch of the run (their bytes differ by one token)
-    f_app, n_app = _kernel_avg(fr, "decode_partition_kernel", "true>(")
-    w_app, _ = _kernel_avg(wr, "decode_partition_kernel", "true>(")
+    kernel = APPEND_KERNEL if kind == "long_context" else LLAMA_APPEND_KERNEL
+    f_app, n_app = _kernel_avg(fr, kernel + "(")
+    w_app, _ = _kernel_avg(wr, kernel + "(")
     f_mrg, n_mrg = _kernel_avg(fr, "decode_merge") if any("decode_merge" in k for k in fr) else (0.0, 0)
     w_mrg, _ = _kernel_avg(wr, "decode_merge") if any("decode_merge" in k for k in wr) else (0.0, 0)
     per_launch = (f_app + f_mrg) * 1024 * ff + (w_app + w_mrg) * 1024 * wf
@@ -1126,7 +1134,7 @@ def counter_summary(kind, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, 
             "decode": "the Llama-3-8B batch of 64 (appending decode launch)"}[kind]
     lines = [
         f"# HBM traffic of {name}",
-        f"# kernels: {APPEND_KERNEL}" + (f" and {MERGE_KERNEL}" if n_mrg else ""),
+        f"# kernels: {kernel}" + (f" and {MERGE_KERNEL}" if n_mrg else ""),
         "#",
         "# Commands (from /tmp, TMPDIR=/tmp), one counter per run:",
         *[f"#   {c}" for c in command.split(" ;; ")],

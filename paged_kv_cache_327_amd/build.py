@@ -66,6 +66,8 @@ def _budget(name, targs):
         return (256, 0, 0 if (d == 64 or big) else 32, 2)
     if name == "decode_partition_kernel":
         return (512, 0, 0, 3) if targs[1] <= 4 else (512, 0, 0, 2)
+    if name == "decode_rows_kernel":
+        return 512, 0, 0, 2
     return 512, 256, 0, 1
 
 

@@ -320,6 +320,12 @@ int make_decode_args(const char* fn, void* out, float* lse, const void* q, const
   a.scale = fp8 ? scale * k_scale : scale;
   a.v_scale = fp8 ? v_scale : 1.f;
   a.fp8 = fp8 ? 1 : 0;
+  // Explicit partitions of up to 1024 tokens over bf16 caches with
+  // head_dim 128 and a multiple of 4 KV heads take the row layout, whose
+  // waves read whole token rows of 4 heads; the rest the head layout.
+  a.rows = (!fp8 && head_dim == 128 && num_kv_heads % 4 == 0 && partition_size > 0 && partition_size <= 1024)
+               ? 1
+               : 0;
   if (parts > 1) {
     const int64_t rows = (int64_t)num_seqs * num_q_heads * parts;
     a.ws_out = static_cast<float*>(workspace);

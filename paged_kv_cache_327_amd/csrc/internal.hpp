@@ -93,6 +93,7 @@ struct DecodeArgs {
   float scale;     // softmax scale (times k_scale for E4M3 caches)
   float v_scale;   // 1 for bf16 caches
   int32_t fp8;     // caches hold E4M3 codes (1 byte per element)
+  int32_t rows;    // row layout: a wave per (4 KV heads, partition, sequence)
   float* ws_out;  // [S][Hq][max_parts][D]   (max_parts > 1 only)
   float* ws_lse;  // [S][Hq][max_parts]
   // appending decode only: the new tokens' K/V rows and the writable tables

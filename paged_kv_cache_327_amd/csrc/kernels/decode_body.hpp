@@ -15,6 +15,8 @@ constexpr int kHalf = 16;     // tokens of a half tile, inside one block when B 
 constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
 constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1)
 constexpr int kChunk = 512;   // tokens whose table entries are staged at once (B < 16)
+template <int G>
+constexpr int kRowBuffers = G <= 4 ? 3 : 2;   // row layout: steps in flight + 1
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
@@ -119,6 +121,121 @@ __device__ __forceinline__ void broadcast_pairs(uint32_t x, int li, uint32_t (&o
   }
 }
 
+// One half tile of a lane: TPL tokens whose K and V pieces are
+// r.k / r.v [base + u] (u < TPL); valid: the token of this lane's score lies
+// inside the range.  Scores of the lane group's 4 heads x TPL tokens are
+// reduce-scattered, one per lane; the running maxima are raised on a rare
+// slow path (ROW_MAX: each 16-lane row has its own KV head, so its maxima are
+// its own; otherwise every lane group of the wave shares them); the bf16
+// weights are paired over tokens and the V pieces accumulated into acc.
+template <int D, int G, bool F8, bool ROW_MAX, typename KVt>
+__device__ __forceinline__ void attend(const KVt& r, const int base, const bool valid, const uint4 (&qr)[G],
+                                       const float scale, float (&m_own)[(G + 3) / 4], float (&l_own)[(G + 3) / 4],
+                                       float (&acc)[G][8], const int li) {
+  using Lay = Layout<D>;
+  constexpr int LPT = Lay::LPT, TPL = Lay::TPL;
+  constexpr int NSET = (G + 3) / 4;
+  static_assert(!ROW_MAX || TPL == 4, "a row's own maxima need the row to hold one KV head");
+  const int my_h = li / TPL;
+  const bool b0 = (li & 1) != 0;
+  // partial dots: value h TPL + u of set j is head 4 j + h, token u
+  float x[NSET];
+  {
+    uint32_t kw[TPL][4];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) bf16_words<F8>(r.k[base + u], kw[u]);
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+      float w[LPT];
+#pragma unroll
+      for (int h4 = 0; h4 < 4; ++h4)
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+          const int h = 4 * j + h4;
+          float d = 0.f;
+          if (h < G) {
+            const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h]);
+#pragma unroll
+            for (int jw = 0; jw < 4; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
+          }
+          w[h4 * TPL + u] = d;
+        }
+      // the reduction is a cross-lane operation: every lane must take
+      // part, so it runs unconditionally and invalid slots are masked
+      // afterwards
+      const float xs = reduce_scatter<LPT>(w, li) * scale;
+      const bool ok = (4 * j + my_h < G) && valid;
+      x[j] = ok ? xs : kNegInf;
+    }
+  }
+  // rare slow path: raise the running maxima
+  bool need = false;
+#pragma unroll
+  for (int j = 0; j < NSET; ++j) need |= x[j] > m_own[j] + kRescaleSlack;
+  if (__any(need)) {
+    uint32_t al[NSET][4][1];
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+      // maximum over the lanes holding the same head: its tokens in the
+      // group, then (unless ROW_MAX) the groups of the wave
+      float mx = x[j];
+      mx = fmaxf(mx, dpp<kDppXor1>(mx));
+      if constexpr (TPL == 4) {
+        mx = fmaxf(mx, dpp<kDppXor2>(mx));
+      } else {
+        mx = fmaxf(mx, dpp<kDppRor8>(mx));
+      }
+      if constexpr (!ROW_MAX) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      const float mn = fmaxf(m_own[j], mx);
+      const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own[j] - mn);
+      l_own[j] *= alpha;
+      m_own[j] = mn;
+      uint32_t al2[4][TPL / 2];
+      broadcast_pairs<TPL>(__float_as_uint(alpha), li, al2);
+#pragma unroll
+      for (int h4 = 0; h4 < 4; ++h4) al[j][h4][0] = al2[h4][0];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float alpha = __uint_as_float(al[h >> 2][h & 3][0]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
+    }
+  }
+  // weights: one exponential per lane, paired over tokens (u, u + 1) of a
+  // head, broadcast to the group
+  uint32_t pp[NSET][4][TPL / 2];
+#pragma unroll
+  for (int j = 0; j < NSET; ++j) {
+    const float p = x[j] == kNegInf ? 0.f : fast_exp2(x[j] - m_own[j]);
+    const float other = dpp<kDppXor1>(p);
+    const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
+    l_own[j] += b0 ? bf16_hi(pk) : bf16_lo(pk);
+    broadcast_pairs<TPL>(pk, li, pp[j]);
+  }
+  // V rows of each token pair interleaved per d: (v0[d], v1[d]) pairs.
+#pragma unroll
+  for (int q2 = 0; q2 < TPL / 2; ++q2) {
+    uint32_t v0[4], v1[4];
+    bf16_words<F8>(r.v[base + 2 * q2], v0);
+    bf16_words<F8>(r.v[base + 2 * q2 + 1], v1);
+#pragma unroll
+    for (int jw = 0; jw < 4; ++jw) {
+      const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
+      const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t w = pp[h >> 2][h & 3][q2];
+        acc[h][2 * jw] = dot2_bf16(w, lo, acc[h][2 * jw]);
+        acc[h][2 * jw + 1] = dot2_bf16(w, hi, acc[h][2 * jw + 1]);
+      }
+    }
+  }
+}
+
 // Appending decode (APP): one new token per sequence of the launch, its slot
 // and position in the kernel arguments (up to kAppendRows sequences per
 // launch).  Every work-group of sequence s takes the sequence's length
@@ -166,7 +283,6 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
   // wave-uniform (SGPR) so that the tile loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane / LPT, li = lane % LPT, row = lane >> 4;
-  const bool b0 = (li & 1) != 0;
   const int my_h = li / TPL, my_u = li % TPL;   // the (head in set, token) whose score this lane finishes
 
   const int P_ = a.partition_size;
@@ -330,101 +446,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
     // One half tile: tokens t0 + grp + NG u of each group, held in
     // r.k / r.v [TPL hf + u].
     auto compute = [&](int t0, const KVt& r, const int hf) __attribute__((always_inline)) {
-      const bool valid = t0 + grp + NG * my_u < c1;   // the token of this lane's score
-      // partial dots: value h TPL + u of set j is head 4 j + h, token u
-      float x[NSET];
-      {
-        uint32_t kw[TPL][4];
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) bf16_words<F8>(r.k[TPL * hf + u], kw[u]);
-#pragma unroll
-        for (int j = 0; j < NSET; ++j) {
-          float w[LPT];
-#pragma unroll
-          for (int h4 = 0; h4 < 4; ++h4)
-#pragma unroll
-            for (int u = 0; u < TPL; ++u) {
-              const int h = 4 * j + h4;
-              float d = 0.f;
-              if (h < G) {
-                const uint32_t* qq = reinterpret_cast<const uint32_t*>(&qr[h]);
-#pragma unroll
-                for (int jw = 0; jw < 4; ++jw) d = dot2_bf16(qq[jw], kw[u][jw], d);
-              }
-              w[h4 * TPL + u] = d;
-            }
-          // the reduction is a cross-lane operation: every lane must take
-          // part, so it runs unconditionally and invalid slots are masked
-          // afterwards
-          const float xs = reduce_scatter<LPT>(w, li) * scale;
-          const bool ok = (4 * j + my_h < G) && valid;
-          x[j] = ok ? xs : kNegInf;
-        }
-      }
-      // rare slow path: raise the wave's running maxima
-      bool need = false;
-#pragma unroll
-      for (int j = 0; j < NSET; ++j) need |= x[j] > m_own[j] + kRescaleSlack;
-      if (__any(need)) {
-        uint32_t al[NSET][4][1];
-#pragma unroll
-        for (int j = 0; j < NSET; ++j) {
-          // maximum over the lanes holding the same head: its tokens in the
-          // group, then the groups of the wave
-          float mx = x[j];
-          mx = fmaxf(mx, dpp<kDppXor1>(mx));
-          if constexpr (TPL == 4) {
-            mx = fmaxf(mx, dpp<kDppXor2>(mx));
-          } else {
-            mx = fmaxf(mx, dpp<kDppRor8>(mx));
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float mn = fmaxf(m_own[j], mx);
-          const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own[j] - mn);
-          l_own[j] *= alpha;
-          m_own[j] = mn;
-          uint32_t al2[4][TPL / 2];
-          broadcast_pairs<TPL>(__float_as_uint(alpha), li, al2);
-#pragma unroll
-          for (int h4 = 0; h4 < 4; ++h4) al[j][h4][0] = al2[h4][0];
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float alpha = __uint_as_float(al[h >> 2][h & 3][0]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
-        }
-      }
-      // weights: one exponential per lane, paired over tokens (u, u + 1) of a
-      // head, broadcast to the group
-      uint32_t pp[NSET][4][TPL / 2];
-#pragma unroll
-      for (int j = 0; j < NSET; ++j) {
-        const float p = x[j] == kNegInf ? 0.f : fast_exp2(x[j] - m_own[j]);
-        const float other = dpp<kDppXor1>(p);
-        const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
-        l_own[j] += b0 ? bf16_hi(pk) : bf16_lo(pk);
-        broadcast_pairs<TPL>(pk, li, pp[j]);
-      }
-      // V rows of each token pair interleaved per d: (v0[d], v1[d]) pairs.
-#pragma unroll
-      for (int q2 = 0; q2 < TPL / 2; ++q2) {
-        uint32_t v0[4], v1[4];
-        bf16_words<F8>(r.v[TPL * hf + 2 * q2], v0);
-        bf16_words<F8>(r.v[TPL * hf + 2 * q2 + 1], v1);
-#pragma unroll
-        for (int jw = 0; jw < 4; ++jw) {
-          const uint32_t lo = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(v1[jw], v0[jw], 0x07060302u);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t w = pp[h >> 2][h & 3][q2];
-            acc[h][2 * jw] = dot2_bf16(w, lo, acc[h][2 * jw]);
-            acc[h][2 * jw + 1] = dot2_bf16(w, hi, acc[h][2 * jw + 1]);
-          }
-        }
-      }
+      attend<D, G, F8, false>(r, TPL * hf, t0 + grp + NG * my_u < c1, qr, scale, m_own, l_own, acc, li);
     };
 
     // kBuffers register buffers: while tile t is computed, the next
@@ -594,6 +616,238 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
       T* cache = const_cast<T*>(lane < D / 8 ? kcache : vcache);
       *reinterpret_cast<uint4*>(cache + dst) = app_piece;
       if (g == 0 && lane == 0) {
+        if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
+        a.wr_lens[s] = app_pos + 1;
+      }
+    }
+  }
+}
+
+// Lane 4 h4 of each 16-lane row to the whole row (h4 a compile-time value
+// after unrolling).
+__device__ __forceinline__ float row_bcast4(float x, int h4) {
+  switch (h4) {
+    case 0: return dpp<kDppRowBcast0 + 0>(x);
+    case 1: return dpp<kDppRowBcast0 + 4>(x);
+    case 2: return dpp<kDppRowBcast0 + 8>(x);
+    default: return dpp<kDppRowBcast0 + 12>(x);
+  }
+}
+
+// Row layout (D = 128, bf16 caches, KV heads a multiple of 4): the
+// partition pass of one wave, item (head set hs, partition part, sequence s),
+// where head set hs is KV heads 4 hs .. 4 hs + 3.  Row r of the wave (lanes
+// 16 r .. 16 r + 15) holds KV head 4 hs + r, lane li its elements
+// 8 li .. 8 li + 7, so one load instruction reads one token's rows of the
+// four heads: 1 KiB of contiguous cache.  The wave walks the partition's
+// tokens 4 at a time (lane load u = token t0 + u) with NB - 1 steps of loads
+// in flight, and writes its heads' partials itself: no LDS and no barrier,
+// so the waves of a work-group are independent.  The work-group's four
+// waves take consecutive items (head sets fastest), so the head sets of one
+// partition read the same tokens' whole rows at about the same time.
+template <int G, bool BIG, bool APP, int NB>
+__device__ __forceinline__ void decode_rows(const DecodeArgs& a, const RowsOf<APP>& rows, const int part,
+                                            const int hs, const int s) {
+  constexpr int D = 128;
+  using T = uint16_t;
+  using Lay = Layout<D>;
+  constexpr int TPL = Lay::TPL;
+  using KVt = KV<false, TPL>;
+  constexpr int NSET = (G + 3) / 4;
+  static_assert(TPL == 4 && NB >= 2, "row layout: 4 tokens per step");
+  const int lane = threadIdx.x & 63;
+  const int row = lane >> 4, li = lane & 15;
+  const int my_h = li / TPL, my_u = li % TPL;   // the (head in set, token) whose score this lane finishes
+  const int g = 4 * hs + row;                   // this row's KV head
+
+  const int P_ = a.partition_size;
+  const int start = part * P_;
+  const int lgB = a.log2_block_size;
+  const int Bmask = (1 << lgB) - 1;
+  const int64_t row_elems = (int64_t)a.num_kv_heads * D;
+  const int64_t bstride = a.cache_block_stride;
+  const T* kcache = static_cast<const T*>(a.key_cache);
+  const T* vcache = static_cast<const T*>(a.value_cache);
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.bt_stride;
+  const int width = (a.max_seq_len + Bmask) >> lgB;
+  const float scale = a.scale * kLog2e;
+
+  int64_t app_slot = -1;
+  int app_pos = -1;
+  if constexpr (APP) {
+    app_slot = rows.slots[s];
+    app_pos = rows.pos[s];
+  }
+  const bool app = APP && app_slot >= 0;
+  const int app_j = app ? app_pos >> lgB : -1;
+  const int app_blk = app ? (int)(app_slot >> lgB) : 0;
+
+  // independent loads first: the length, the queries and the table entry of
+  // the partition's first token (index kept inside the row)
+  int len = a.seq_lens[s];
+  if (app) len = app_pos + 1;
+  uint4 qr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qr[h] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                            ((int64_t)s * a.num_q_heads + g * G + h) * D + 8 * li);
+  int nxt = 0;
+  if constexpr (BIG) {
+    const int j_start = (start >> lgB) < width - 1 ? (start >> lgB) : width - 1;
+    nxt = bt_row[j_start];
+  }
+
+  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  const bool live = part * P_ < len || part == 0;
+  const int end = !live ? start : (start + P_ < len ? start + P_ : len);
+  const int lane_off = g * D + 8 * li;
+
+  // APP: this row's pieces of the new token's K/V rows, copied into the slot
+  // by the waves of the partition that holds the new position
+  const T* new_k = nullptr;
+  const T* new_v = nullptr;
+  bool app_copy = false;
+  uint4 app_k = make_uint4(0, 0, 0, 0), app_v = app_k;
+  if constexpr (APP) {
+    new_k = static_cast<const T*>(a.new_key) + (int64_t)s * a.new_key_stride + lane_off;
+    new_v = static_cast<const T*>(a.new_value) + (int64_t)s * a.new_value_stride + lane_off;
+    app_copy = app && app_pos / P_ == part;
+    if (app_copy) {
+      app_k = *reinterpret_cast<const uint4*>(new_k);
+      app_v = *reinterpret_cast<const uint4*>(new_v);
+    }
+  }
+
+  float m_own[NSET], l_own[NSET], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < NSET; ++j) {
+    m_own[j] = kNegInf;
+    l_own[j] = 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+
+  // Step t0 (a multiple of 4 from the partition start): tokens past `end`
+  // read token tc (valid), steps past `end` read the partition's first
+  // token, so every load stays inside the cache and is issued
+  // unconditionally.  B >= 16: the step's 4 tokens lie in one block; the
+  // steps are loaded in order, and each load fetches the next step's table
+  // entry (nxt) for the next call, so the scalar load has a whole step to
+  // land.  B < 16: each token's entry is a scalar load of its own (all lanes
+  // of a load read the same token).
+  auto load = [&](const int t0, KVt& r) __attribute__((always_inline)) {
+    const int tc = t0 < end ? t0 : start;
+    const T* kp[TPL];
+    const T* vp[TPL];
+    if constexpr (BIG) {
+      int blk = __builtin_amdgcn_readfirstlane(APP && (tc >> lgB) == app_j ? app_blk : nxt);
+      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      const int t1 = t0 + 4 < end ? t0 + 4 : start;
+      nxt = bt_row[t1 >> lgB];
+      const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_elems + lane_off;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const int r_ = tc + u < end ? u : 0;
+        const bool isnew = APP && app && tc + r_ == app_pos;
+        kp[u] = isnew ? new_k : kcache + base + r_ * row_elems;
+        vp[u] = isnew ? new_v : vcache + base + r_ * row_elems;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const int tok = tc + u < end ? tc + u : tc;
+        const int j = tok >> lgB;
+        int blk = __builtin_amdgcn_readfirstlane(APP && j == app_j ? app_blk : bt_row[j]);
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        const int64_t off = (int64_t)blk * bstride + (int64_t)(tok & Bmask) * row_elems + lane_off;
+        const bool isnew = APP && app && tok == app_pos;
+        kp[u] = isnew ? new_k : kcache + off;
+        vp[u] = isnew ? new_v : vcache + off;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) r.k[u] = *reinterpret_cast<const uint4*>(kp[u]);
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) r.v[u] = *reinterpret_cast<const uint4*>(vp[u]);
+  };
+
+  // NB register buffers: while step i is computed, steps i + 1 .. i + NB - 1
+  // are in flight.  Whole rounds of NB steps with a single bottom-tested
+  // exit, then the loaded tail (as in the head layout).
+  const int n_steps = (end - start + 3) >> 2;
+  KVt r[NB];
+  int t = start;
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k) load(t + 4 * k, r[k]);
+  int i = 0;
+  for (; i + NB <= n_steps; i += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      load(t + 4 * (NB - 1), r[(k + NB - 1) % NB]);
+      attend<D, G, false, true>(r[k], 0, t + my_u < end, qr, scale, m_own, l_own, acc, li);
+      t += 4;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k)
+    if (n_steps - i > k) attend<D, G, false, true>(r[k], 0, t + 4 * k + my_u < end, qr, scale, m_own, l_own, acc, li);
+
+  if (!live) return;
+  const int nparts = len > 0 ? (len + P_ - 1) / P_ : 1;
+
+  // the row's sums of the weights per head (over the head's 4 token lanes);
+  // the maxima are already equal on those lanes
+  float lsum[NSET];
+#pragma unroll
+  for (int j = 0; j < NSET; ++j) {
+    lsum[j] = l_own[j] + dpp<kDppXor1>(l_own[j]);
+    lsum[j] += dpp<kDppXor2>(lsum[j]);
+  }
+  const int64_t q0 = (int64_t)s * a.num_q_heads + g * G;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float L = row_bcast4(lsum[h >> 2], h & 3);
+    float val[8];
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) val[i2] = L > 0.f ? acc[h][i2] / L * a.v_scale : 0.f;
+    if (nparts == 1) {
+      uint4 o;
+      o.x = pack_bf16x2(val[0], val[1]);
+      o.y = pack_bf16x2(val[2], val[3]);
+      o.z = pack_bf16x2(val[4], val[5]);
+      o.w = pack_bf16x2(val[6], val[7]);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (q0 + h) * D + 8 * li) = o;
+    } else {
+      float* dst = a.ws_out + ((q0 + h) * a.max_parts + part) * D + 8 * li;
+      *reinterpret_cast<float4*>(dst) = make_float4(val[0], val[1], val[2], val[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(val[4], val[5], val[6], val[7]);
+    }
+  }
+  if (my_u == 0) {
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+      const int h = 4 * j + my_h;
+      if (h < G) {
+        const float lse2 = lsum[j] > 0.f ? m_own[j] + fast_log2(lsum[j]) : kNegInf;
+        if (nparts == 1) {
+          if (a.lse) a.lse[q0 + h] = lse2 * kLn2;
+        } else {
+          a.ws_lse[(q0 + h) * a.max_parts + part] = lse2;
+        }
+      }
+    }
+  }
+
+  // APP: the new token's K/V rows of this wave's heads into the slot, and
+  // (head set 0) the new position's table entry and the length
+  if constexpr (APP) {
+    if (app_copy) {
+      const int64_t dst = (int64_t)app_blk * bstride + (app_slot & Bmask) * row_elems + lane_off;
+      *reinterpret_cast<uint4*>(const_cast<T*>(kcache) + dst) = app_k;
+      *reinterpret_cast<uint4*>(const_cast<T*>(vcache) + dst) = app_v;
+      if (hs == 0 && lane == 0) {
         if (app_j < a.bt_stride) a.wr_tables[(int64_t)s * a.bt_stride + app_j] = app_blk;
         a.wr_lens[s] = app_pos + 1;
       }

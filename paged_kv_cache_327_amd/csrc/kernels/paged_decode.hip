@@ -113,6 +113,32 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[row] = (M + fast_log2(W)) * kLn2;
 }
 
+// Row layout: wave item 4 blockIdx.x + wave = (head set fastest, partition,
+// sequence); waves past the last item have nothing to do.
+template <int G, bool BIG, bool APP>
+__global__ void __launch_bounds__(256) decode_rows_kernel(DecodeArgs a, RowsOf<APP> rows, int32_t n_items) {
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= n_items) return;
+  const int hsn = a.num_kv_heads >> 2;
+  const int hs = item % hsn, rest = item / hsn;
+  decode_rows<G, BIG, APP, kRowBuffers<G>>(a, rows, rest % a.max_parts, hs, rest / a.max_parts);
+}
+
+template <int G, bool APP>
+void launch_rows(const DecodeArgs& a, const RowsOf<APP>& rows, int64_t items, hipStream_t st) {
+  const dim3 grid((unsigned)((items + 3) / 4));
+  if (a.log2_block_size >= 4)
+    hipLaunchKernelGGL((decode_rows_kernel<G, true, APP>), grid, dim3(256), 0, st, a, rows, (int32_t)items);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<G, false, APP>), grid, dim3(256), 0, st, a, rows, (int32_t)items);
+}
+
+// Wave items of a row-layout launch over n sequences (-1 past int range).
+int64_t row_items(const DecodeArgs& a, int32_t n) {
+  const int64_t items = (int64_t)a.max_parts * (a.num_kv_heads / 4) * n;
+  return items + 3 > 0x7fffffffLL ? -1 : items;
+}
+
 template <int D, int G, bool BIG, bool F8>
 int launch_parts(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
@@ -131,6 +157,15 @@ template <int D, int G>
 int launch_g(const DecodeArgs& a, hipStream_t st) {
   const bool big = a.log2_block_size >= 4;
   int e;
+  if constexpr (D == 128) {
+    if (a.rows) {
+      const int64_t items = row_items(a, a.num_seqs);
+      if (items < 0) return (int)hipErrorInvalidConfiguration;
+      launch_rows<G, false>(a, NoAppend{0}, items, st);
+      e = (int)hipGetLastError();
+      return e != 0 ? e : launch_merge<D>(a, st);
+    }
+  }
   if (a.fp8)
     e = big ? launch_parts<D, G, true, true>(a, st) : launch_parts<D, G, false, true>(a, st);
   else
@@ -167,6 +202,16 @@ int launch_g_append(const DecodeArgs& a, const int64_t* slots, const int32_t* po
     b.new_value = static_cast<const uint16_t*>(a.new_value) + r0 * a.new_value_stride;
     b.wr_tables = a.wr_tables + (int64_t)r0 * a.bt_stride;
     b.wr_lens = a.wr_lens + r0;
+    if constexpr (D == 128) {
+      if (a.rows) {
+        const int64_t items = row_items(a, n);
+        if (items < 0) return (int)hipErrorInvalidConfiguration;
+        launch_rows<G, true>(b, rows, items, st);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+        continue;
+      }
+    }
     const dim3 grid(a.max_parts, a.num_kv_heads, n);
     if (big)
       hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(256), 0, st, b, rows);

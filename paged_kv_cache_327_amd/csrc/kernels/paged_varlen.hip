@@ -32,9 +32,11 @@ struct VarlenGrid {
   int32_t n_chunks;      // chunks of 8 work-groups in the grid
   int32_t n_pre_chunks;  // chunks running prefill work-groups
   int32_t dec_wgs;       // decode work-groups: max_parts x num_kv_heads x decode rows
+                         // (row layout: a quarter of the wave items, rounded up)
+  int32_t dec_items;     // row layout: wave items, max_parts x num_kv_heads / 4 x decode rows
 };
 
-template <int D, int G, int HW, bool CAUSAL, bool BIG, bool SMALL>
+template <int D, int G, int HW, bool CAUSAL, bool BIG, bool SMALL, bool ROWS>
 __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArgs d, VarlenGrid vg) {
   const int c = blockIdx.x >> 3, x = blockIdx.x & 7;
   // chunk c runs prefill when the even spread of n_pre_chunks over n_chunks
@@ -44,19 +46,38 @@ __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArg
   if (kp1 > kp) {
     prefill_body::prefill_tile<D, HW, CAUSAL, BIG, false, SMALL>(p, 8 * kp + x);
   } else {
-    const int v = 8 * (c - kp) + x;   // decode work-group, partition fastest as in its own grid
+    const int v = 8 * (c - kp) + x;   // decode work-group, in the order of its own grid
     if (v >= vg.dec_wgs) return;
-    const int part = v % d.max_parts, rest = v / d.max_parts;
-    decode_body::decode_partition<D, G, BIG, false, false>(d, decode_body::NoAppend{0}, part, rest % d.num_kv_heads,
-                                                          rest / d.num_kv_heads);
+    if constexpr (ROWS) {
+      const int item = 4 * v + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      if (item >= vg.dec_items) return;
+      const int hsn = d.num_kv_heads >> 2;
+      const int hs = item % hsn, rest = item / hsn;
+      decode_body::decode_rows<G, BIG, false, decode_body::kRowBuffers<G>>(d, decode_body::NoAppend{0},
+                                                                          rest % d.max_parts, hs, rest / d.max_parts);
+    } else {
+      const int part = v % d.max_parts, rest = v / d.max_parts;
+      decode_body::decode_partition<D, G, BIG, false, false>(d, decode_body::NoAppend{0}, part,
+                                                            rest % d.num_kv_heads, rest / d.num_kv_heads);
+    }
   }
 }
 
-template <int D, int G, bool CAUSAL, bool BIG, bool SMALL>
+template <int D, int G, bool CAUSAL, bool BIG, bool SMALL, bool ROWS = false>
 void launch_one(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, hipStream_t st) {
   constexpr int HW = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-  hipLaunchKernelGGL((varlen_kernel<D, G, HW, CAUSAL, BIG, SMALL>), dim3((unsigned)vg.n_chunks * 8), dim3(256), 0, st,
-                     p, d, vg);
+  hipLaunchKernelGGL((varlen_kernel<D, G, HW, CAUSAL, BIG, SMALL, ROWS>), dim3((unsigned)vg.n_chunks * 8), dim3(256),
+                     0, st, p, d, vg);
+}
+
+// The decode rows in the row layout when the decode arguments chose it
+// (head_dim 128 only).
+template <int D, int G, bool CAUSAL, bool BIG, bool SMALL>
+void launch_layout(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (d.rows) return launch_one<D, G, CAUSAL, BIG, SMALL, true>(p, d, vg, st);
+  }
+  launch_one<D, G, CAUSAL, BIG, SMALL>(p, d, vg, st);
 }
 
 template <int D, int G>
@@ -66,18 +87,18 @@ void launch_g(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, h
   const bool small = (int64_t)p.num_blocks * p.cache_block_stride * 2 <= 0xffffffffLL;
   if (p.causal) {
     if (big)
-      launch_one<D, G, true, true, false>(p, d, vg, st);
+      launch_layout<D, G, true, true, false>(p, d, vg, st);
     else if (small)
-      launch_one<D, G, true, false, true>(p, d, vg, st);
+      launch_layout<D, G, true, false, true>(p, d, vg, st);
     else
-      launch_one<D, G, true, false, false>(p, d, vg, st);
+      launch_layout<D, G, true, false, false>(p, d, vg, st);
   } else {
     if (big)
-      launch_one<D, G, false, true, false>(p, d, vg, st);
+      launch_layout<D, G, false, true, false>(p, d, vg, st);
     else if (small)
-      launch_one<D, G, false, false, true>(p, d, vg, st);
+      launch_layout<D, G, false, false, true>(p, d, vg, st);
     else
-      launch_one<D, G, false, false, false>(p, d, vg, st);
+      launch_layout<D, G, false, false, false>(p, d, vg, st);
   }
 }
 
@@ -115,7 +136,13 @@ int launch_paged_varlen(const PrefillArgs& p, const DecodeArgs& d, void* stream)
   }
   const int64_t n_pre = prefill_grid_size(p);
   if (n_pre < 0) return (int)hipErrorInvalidConfiguration;
-  const int64_t dec = d.num_seqs > 0 ? (int64_t)d.max_parts * d.num_kv_heads * d.num_seqs : 0;
+  int64_t dec = 0, dec_items = 0;
+  if (d.num_seqs > 0 && d.rows) {
+    dec_items = (int64_t)d.max_parts * (d.num_kv_heads / 4) * d.num_seqs;
+    dec = (dec_items + 3) / 4;
+  } else if (d.num_seqs > 0) {
+    dec = (int64_t)d.max_parts * d.num_kv_heads * d.num_seqs;
+  }
   const int64_t chunks = n_pre / 8 + (dec + 7) / 8;
   if (chunks == 0) return 0;
   if (chunks * 8 * 256 > 0xffffffffLL) return (int)hipErrorInvalidConfiguration;
@@ -123,6 +150,7 @@ int launch_paged_varlen(const PrefillArgs& p, const DecodeArgs& d, void* stream)
   vg.n_chunks = (int32_t)chunks;
   vg.n_pre_chunks = (int32_t)(n_pre / 8);
   vg.dec_wgs = (int32_t)dec;
+  vg.dec_items = (int32_t)dec_items;
   if (p.head_dim == 64)
     launch_d<64>(p, d, vg, st);
   else

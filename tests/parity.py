@@ -6,7 +6,11 @@ import torch
 # Attention tolerance for bf16 storage with fp32 accumulation.
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-LSE_ABS = 2e-3
+# The softmax weights enter p.v and their sum rounded to bf16 (8 significant
+# bits, nearest-even: relative error <= 2^-8 each), so the sum's relative
+# error is <= 2^-8 and the log-sum-exp's <= ln(1 + 2^-8) = 3.90e-3, plus
+# fp32 rounding far below 1e-4.
+LSE_ABS = 4e-3
 
 
 def attention_errors(got: torch.Tensor, want: np.ndarray):
