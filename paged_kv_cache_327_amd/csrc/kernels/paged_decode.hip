@@ -63,53 +63,76 @@ __global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, Row
 
 // out[s, h] = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M) over the
 // sequence's partitions (log-sum-exp identity); lse = (M + log2 W) ln 2.
-// One wave per (sequence, query head): lane p holds partition p's log2 lse
-// (64 partitions per pass), the wave takes their maximum, and the partial
-// outputs are loaded kMergeBatch partitions at a time before any is summed,
-// so a merge costs a few round trips to memory instead of one per partition.
-// The sums run in partition order.
-constexpr int kMergeBatch = 16;
+// One wave per (sequence, query head), 64 partitions per round.  Lane l
+// holds 16-byte chunk l % (D / 4) of partition l / (D / 4) of each group of
+// 64 / (D / 4) consecutive partitions, so one load instruction reads whole
+// consecutive partials (1 KiB at D = 128); a round's partial loads are
+// issued together with its log2 lse loads (lane p: partition p), so it
+// costs one round trip to memory.  Each lane sums its partitions in order,
+// the lane groups are then added with a fixed butterfly: the result depends
+// on the partials only.
 template <int D>
 __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
+  constexpr int CH = D / 4;         // 16-byte chunks of a partial
+  constexpr int PPI = 64 / CH;      // partitions per load instruction
+  constexpr int NI = 64 / PPI;      // load instructions per 64 partitions
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int c = lane % CH, j = lane / CH;
   int len = a.seq_lens[s];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int nparts = (len + a.partition_size - 1) / a.partition_size;
   if (nparts <= 1) return;
   const int64_t row = (int64_t)s * a.num_q_heads + hq;
   const float* lse2 = a.ws_lse + row * a.max_parts;
-  const float* po = a.ws_out + row * a.max_parts * D;
-  float M = kNegInf;
-  for (int p0 = 0; p0 < nparts; p0 += 64) M = fmaxf(M, p0 + lane < nparts ? lse2[p0 + lane] : kNegInf);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float W = 0.f, o[D / 64];
-#pragma unroll
-  for (int k = 0; k < D / 64; ++k) o[k] = 0.f;
+  const float* po = a.ws_out + row * a.max_parts * D + 4 * c;
+  float M = kNegInf, W = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     const int n = nparts - p0 < 64 ? nparts - p0 : 64;
-    const float w = lane < n ? fast_exp2(lse2[p0 + lane] - M) : 0.f;
-    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-      float v[kMergeBatch][D / 64];
+    float4 v[NI];
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int i = i0 + j < n ? i0 + j : n - 1;     // a valid partial; its weight is not used
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) v[j][k] = po[(int64_t)(p0 + i) * D + lane + 64 * k];
+    for (int i = 0; i < NI; ++i) {
+      if (PPI * i < n) {   // wave-uniform
+        const int p = PPI * i + j < n ? PPI * i + j : n - 1;   // a valid partial; its weight is 0
+        v[i] = *reinterpret_cast<const float4*>(po + (int64_t)(p0 + p) * D);
       }
+    }
+    const float l = lane < n ? lse2[p0 + lane] : kNegInf;
+    float mb = l;
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        if (i0 + j < n) {
-          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i0 + j));
-          W += wj;
+    for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+    const float Mn = fmaxf(M, mb);
+    const float alpha = M == kNegInf ? 0.f : fast_exp2(M - Mn);   // earlier rounds' sums
+    M = Mn;
+    W *= alpha;
 #pragma unroll
-          for (int k = 0; k < D / 64; ++k) o[k] += wj * v[j][k];
-        }
+    for (int k = 0; k < 4; ++k) acc[k] *= alpha;
+    const float w = lane < n ? fast_exp2(l - M) : 0.f;
+    float ws = w;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
+    W += ws;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (PPI * i < n) {
+        const float wi = __shfl(w, PPI * i + j);   // 0 past the round's last partition
+        acc[0] += wi * v[i].x;
+        acc[1] += wi * v[i].y;
+        acc[2] += wi * v[i].z;
+        acc[3] += wi * v[i].w;
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) static_cast<uint16_t*>(a.out)[row * D + lane + 64 * k] = to_bf16(o[k] / W);
+  for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += __shfl_xor(acc[k], off);
+  if (j == 0) {
+    uint2 o;
+    o.x = pack_bf16x2(acc[0] / W, acc[1] / W);
+    o.y = pack_bf16x2(acc[2] / W, acc[3] / W);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * D + 4 * c) = o;
+  }
   if (a.lse && lane == 0) a.lse[row] = (M + fast_log2(W)) * kLn2;
 }
 
