@@ -66,6 +66,8 @@ MERGE_KERNEL = "decode_merge_kernel<128>"
 # head_dim, query heads per work-group, causal, block size >= 16, E4M3 caches, 32-bit key offsets
 PREFILL_KERNEL = "prefill_kernel<128, 4, true, true, false, false>"
 HEADLINE_PARTITION = 512
+FP8_SCALES = (0.05, 0.05)        # E4M3 k_scale, v_scale of the E4M3 workloads
+FP8_LONG_CONTEXT_PARTITION = 1024
 COUNTERS = {
     "long_context": os.path.join(ROOT, "profiles", "decode_append_long_context_traffic.txt"),
     "decode": os.path.join(ROOT, "profiles", "decode_append_llama3_8b_traffic.txt"),
@@ -844,7 +846,7 @@ def measure_host_pool(B, num_blocks=26_785, block_size=16, prompt=8192, batch=64
             f"append_batch_{batch}x1_us": round(t_app * 1e6, 2)}
 
 
-def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), instances=8, reps=48):
+def measure_fp8_decode(torch, B, hip_side, workloads, scales=FP8_SCALES, instances=8, reps=48):
     """Decode over E4M3 caches: the 64-sequence Llama-3-8B decode batch
     (8 pools rotated, about 590 MB of K/V codes, so that no pool stays in the
     last-level cache between its calls) and the 32-layer long-context pool;
@@ -905,7 +907,7 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=(0.05, 0.05), insta
     torch.cuda.empty_cache()
 
     wl = workloads.long_context()
-    L_, S, P = wl.num_layers, wl.num_seqs, 2048
+    L_, S, P = wl.num_layers, wl.num_seqs, FP8_LONG_CONTEXT_PARTITION
     kv = torch.full((L_, 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), 0x7F,
                     dtype=torch.uint8, device="cuda")
     h = hip_side.HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]),

@@ -131,6 +131,49 @@ def test_long_context_plain_decode_at_512_1024_2048(lc):
             check_rows(out, lse, want, f"P={P} layer {l}")
 
 
+def test_fp8_long_context_decode_at_bench_partition():
+    """bench.py's E4M3 long-context pool (the 26,785-block layout, 8
+    sequences of U{16384..32768} tokens, per-cache scales) for layers 0 and
+    31, decoded at bench.py's partition size: every sequence against the
+    oracle over the same codes."""
+    from oracle import fp8
+    wl = workloads.long_context()
+    scales, P = bench.FP8_SCALES, bench.FP8_LONG_CONTEXT_PARTITION
+    layers = (0, 31)
+    print(f"[bench steps] E4M3 long-context pool, layers {layers}, P={P}", flush=True)
+    kv = torch.full((len(layers), 2, wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim), 0x7F,
+                    dtype=torch.uint8, device="cuda")
+    h = hip_side.HipStep(wl, gen="device", caches=(kv[0, 0], kv[0, 1]),
+                         layers=[(l, kv[i, 0], kv[i, 1]) for i, l in enumerate(layers)], fp8=scales)
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    G = Hq // Hkv
+    msl = max(wl.seq_lens)
+    ws = torch.empty(B.pa_paged_decode_workspace_size(S, Hq, D, msl, P), dtype=torch.uint8, device="cuda")
+    for i, l in enumerate(layers):
+        q = workloads.query_bits(wl.seed, S, Hq, D, layer=l)
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((S, Hq), dtype=torch.float32, device="cuda")
+        B.pa_paged_decode_fp8(out, hip_side.to_device(q), kv[i, 0], kv[i, 1], h.table_dev, h.seq_lens_dev, msl,
+                              wl.scale, *scales, partition_size=P, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        want = []
+        for s in range(S):
+            kb, vb = h.logical_kv_bits(s, l)
+            k8, v8 = fp8.quantize_bf16(kb, scales[0]), fp8.quantize_bf16(vb, scales[1])
+            qq = attention.bf16_to_f64(q[s])
+            o = np.zeros((Hq, D))
+            ls = np.zeros(Hq)
+            for g in range(Hkv):
+                o[g * G:(g + 1) * G], ls[g * G:(g + 1) * G] = attention.softmax_attend(
+                    qq[g * G:(g + 1) * G], fp8.dequantize(k8[:, g], scales[0]), fp8.dequantize(v8[:, g], scales[1]),
+                    wl.scale)
+            want.append((s, o, ls))
+        print(f"[bench steps] E4M3 long context layer {l}: max/mean error "
+              f"{check_rows(out, lse, want, f'E4M3 P={P} layer {l}')}", flush=True)
+    del kv, h
+    torch.cuda.empty_cache()
+
+
 def test_long_context_appending_steps(lc):
     """Four consecutive headline steps: after each, layers 0 and 31 against
     the oracle on every sequence, the device tables and lengths against the
