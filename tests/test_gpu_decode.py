@@ -44,8 +44,11 @@ def test_llama_decode(partition_size):
     run_parity(workloads.llama_decode(), partition_size)
 
 
-def test_prefix_sharing_decode():
-    run_parity(workloads.prefix_cow())
+@pytest.mark.parametrize("partition_size", [512, 0])
+def test_prefix_sharing_decode(partition_size):
+    """bench.py times this workload at one partition per sequence and at
+    partitions of 512."""
+    run_parity(workloads.prefix_cow(), partition_size)
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])

@@ -119,6 +119,13 @@ def test_fp8_llama_decode(scales):
     run_parity(workloads.llama_decode(batch=16), scales)
 
 
+def test_fp8_llama_decode_bench_batch():
+    """bench.py's E4M3 batch: the 64 Llama-3-8B-shaped sequences, one
+    partition per sequence, scales 0.05, every row against the oracle."""
+    import bench
+    run_parity(workloads.llama_decode(), bench.FP8_SCALES, partition_size=0, what="batch of 64")
+
+
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("gqa", [(4, 4), (8, 2), (32, 8), (24, 3)])
 @pytest.mark.parametrize("block_size", [1, 16, 32])
