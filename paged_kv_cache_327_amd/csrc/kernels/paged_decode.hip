@@ -78,26 +78,43 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
   constexpr int NI = 64 / PPI;      // load instructions per 64 partitions
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   const int c = lane % CH, j = lane / CH;
+  const int64_t row = (int64_t)s * a.num_q_heads + hq;
+  const float* lse2 = a.ws_lse + row * a.max_parts;
+  const float* po = a.ws_out + row * a.max_parts * D + 4 * c;
+  // The first round's partials and sums are loaded together with the
+  // length, before the partition count is known, so that the merge waits for
+  // one round trip instead of two.  Slots past the count hold whatever an
+  // earlier call left there; they are read (inside the workspace) but get no
+  // weight and are never added.
+  const int n0 = a.max_parts < 64 ? a.max_parts : 64;
+  float4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (PPI * i < n0) {   // wave-uniform
+      const int p = PPI * i + j < n0 ? PPI * i + j : n0 - 1;
+      v[i] = *reinterpret_cast<const float4*>(po + (int64_t)p * D);
+    }
+  }
+  float l = lane < n0 ? lse2[lane] : kNegInf;
   int len = a.seq_lens[s];
   len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
   const int nparts = (len + a.partition_size - 1) / a.partition_size;
   if (nparts <= 1) return;
-  const int64_t row = (int64_t)s * a.num_q_heads + hq;
-  const float* lse2 = a.ws_lse + row * a.max_parts;
-  const float* po = a.ws_out + row * a.max_parts * D + 4 * c;
   float M = kNegInf, W = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < nparts; p0 += 64) {
     const int n = nparts - p0 < 64 ? nparts - p0 : 64;
-    float4 v[NI];
+    if (p0 > 0) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (PPI * i < n) {   // wave-uniform
-        const int p = PPI * i + j < n ? PPI * i + j : n - 1;   // a valid partial; its weight is 0
-        v[i] = *reinterpret_cast<const float4*>(po + (int64_t)(p0 + p) * D);
+      for (int i = 0; i < NI; ++i) {
+        if (PPI * i < n) {
+          const int p = PPI * i + j < n ? PPI * i + j : n - 1;
+          v[i] = *reinterpret_cast<const float4*>(po + (int64_t)(p0 + p) * D);
+        }
       }
+      l = lse2[p0 + (lane < n ? lane : 0)];
     }
-    const float l = lane < n ? lse2[p0 + lane] : kNegInf;
+    l = lane < n ? l : kNegInf;
     float mb = l;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
@@ -115,11 +132,21 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (PPI * i < n) {
-        const float wi = __shfl(w, PPI * i + j);   // 0 past the round's last partition
-        acc[0] += wi * v[i].x;
-        acc[1] += wi * v[i].y;
-        acc[2] += wi * v[i].z;
-        acc[3] += wi * v[i].w;
+        // the weight of the lane's partition PPI i + j (two scalar reads
+        // when a load covers two partitions)
+        float wi;
+        if constexpr (PPI == 2) {
+          const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), PPI * i));
+          const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), PPI * i + 1));
+          wi = j == 0 ? w0 : w1;
+        } else {
+          wi = __shfl(w, PPI * i + j);
+        }
+        const bool use = PPI * i + j < n;
+        acc[0] = use ? fmaf(wi, v[i].x, acc[0]) : acc[0];
+        acc[1] = use ? fmaf(wi, v[i].y, acc[1]) : acc[1];
+        acc[2] = use ? fmaf(wi, v[i].z, acc[2]) : acc[2];
+        acc[3] = use ? fmaf(wi, v[i].w, acc[3]) : acc[3];
       }
     }
   }
