@@ -149,3 +149,36 @@ def test_split_workspace_reuse_is_deterministic():
             assert_lse_close(lse, want_lse)
         else:
             assert torch.equal(out, first)
+
+
+@pytest.mark.parametrize("head_dim,partition_size", [(128, 64), (64, 64), (128, 2048)])
+def test_merge_gives_stale_partial_slots_no_weight(head_dim, partition_size):
+    """The merge loads the first 64 partial slots of a (sequence, head)
+    before it knows the sequence's partition count.  Here every slot starts
+    as NaN bytes: the rows' partition counts run from 1 to 79 (so a second
+    round of 64 is taken), and no slot past a row's count may reach its
+    output or its lse.  Row layout with the two-partitions-per-load merge
+    (head_dim 128, partitions of 64), head layout with four per load
+    (head_dim 64), and partitions of 2048."""
+    from paged_kv_cache_327_amd import binding as B
+    lens = [1, 60, 65, 700, 4100, 5000, 130, 2049]
+    wl = workloads.custom(f"stale_slots_d{head_dim}_p{partition_size}", 47, 16, 4, head_dim, 16, lens)
+    print(f"[decode] {wl.name}", flush=True)
+    h, o = HipStep(wl), OracleStep(wl)
+    q = decode_queries(wl)
+    msl = max(lens)
+    need = B.pa_paged_decode_workspace_size(len(lens), 16, head_dim, msl, partition_size)
+    assert need > 0
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    want, want_lse = attention.paged_decode(q, o.kc, o.vc, o.table, o.seq_lens, wl.scale)
+    for rep in range(2):
+        ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN floats everywhere
+        out = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda")
+        B.pa_paged_decode(out, qd, h.kc, h.vc, h.table_dev, h.seq_lens_dev, msl, wl.scale,
+                          partition_size=partition_size, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+        assert_attention_close(out, want, what=f"{wl.name} rep {rep}")
+        assert_lse_close(lse, want_lse)
+
