@@ -49,6 +49,8 @@ def sources():
 # * prefill, head_dim 64: two waves per SIMD, no scratch.
 # * decode partition pass: no AGPRs and no scratch; three waves per SIMD up
 #   to 4 query heads per KV head, two for 5-8.
+# * decode row layouts (bf16 and E4M3): no AGPRs, no scratch, two waves per
+#   SIMD.
 # * mixed-batch kernel (prefill and decode bodies in one kernel): 256
 #   VGPRs, no AGPRs, two waves per SIMD; with B < 16 at head_dim 128 up to
 #   32 bytes per lane of scratch (prefill's per-key offsets beside the
@@ -66,7 +68,7 @@ def _budget(name, targs):
         return (256, 0, 0 if (d == 64 or big) else 32, 2)
     if name == "decode_partition_kernel":
         return (512, 0, 0, 3) if targs[1] <= 4 else (512, 0, 0, 2)
-    if name == "decode_rows_kernel":
+    if name in ("decode_rows_kernel", "decode_rows8_kernel"):
         return 512, 0, 0, 2
     return 512, 256, 0, 1
 

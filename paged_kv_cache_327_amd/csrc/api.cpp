@@ -320,10 +320,14 @@ int make_decode_args(const char* fn, void* out, float* lse, const void* q, const
   a.scale = fp8 ? scale * k_scale : scale;
   a.v_scale = fp8 ? v_scale : 1.f;
   a.fp8 = fp8 ? 1 : 0;
-  // Explicit partitions of up to 1024 tokens over bf16 caches with
-  // head_dim 128 and a multiple of 4 KV heads take the row layout, whose
-  // waves read whole token rows of 4 heads; the rest the head layout.
-  a.rows = (!fp8 && head_dim == 128 && num_kv_heads % 4 == 0 && partition_size > 0 && partition_size <= 1024)
+  // Explicit partitions with head_dim 128 and a multiple of 4 KV heads take
+  // the row layout, whose waves read whole token rows of 4 heads: bf16
+  // caches up to 1024 tokens per partition, E4M3 caches up to 512 and with
+  // at most 4 query heads per KV head (one wave's item holds half the bytes
+  // of a bf16 one, so longer partitions leave too few items in flight); the
+  // rest the head layout.
+  a.rows = (head_dim == 128 && num_kv_heads % 4 == 0 && partition_size > 0 &&
+            (fp8 ? partition_size <= 512 && num_q_heads / num_kv_heads <= 4 : partition_size <= 1024))
                ? 1
                : 0;
   if (parts > 1) {

@@ -855,5 +855,298 @@ __device__ __forceinline__ void decode_rows(const DecodeArgs& a, const RowsOf<AP
   }
 }
 
+// ---------------------------------------------------------------------------
+// E4M3 row layout (head_dim 128, at most 4 query heads per KV head).  Wave
+// item = (head set hs of 4 KV heads, partition, sequence), as in the bf16
+// row layout, but a lane holds 16 codes: 16-lane row r holds KV head
+// 4 hs + r, its half row hw the tokens of parity hw, and lane c of the half
+// row the codes 16 c .. 16 c + 15 of its token's row.  One load instruction
+// thus reads the four heads' rows of two consecutive tokens (two runs of
+// 512 contiguous bytes), and a step of 8 tokens is 4 loads each of K and V.
+constexpr int kRows8Tokens = 8;
+constexpr int kRows8Buffers = 2;   // steps in flight + 1
+
+// 8 bf16 pairs (elements 2 j, 2 j + 1) of 16 E4M3 codes (exact conversion).
+__device__ __forceinline__ void e4m3x16_words(const uint4& x, uint32_t (&w)[8]) {
+  w[0] = e4m3x2_to_bf16x2<false>(x.x);
+  w[1] = e4m3x2_to_bf16x2<true>(x.x);
+  w[2] = e4m3x2_to_bf16x2<false>(x.y);
+  w[3] = e4m3x2_to_bf16x2<true>(x.y);
+  w[4] = e4m3x2_to_bf16x2<false>(x.z);
+  w[5] = e4m3x2_to_bf16x2<true>(x.z);
+  w[6] = e4m3x2_to_bf16x2<false>(x.w);
+  w[7] = e4m3x2_to_bf16x2<true>(x.w);
+}
+
+// Lane c of row (r, half row hw) of the E4M3 row layout; broadcast of the
+// value of lane 2 h of its row (the first lane holding head h) to the row.
+__device__ __forceinline__ float row_bcast_pair(float x, int h) {
+  switch (h) {
+    case 0: return dpp<kDppRowBcast0 + 0>(x);
+    case 1: return dpp<kDppRowBcast0 + 2>(x);
+    case 2: return dpp<kDppRowBcast0 + 4>(x);
+    default: return dpp<kDppRowBcast0 + 6>(x);
+  }
+}
+
+// Two tokens of a lane group (the half row): k0/v0 and k1/v1 hold the lane's
+// codes of tokens t0 + hw and t0 + 2 + hw.  The group's G heads x 2 tokens
+// partial dots are reduce-scattered over its 8 lanes (lane c finishes head
+// c / 2, token c % 2); a row's maxima are its own (one KV head per row) and
+// are taken over both half rows; the bf16 weights are paired over the two
+// tokens and broadcast to the half row, and the V codes accumulated.
+template <int G>
+__device__ __forceinline__ void attend_e4m3_rows(const uint4& k0, const uint4& k1, const uint4& v0, const uint4& v1,
+                                                 const bool valid, const uint32_t (&qw)[G][8], const float scale,
+                                                 float& m_own, float& l_own, float (&acc)[G][16], const int c) {
+  static_assert(G >= 1 && G <= 4, "E4M3 row layout: at most 4 query heads per KV head");
+  float x;
+  {
+    uint32_t kw[2][8];
+    e4m3x16_words(k0, kw[0]);
+    e4m3x16_words(k1, kw[1]);
+    float w[8];
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float d = 0.f;
+        if (h4 < G) {
+#pragma unroll
+          for (int jw = 0; jw < 8; ++jw) d = dot2_bf16(qw[h4][jw], kw[u][jw], d);
+        }
+        w[2 * h4 + u] = d;
+      }
+    const float xs = reduce_scatter<8>(w, c) * scale;
+    x = (c / 2 < G && valid) ? xs : kNegInf;
+  }
+  // rare slow path: raise the row's running maxima
+  if (__any(x > m_own + kRescaleSlack)) {
+    float mx = fmaxf(x, dpp<kDppXor1>(x));
+    mx = fmaxf(mx, dpp<kDppRor8>(mx));
+    const float mn = fmaxf(m_own, mx);
+    const float alpha = mn == kNegInf ? 1.f : fast_exp2(m_own - mn);
+    l_own *= alpha;
+    m_own = mn;
+    uint32_t al[4][1];
+    broadcast_pairs<2>(__float_as_uint(alpha), c, al);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = __uint_as_float(al[h][0]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[h][i] *= ah;
+    }
+  }
+  // weights: one exponential per lane, paired over the two tokens of a head
+  const bool b0 = (c & 1) != 0;
+  const float p = x == kNegInf ? 0.f : fast_exp2(x - m_own);
+  const float other = dpp<kDppXor1>(p);
+  const uint32_t pk = pack_bf16x2(b0 ? other : p, b0 ? p : other);
+  l_own += b0 ? bf16_hi(pk) : bf16_lo(pk);
+  uint32_t pp[4][1];
+  broadcast_pairs<2>(pk, c, pp);
+  // V rows of the two tokens interleaved per d: (v0[d], v1[d]) pairs
+  uint32_t vw0[8], vw1[8];
+  e4m3x16_words(v0, vw0);
+  e4m3x16_words(v1, vw1);
+#pragma unroll
+  for (int jw = 0; jw < 8; ++jw) {
+    const uint32_t lo = __builtin_amdgcn_perm(vw1[jw], vw0[jw], 0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(vw1[jw], vw0[jw], 0x07060302u);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      acc[h][2 * jw] = dot2_bf16(pp[h][0], lo, acc[h][2 * jw]);
+      acc[h][2 * jw + 1] = dot2_bf16(pp[h][0], hi, acc[h][2 * jw + 1]);
+    }
+  }
+}
+
+// The partition pass of wave item (partition part, head set hs, sequence s)
+// over E4M3 caches; NB register buffers of one step each.
+template <int G, bool BIG, int NB>
+__device__ __forceinline__ void decode_rows8(const DecodeArgs& a, const int part, const int hs, const int s) {
+  constexpr int D = 128;
+  constexpr int kT = kRows8Tokens;
+  static_assert(NB >= 2, "at least one step in flight");
+  const int lane = threadIdx.x & 63;
+  const int row = lane >> 4, hw = (lane >> 3) & 1, c = lane & 7;
+  const int g = 4 * hs + row;   // this row's KV head
+
+  const int P_ = a.partition_size;
+  const int start = part * P_;
+  const int lgB = a.log2_block_size;
+  const int Bmask = (1 << lgB) - 1;
+  const int64_t row_bytes = (int64_t)a.num_kv_heads * D;   // one byte per code
+  const int64_t bstride = a.cache_block_stride;
+  const uint8_t* kcache = static_cast<const uint8_t*>(a.key_cache);
+  const uint8_t* vcache = static_cast<const uint8_t*>(a.value_cache);
+  const int32_t* bt_row = a.block_tables + (int64_t)s * a.bt_stride;
+  const int width = (a.max_seq_len + Bmask) >> lgB;
+  const float scale = a.scale * kLog2e;
+
+  // independent loads first: the length, the queries (the lane's 16
+  // elements of each of its KV head's query heads) and the table entry of
+  // the partition's first token
+  int len = a.seq_lens[s];
+  uint32_t qw[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                                     ((int64_t)s * a.num_q_heads + g * G + h) * D + 16 * c);
+    const uint4 x0 = qp[0], x1 = qp[1];
+    qw[h][0] = x0.x;
+    qw[h][1] = x0.y;
+    qw[h][2] = x0.z;
+    qw[h][3] = x0.w;
+    qw[h][4] = x1.x;
+    qw[h][5] = x1.y;
+    qw[h][6] = x1.z;
+    qw[h][7] = x1.w;
+  }
+  int nxt = 0;
+  if constexpr (BIG) {
+    const int j_start = (start >> lgB) < width - 1 ? (start >> lgB) : width - 1;
+    nxt = bt_row[j_start];
+  }
+
+  len = len < 0 ? 0 : (len > a.max_seq_len ? a.max_seq_len : len);
+  const bool live = part * P_ < len || part == 0;
+  const int end = !live ? start : (start + P_ < len ? start + P_ : len);
+  const int lane_off = g * D + 16 * c;
+
+  float m_own = kNegInf, l_own = 0.f, acc[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+
+  struct Step {
+    uint4 k[kT / 2];
+    uint4 v[kT / 2];
+  };
+  // Step t0 (a multiple of 8 from the partition start, so with B >= 16 its
+  // tokens lie in one block): load u fetches token t0 + 2 u + hw.  Tokens
+  // past `end` read the step's first token (valid), steps past `end` the
+  // partition's first token, so every load stays inside the cache and is
+  // issued unconditionally.  B >= 16: the step's block id was fetched by the
+  // previous load (nxt); B < 16: a scalar load per token.
+  auto load = [&](const int t0, Step& r) __attribute__((always_inline)) {
+    const int tc = t0 < end ? t0 : start;
+    const uint8_t* kp[kT / 2];
+    const uint8_t* vp[kT / 2];
+    if constexpr (BIG) {
+      int blk = __builtin_amdgcn_readfirstlane(nxt);
+      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      const int t1 = t0 + kT < end ? t0 + kT : start;
+      nxt = bt_row[t1 >> lgB];
+      const int64_t base = (int64_t)blk * bstride + (int64_t)(tc & Bmask) * row_bytes + lane_off;
+#pragma unroll
+      for (int u = 0; u < kT / 2; ++u) {
+        const int o = 2 * u + hw;
+        const int r_ = tc + o < end ? o : 0;
+        kp[u] = kcache + base + r_ * row_bytes;
+        vp[u] = vcache + base + r_ * row_bytes;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kT / 2; ++u) {
+        const int ta = tc + 2 * u < end ? tc + 2 * u : tc;
+        const int tb = tc + 2 * u + 1 < end ? tc + 2 * u + 1 : tc;
+        int ba = __builtin_amdgcn_readfirstlane(bt_row[ta >> lgB]);
+        int bb = __builtin_amdgcn_readfirstlane(bt_row[tb >> lgB]);
+        ba = ba < 0 ? 0 : (ba >= a.num_blocks ? a.num_blocks - 1 : ba);
+        bb = bb < 0 ? 0 : (bb >= a.num_blocks ? a.num_blocks - 1 : bb);
+        const int tok = hw ? tb : ta;
+        const int64_t off = (int64_t)(hw ? bb : ba) * bstride + (int64_t)(tok & Bmask) * row_bytes + lane_off;
+        kp[u] = kcache + off;
+        vp[u] = vcache + off;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kT / 2; ++u) r.k[u] = *reinterpret_cast<const uint4*>(kp[u]);
+#pragma unroll
+    for (int u = 0; u < kT / 2; ++u) r.v[u] = *reinterpret_cast<const uint4*>(vp[u]);
+  };
+  // the lane's score in pair q of step t0 is of token t0 + 4 q + 2 (c % 2) + hw
+  auto compute = [&](const int t0, const Step& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q2 = 0; q2 < kT / 4; ++q2)
+      attend_e4m3_rows<G>(r.k[2 * q2], r.k[2 * q2 + 1], r.v[2 * q2], r.v[2 * q2 + 1],
+                          t0 + 4 * q2 + 2 * (c & 1) + hw < end, qw, scale, m_own, l_own, acc, c);
+  };
+
+  // NB register buffers: while step i is computed, steps i + 1 .. i + NB - 1
+  // are in flight; whole rounds of NB steps with a single bottom-tested exit,
+  // then the loaded tail.
+  const int n_steps = (end - start + kT - 1) / kT;
+  Step rb[NB];
+  int t = start;
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k) load(t + kT * k, rb[k]);
+  int i = 0;
+  for (; i + NB <= n_steps; i += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      load(t + kT * (NB - 1), rb[(k + NB - 1) % NB]);
+      compute(t, rb[k]);
+      t += kT;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k + 1 < NB; ++k)
+    if (n_steps - i > k) compute(t + kT * k, rb[k]);
+
+  if (!live) return;
+  const int nparts = len > 0 ? (len + P_ - 1) / P_ : 1;
+
+  // the two half rows of a row hold the same head over different tokens:
+  // add them; the weight sum of head h: its lanes 2 h, 2 h + 1 of both
+  // half rows
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i2 = 0; i2 < 16; ++i2) acc[h][i2] += dpp<kDppRor8>(acc[h][i2]);
+  float lsum = l_own + dpp<kDppXor1>(l_own);
+  lsum += dpp<kDppRor8>(lsum);
+  const int64_t q0 = (int64_t)s * a.num_q_heads + g * G;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float L = row_bcast_pair(lsum, h);
+    if ((h & 1) != hw) continue;   // the half rows write alternate heads
+    float val[16];
+#pragma unroll
+    for (int i2 = 0; i2 < 16; ++i2) val[i2] = L > 0.f ? acc[h][i2] / L * a.v_scale : 0.f;
+    if (nparts == 1) {
+      uint4 o0, o1;
+      o0.x = pack_bf16x2(val[0], val[1]);
+      o0.y = pack_bf16x2(val[2], val[3]);
+      o0.z = pack_bf16x2(val[4], val[5]);
+      o0.w = pack_bf16x2(val[6], val[7]);
+      o1.x = pack_bf16x2(val[8], val[9]);
+      o1.y = pack_bf16x2(val[10], val[11]);
+      o1.z = pack_bf16x2(val[12], val[13]);
+      o1.w = pack_bf16x2(val[14], val[15]);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (q0 + h) * D + 16 * c);
+      dst[0] = o0;
+      dst[1] = o1;
+    } else {
+      float4* dst = reinterpret_cast<float4*>(a.ws_out + ((q0 + h) * a.max_parts + part) * D + 16 * c);
+      dst[0] = make_float4(val[0], val[1], val[2], val[3]);
+      dst[1] = make_float4(val[4], val[5], val[6], val[7]);
+      dst[2] = make_float4(val[8], val[9], val[10], val[11]);
+      dst[3] = make_float4(val[12], val[13], val[14], val[15]);
+    }
+  }
+  if (hw == 0 && (c & 1) == 0 && c / 2 < G) {
+    const int h = c / 2;
+    const float lse2 = lsum > 0.f ? m_own + fast_log2(lsum) : kNegInf;
+    if (nparts == 1) {
+      if (a.lse) a.lse[q0 + h] = lse2 * kLn2;
+    } else {
+      a.ws_lse[(q0 + h) * a.max_parts + part] = lse2;
+    }
+  }
+}
+
 }  // namespace decode_body
 }  // namespace pa

@@ -174,6 +174,25 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(DecodeArgs a, RowsOf<A
   decode_rows<G, BIG, APP, kRowBuffers<G>>(a, rows, rest % a.max_parts, hs, rest / a.max_parts);
 }
 
+// E4M3 row layout (at most 4 query heads per KV head): the same wave items.
+template <int G, bool BIG>
+__global__ void __launch_bounds__(256) decode_rows8_kernel(DecodeArgs a, int32_t n_items) {
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= n_items) return;
+  const int hsn = a.num_kv_heads >> 2;
+  const int hs = item % hsn, rest = item / hsn;
+  decode_rows8<G, BIG, kRows8Buffers>(a, rest % a.max_parts, hs, rest / a.max_parts);
+}
+
+template <int G>
+void launch_rows8(const DecodeArgs& a, int64_t items, hipStream_t st) {
+  const dim3 grid((unsigned)((items + 3) / 4));
+  if (a.log2_block_size >= 4)
+    hipLaunchKernelGGL((decode_rows8_kernel<G, true>), grid, dim3(256), 0, st, a, (int32_t)items);
+  else
+    hipLaunchKernelGGL((decode_rows8_kernel<G, false>), grid, dim3(256), 0, st, a, (int32_t)items);
+}
+
 template <int G, bool APP>
 void launch_rows(const DecodeArgs& a, const RowsOf<APP>& rows, int64_t items, hipStream_t st) {
   const dim3 grid((unsigned)((items + 3) / 4));
@@ -211,7 +230,15 @@ int launch_g(const DecodeArgs& a, hipStream_t st) {
     if (a.rows) {
       const int64_t items = row_items(a, a.num_seqs);
       if (items < 0) return (int)hipErrorInvalidConfiguration;
-      launch_rows<G, false>(a, NoAppend{0}, items, st);
+      if (a.fp8) {
+        if constexpr (G <= 4) {
+          launch_rows8<G>(a, items, st);
+        } else {
+          return (int)hipErrorInvalidValue;   // the host sets rows with E4M3 only for G <= 4
+        }
+      } else {
+        launch_rows<G, false>(a, NoAppend{0}, items, st);
+      }
       e = (int)hipGetLastError();
       return e != 0 ? e : launch_merge<D>(a, st);
     }
