@@ -104,6 +104,30 @@ def test_decode_reads_every_code_exactly(v_scale, head_dim):
     assert np.array_equal(got.view(np.float32).reshape(nb, head_dim).astype(np.float64), want)
 
 
+@pytest.mark.parametrize("v_scale", [1.0, 0.5])
+def test_row_layout_decode_reads_every_code_exactly(v_scale):
+    """The same check through the E4M3 row layout (head_dim 128, 4 KV heads,
+    one query head each, partitions of 64): every non-NaN code of every KV
+    head's V row comes back exactly."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    hkv, d = 4, 128
+    n_seq = -(-len(codes) // (hkv * d))
+    rows = np.resize(codes, (n_seq, hkv, d))
+    print(f"[fp8] every code, row layout, v_scale={v_scale}", flush=True)
+    nb, bs = n_seq, 16
+    kc = torch.full((nb, bs, hkv, d), 0x38, dtype=torch.uint8, device="cuda")   # K = 1.0
+    vc = torch.full((nb, bs, hkv, d), 0x7F, dtype=torch.uint8, device="cuda")
+    vc[:, 0] = torch.from_numpy(rows).cuda()
+    table = torch.arange(nb, dtype=torch.int32, device="cuda").reshape(nb, 1)
+    lens = torch.ones(nb, dtype=torch.int32, device="cuda")
+    q = to_device(workloads.query_bits(10, nb, hkv, d))
+    out = torch.empty_like(q)
+    B.pa_paged_decode_fp8(out, q, kc, vc, table, lens, 1, 0.1, 1.0, v_scale, partition_size=64)
+    want = fp8.decode(rows) * v_scale
+    got = to_bits(out).astype(np.uint32) << 16
+    assert np.array_equal(got.view(np.float32).reshape(nb, hkv, d).astype(np.float64), want)
+
+
 def run_parity(wl, scales, partition_size=512, what=""):
     print(f"[fp8] decode {wl.name} {what} scales={scales} P={partition_size}", flush=True)
     h, o = HipStep(wl, fp8=scales), OracleStep(wl, fp8=scales)
