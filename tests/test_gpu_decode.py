@@ -52,7 +52,7 @@ def test_prefix_sharing_decode(partition_size):
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("gqa", [(4, 4), (8, 4), (16, 4), (24, 3)])
+@pytest.mark.parametrize("gqa", [(4, 4), (8, 4), (12, 4), (16, 4), (24, 3), (40, 8)])
 @pytest.mark.parametrize("block_size", [1, 16, 32])
 def test_decode_shapes(head_dim, gqa, block_size):
     hq, hkv = gqa

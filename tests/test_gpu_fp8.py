@@ -151,7 +151,7 @@ def test_fp8_llama_decode_bench_batch():
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("gqa", [(4, 4), (8, 2), (32, 8), (24, 3)])
+@pytest.mark.parametrize("gqa", [(4, 4), (8, 2), (32, 8), (24, 3), (8, 4), (12, 4)])
 @pytest.mark.parametrize("block_size", [1, 16, 32])
 def test_fp8_decode_shapes(head_dim, gqa, block_size):
     hq, hkv = gqa
