@@ -44,6 +44,18 @@
 //    identity.  A sequence with one partition writes its bf16 output
 //    directly; otherwise partials (normalised output, log2 lse) go to the
 //    workspace for the merge pass.
+//
+// Row layouts (explicit partitions, head_dim 128, a multiple of 4 KV heads):
+// one wave per (set of 4 KV heads, partition, sequence), four per
+// work-group, no LDS.  bf16 (partitions up to 1024 tokens): 16-lane row r
+// holds KV head 4 hs + r, 8 elements per lane, so one load reads a token's
+// rows of the 4 heads (1 KiB contiguous).  E4M3 (partitions up to 512, at
+// most 4 query heads per KV head): 16 codes per lane, the half rows holding
+// tokens of either parity, so one load reads two tokens' 512-byte runs.
+// Both keep each row's running maxima in the row (one KV head per row).
+//
+// Merge pass: one wave per (query head, sequence) combines the partials of
+// up to 64 partitions per round with the log-sum-exp identity.
 #include <mutex>
 #include <type_traits>
 
