@@ -932,7 +932,13 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=FP8_SCALES, instanc
                            "kernel": f"{FP8_LONG_CONTEXT_KERNEL} + {MERGE_KERNEL}",
                            "pass_ms": round(sec * 1e3, 3), "layer_us": round(sec / L_ * 1e6, 1),
                            "bytes_per_layer": per_layer, "gbps": round(gbps, 1), "hbm_frac": hbm(gbps),
-                           "seqs_per_s": round(S / sec, 1)}
+                           "seqs_per_s": round(S / sec, 1),
+                           "roofline": {"bound": "hbm", "kernel": f"{FP8_LONG_CONTEXT_KERNEL} + {MERGE_KERNEL}",
+                                        "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                        "frac": hbm(gbps), "traffic": traffic_from_counters("fp8_long_context"),
+                                        "algorithmic_bytes_per_launch": per_layer,
+                                        "launch": "one layer's decode call (partition pass + merge), timed over "
+                                                  "back-to-back passes of the 32 layer calls"}}
     del kv, h, qs
     torch.cuda.empty_cache()
     return res
