@@ -26,8 +26,9 @@
 //   * Each wave stages 16 keys of the tile.  With B >= 16 they lie in one
 //     block: the block id is a scalar load and the row base a scalar address.
 //     With B < 16 every key has its own block; when a cache's whole byte
-//     span fits in 32 bits the lanes' offsets are 32-bit (SMALL), so the
-//     loads take a scalar base and a 32-bit lane offset there too.
+//     span fits in 32 bits the lanes' offsets are 32-bit (KO 1; KO 2 with
+//     B = 1, where a key's offset is its block's alone), so the loads take
+//     a scalar base and a 32-bit lane offset there too.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane owns one query column,
 //     so the softmax max and sum are in-lane (plus one exchange between the
 //     two lane halves).
@@ -56,9 +57,9 @@ namespace {
 
 using namespace prefill_body;
 
-template <int D, int HW, bool CAUSAL, bool BIG, bool F8, bool SMALL>
+template <int D, int HW, bool CAUSAL, bool BIG, bool F8, int KO>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
-  prefill_tile<D, HW, CAUSAL, BIG, F8, SMALL>(a, blockIdx.x);
+  prefill_tile<D, HW, CAUSAL, BIG, F8, KO>(a, blockIdx.x);
 }
 
 template <int D, int HW, bool CAUSAL, bool BIG, bool F8>
@@ -66,13 +67,17 @@ void launch_one(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (!BIG) {
     // B < 16: 32-bit key offsets when every byte offset of a cache fits
     // (num_blocks block strides; ids are clamped into [0, num_blocks))
+    // (block size 1: a key is row 0 of its block)
     const int64_t span = (int64_t)a.num_blocks * a.cache_block_stride * (F8 ? 1 : 2);
     if (span <= 0xffffffffLL) {
-      hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, true>), grid, dim3(256), 0, st, a);
+      if (a.log2_block_size == 0)
+        hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, 2>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, 1>), grid, dim3(256), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<D, HW, CAUSAL, BIG, F8, 0>), grid, dim3(256), 0, st, a);
 }
 
 template <int D, int HW>

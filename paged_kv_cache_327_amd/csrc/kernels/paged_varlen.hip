@@ -36,7 +36,7 @@ struct VarlenGrid {
   int32_t dec_items;     // row layout: wave items, max_parts x num_kv_heads / 4 x decode rows
 };
 
-template <int D, int G, int HW, bool CAUSAL, bool BIG, bool SMALL, bool ROWS>
+template <int D, int G, int HW, bool CAUSAL, bool BIG, int KO, bool ROWS>
 __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArgs d, VarlenGrid vg) {
   const int c = blockIdx.x >> 3, x = blockIdx.x & 7;
   // chunk c runs prefill when the even spread of n_pre_chunks over n_chunks
@@ -44,7 +44,7 @@ __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArg
   const int kp = (int)((int64_t)c * vg.n_pre_chunks / vg.n_chunks);
   const int kp1 = (int)((int64_t)(c + 1) * vg.n_pre_chunks / vg.n_chunks);
   if (kp1 > kp) {
-    prefill_body::prefill_tile<D, HW, CAUSAL, BIG, false, SMALL>(p, 8 * kp + x);
+    prefill_body::prefill_tile<D, HW, CAUSAL, BIG, false, KO>(p, 8 * kp + x);
   } else {
     const int v = 8 * (c - kp) + x;   // decode work-group, in the order of its own grid
     if (v >= vg.dec_wgs) return;
@@ -63,42 +63,48 @@ __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArg
   }
 }
 
-template <int D, int G, bool CAUSAL, bool BIG, bool SMALL, bool ROWS = false>
+template <int D, int G, bool CAUSAL, bool BIG, int KO, bool ROWS = false>
 void launch_one(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, hipStream_t st) {
   constexpr int HW = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-  hipLaunchKernelGGL((varlen_kernel<D, G, HW, CAUSAL, BIG, SMALL, ROWS>), dim3((unsigned)vg.n_chunks * 8), dim3(256),
+  hipLaunchKernelGGL((varlen_kernel<D, G, HW, CAUSAL, BIG, KO, ROWS>), dim3((unsigned)vg.n_chunks * 8), dim3(256),
                      0, st, p, d, vg);
 }
 
 // The decode rows in the row layout when the decode arguments chose it
 // (head_dim 128 only).
-template <int D, int G, bool CAUSAL, bool BIG, bool SMALL>
+template <int D, int G, bool CAUSAL, bool BIG, int KO>
 void launch_layout(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, hipStream_t st) {
   if constexpr (D == 128) {
-    if (d.rows) return launch_one<D, G, CAUSAL, BIG, SMALL, true>(p, d, vg, st);
+    if (d.rows) return launch_one<D, G, CAUSAL, BIG, KO, true>(p, d, vg, st);
   }
-  launch_one<D, G, CAUSAL, BIG, SMALL>(p, d, vg, st);
+  launch_one<D, G, CAUSAL, BIG, KO>(p, d, vg, st);
 }
 
 template <int D, int G>
 void launch_g(const PrefillArgs& p, const DecodeArgs& d, const VarlenGrid& vg, hipStream_t st) {
   const bool big = p.log2_block_size >= 4;
   // B < 16: 32-bit key offsets in the prefill when a cache's byte span fits
+  // (block size 1: a key is row 0 of its block)
   const bool small = (int64_t)p.num_blocks * p.cache_block_stride * 2 <= 0xffffffffLL;
+  const bool b1 = p.log2_block_size == 0;
   if (p.causal) {
     if (big)
-      launch_layout<D, G, true, true, false>(p, d, vg, st);
+      launch_layout<D, G, true, true, 0>(p, d, vg, st);
+    else if (small && b1)
+      launch_layout<D, G, true, false, 2>(p, d, vg, st);
     else if (small)
-      launch_layout<D, G, true, false, true>(p, d, vg, st);
+      launch_layout<D, G, true, false, 1>(p, d, vg, st);
     else
-      launch_layout<D, G, true, false, false>(p, d, vg, st);
+      launch_layout<D, G, true, false, 0>(p, d, vg, st);
   } else {
     if (big)
-      launch_layout<D, G, false, true, false>(p, d, vg, st);
+      launch_layout<D, G, false, true, 0>(p, d, vg, st);
+    else if (small && b1)
+      launch_layout<D, G, false, false, 2>(p, d, vg, st);
     else if (small)
-      launch_layout<D, G, false, false, true>(p, d, vg, st);
+      launch_layout<D, G, false, false, 1>(p, d, vg, st);
     else
-      launch_layout<D, G, false, false, false>(p, d, vg, st);
+      launch_layout<D, G, false, false, 0>(p, d, vg, st);
   }
 }
 

@@ -66,7 +66,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 
 // The prefill work of work-group number bid (every work-group runs it with
 // 256 threads, two work-groups per CU).
-template <int D, int HW, bool CAUSAL, bool BIG, bool F8, bool SMALL>
+// KO, the form of the per-key byte offsets with block size < 16: 0 64-bit,
+// 1 32-bit (every byte offset of a cache fits), 2 32-bit with block size 1
+// (a key's offset is its block's alone).
+template <int D, int HW, bool CAUSAL, bool BIG, bool F8, int KO>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const int bid) {
   constexpr int QS = 4 / HW;                 // 32-query sub-tiles per work-group
   constexpr int DS = D / 16;                 // MFMA k-steps over head_dim
@@ -220,7 +223,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const int bid
       for (int j = 0; j < NI; ++j) {
         int p = tile * kKeys + 16 * wave + KPI * j + kr0;
         p = p < kv_end ? p : 0;
-        e[j] = bt_row[p >> lgB];
+        e[j] = bt_row[KO == 2 ? p : p >> lgB];
       }
     }
   };
@@ -260,7 +263,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, const int bid
   auto key_off = [&](int tile, int j) __attribute__((always_inline)) {
     int p = tile * kKeys + 16 * wave + KPI * j + kr0;
     p = p < kv_end ? p : 0;
-    if constexpr (SMALL) {
+    if constexpr (KO == 2) {
+      // block size 1: the key is row 0 of its block (32-bit offsets, as KO 1)
+      uint32_t off = (uint32_t)clamp_blk(ent[j]) * (uint32_t)(bstride * (F8 ? 1 : 2)) + voff0[j];
+      asm("" : "+v"(off));
+      return off;
+    } else if constexpr (KO == 1) {
       // every byte offset of the cache fits in 32 bits (checked on the host)
       uint32_t off = (uint32_t)clamp_blk(ent[j]) * (uint32_t)(bstride * (F8 ? 1 : 2)) +
                      (uint32_t)(p & Bmask) * (uint32_t)(row_elems * (F8 ? 1 : 2)) + voff0[j];
