@@ -66,7 +66,7 @@ MERGE_KERNEL = "decode_merge_kernel<128>"
 FP8_KERNEL = "decode_partition_kernel<128, 4, true, true, false>"
 FP8_LONG_CONTEXT_KERNEL = "decode_rows8_kernel<4, true>"
 # head_dim, query heads per work-group, causal, block size >= 16, E4M3 caches, 32-bit key offsets
-PREFILL_KERNEL = "prefill_kernel<128, 4, true, true, false, false>"
+PREFILL_KERNEL = "prefill_kernel<128, 4, true, true, false, 0>"
 HEADLINE_PARTITION = 512
 FP8_SCALES = (0.05, 0.05)        # E4M3 k_scale, v_scale of the E4M3 workloads
 FP8_LONG_CONTEXT_PARTITION = 512
@@ -903,7 +903,7 @@ def measure_fp8_decode(torch, B, hip_side, workloads, scales=FP8_SCALES, instanc
     t_p = time_launches(torch, lambda: L.pa_paged_prefill_fp8(*p_args), 10)
     pflops = prefill_flops(pw.q_lens, pw.seq_lens, pw.num_q_heads, pw.head_dim)
     res["prefill"] = {"workload": "16 prefill chunks of 512 queries over U{0..8192} context tokens",
-                      "kernel": "prefill_kernel<128, 4, true, true, true, false>", "us": round(t_p * 1e6, 1),
+                      "kernel": "prefill_kernel<128, 4, true, true, true, 0>", "us": round(t_p * 1e6, 1),
                       "tflops": round(pflops / t_p / 1e12, 1),
                       "frac": round(pflops / t_p / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     del ph, pq, pout
