@@ -878,8 +878,8 @@ __device__ __forceinline__ void e4m3x16_words(const uint4& x, uint32_t (&w)[8]) 
   w[7] = e4m3x2_to_bf16x2<true>(x.w);
 }
 
-// Lane c of row (r, half row hw) of the E4M3 row layout; broadcast of the
-// value of lane 2 h of its row (the first lane holding head h) to the row.
+// E4M3 row layout: the value of lane 2 h of each 16-lane row (the first
+// lane that finishes head h's scores) broadcast to the whole row.
 __device__ __forceinline__ float row_bcast_pair(float x, int h) {
   switch (h) {
     case 0: return dpp<kDppRowBcast0 + 0>(x);
