@@ -48,7 +48,8 @@ def sources():
 #   (around its step loop).
 # * prefill, head_dim 64: two waves per SIMD, no scratch.
 # * decode partition pass: no AGPRs and no scratch; three waves per SIMD up
-#   to 4 query heads per KV head, two for 5-8.
+#   to 4 query heads per KV head (four with E4M3 caches, whose 8-wave
+#   work-groups then share a CU two at a time), two for 5-8.
 # * decode row layouts (bf16 and E4M3): no AGPRs, no scratch, two waves per
 #   SIMD.
 # * mixed-batch kernel (prefill and decode bodies in one kernel): 256
@@ -67,7 +68,8 @@ def _budget(name, targs):
         d, big = targs[0], targs[4]
         return (256, 0, 0 if (d == 64 or big) else 32, 2)
     if name == "decode_partition_kernel":
-        return (512, 0, 0, 3) if targs[1] <= 4 else (512, 0, 0, 2)
+        g, f8 = targs[1], targs[3]
+        return (512, 0, 0, 2) if g > 4 else (512, 0, 0, 4 if f8 else 3)
     if name in ("decode_rows_kernel", "decode_rows8_kernel"):
         return 512, 0, 0, 2
     return 512, 256, 0, 1

@@ -10,7 +10,11 @@
 namespace pa {
 namespace decode_body {
 
-constexpr int kWaves = 4;
+// Waves of a head-layout work-group: E4M3 rows with at most 4 query heads
+// per KV head take 8 (their registers leave room for four waves per SIMD, so
+// two 8-wave work-groups share a CU); every other case 4.
+template <bool F8, int G>
+constexpr int kWaves = F8 && G <= 4 ? 8 : 4;
 constexpr int kHalf = 16;     // tokens of a half tile, inside one block when B >= 16
 constexpr int kBuffers = 2;   // register buffers per wave (tiles in flight + 1)
 constexpr int kHalves8 = 1;   // half tiles per tile with E4M3 rows (bf16: 1)
@@ -258,8 +262,8 @@ template <bool APP>
 using RowsOf = typename std::conditional<APP, AppendRows, NoAppend>::type;
 
 // The partition pass of work-group (partition part, KV head g, sequence s);
-// every work-group runs it with 256 threads.
-template <int D, int G, bool BIG, bool F8, bool APP>
+// every work-group runs it with 64 W threads (W waves).
+template <int D, int G, bool BIG, bool F8, bool APP, int W = kWaves<F8, G>>
 __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const RowsOf<APP>& rows, const int part,
                                                  const int g, const int s) {
   using T = typename std::conditional<F8, uint8_t, uint16_t>::type;  // cache element
@@ -271,9 +275,9 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
   using P = PieceOf<F8>;
   constexpr int NSET = (G + 3) / 4;        // sets of 4 heads: one score per lane per set
   __shared__ int32_t s_bt[BIG ? 1 : kChunk];
-  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][D];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_m[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[W][G][D];
+  __shared__ float s_l[W][G];
+  __shared__ float s_m[W][G];
 
   static_assert(!(APP && F8), "appending decode takes bf16 caches");
   static_assert(LPT == 4 * TPL, "a group reduces 4 heads x TPL tokens, one value per lane");
@@ -329,7 +333,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
     const int j0 = c0 >> lgB;
     int nj = ((c0 + kChunk - 1) >> lgB) - j0 + 1;
     nj = nj < width - j0 ? nj : width - j0;
-    for (int i = tid; i < nj; i += 256) {
+    for (int i = tid; i < nj; i += 64 * W) {
       int b = entry(j0 + i);
       b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
       s_bt[i] = b;
@@ -348,7 +352,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int hf = 0; hf < NH; ++hf) {
-        const int i = (tw + k * kWaves * kTile + hf * kHalf) >> lgB;
+        const int i = (tw + k * W * kTile + hf * kHalf) >> lgB;
         pre[k][hf] = bt_row[i < wmax ? i : wmax];
       }
     const int is = start >> lgB;
@@ -457,7 +461,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
     // computed after it from buffers already loaded.  All branches here are
     // wave-uniform.  The first loads are issued whatever n_tiles is (they
     // stay inside the cache), so nothing delays them.
-    constexpr int kStep = kWaves * kTile;
+    constexpr int kStep = W * kTile;
     constexpr int NB = kBuffers;
     int t = c0 + wave * kTile;
     const int n_tiles = t < c1 ? (c1 - t + kStep - 1) / kStep : 0;
@@ -502,7 +506,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
   // Merge.  All lane groups of a wave share the running maxima, so their
   // partial sums add directly: (D = 64) the two groups of each 16-lane row
   // with DPP, then the four rows in registers with gfx950's lane swaps, then
-  // the four waves through LDS.  permlane32_swap(x, y) exchanges lanes 32..63
+  // the W waves through LDS.  permlane32_swap(x, y) exchanges lanes 32..63
   // of x with lanes 0..31 of y, permlane16_swap(x, y) the odd 16-lane rows of
   // x with the even rows of y; adding the two results of a swap sums rows
   // (0, 2) and (1, 3), then rows 0 and 1.  With the lane's NV sums flattened
@@ -579,15 +583,15 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs& a, const Rows
   __syncthreads();
 
   // Combine the waves: thread -> (head h, dim d) outputs.
-  for (int o = tid; o < G * D; o += 256) {
+  for (int o = tid; o < G * D; o += 64 * W) {
     const int h = o / D, d = o % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
     float L = 0.f, A = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float mw = s_m[w][h];
         const float e = mw == kNegInf ? 0.f : fast_exp2(mw - M);
         L += s_l[w][h] * e;

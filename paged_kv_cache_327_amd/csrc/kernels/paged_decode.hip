@@ -9,7 +9,9 @@
 // work-groups (split-K) among the kernel's concerns but gives no design; the
 // design below is ours.
 //
-// Partition pass: one work-group (4 waves) per (partition, KV head g, seq s).
+// Partition pass: one work-group per (partition, KV head g, seq s), of 4
+// waves (8 for E4M3 caches with at most 4 query heads per KV head, whose
+// registers allow four waves per SIMD).
 //  * A token's K (or V) row of head g is held by D / 8 lanes, 8 elements
 //    each (one 16-byte piece of bf16, or 8 one-byte E4M3 codes), so every
 //    row load is a coalesced access of the row's contiguous bytes.  With
@@ -69,7 +71,7 @@ namespace {
 using namespace decode_body;
 
 template <int D, int G, bool BIG, bool F8, bool APP>
-__global__ void __launch_bounds__(256) decode_partition_kernel(DecodeArgs a, RowsOf<APP> rows) {
+__global__ void __launch_bounds__((64 * kWaves<F8, G>)) decode_partition_kernel(DecodeArgs a, RowsOf<APP> rows) {
   decode_partition<D, G, BIG, F8, APP>(a, rows, blockIdx.x, blockIdx.y, (int)blockIdx.z);
 }
 
@@ -223,7 +225,8 @@ int64_t row_items(const DecodeArgs& a, int32_t n) {
 template <int D, int G, bool BIG, bool F8>
 int launch_parts(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, BIG, F8, false>), grid, dim3(256), 0, st, a, NoAppend{0});
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, BIG, F8, false>), grid, dim3(64 * kWaves<F8, G>), 0, st, a,
+                     NoAppend{0});
   return (int)hipGetLastError();
 }
 
@@ -303,9 +306,11 @@ int launch_g_append(const DecodeArgs& a, const int64_t* slots, const int32_t* po
     }
     const dim3 grid(a.max_parts, a.num_kv_heads, n);
     if (big)
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(256), 0, st, b, rows);
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, true, false, true>), grid, dim3(64 * kWaves<false, G>), 0, st, b,
+                         rows);
     else
-      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false, true>), grid, dim3(256), 0, st, b, rows);
+      hipLaunchKernelGGL((decode_partition_kernel<D, G, false, false, true>), grid, dim3(64 * kWaves<false, G>), 0, st, b,
+                         rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
