@@ -57,8 +57,8 @@ __global__ void __launch_bounds__(256, 2) varlen_kernel(PrefillArgs p, DecodeArg
                                                                           rest % d.max_parts, hs, rest / d.max_parts);
     } else {
       const int part = v % d.max_parts, rest = v / d.max_parts;
-      decode_body::decode_partition<D, G, BIG, false, false>(d, decode_body::NoAppend{0}, part,
-                                                            rest % d.num_kv_heads, rest / d.num_kv_heads);
+      decode_body::decode_partition<D, G, BIG, false, false, 4>(d, decode_body::NoAppend{0}, part,
+                                                               rest % d.num_kv_heads, rest / d.num_kv_heads);
     }
   }
 }
