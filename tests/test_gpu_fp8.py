@@ -161,6 +161,17 @@ def test_fp8_decode_shapes(head_dim, gqa, block_size):
         run_parity(wl, (0.0173, 0.05), p, what=f"P={p}")
 
 
+@pytest.mark.parametrize("partition_size", [1024, 2048])
+def test_fp8_head_layout_long_partitions(partition_size):
+    """E4M3 partitions longer than 512 tokens at head_dim 128 and 4 query
+    heads per KV head take the head layout with 8-wave work-groups; every
+    wave's tiles, the merge across waves and the merge across partitions
+    against the oracle (lengths around partition and wave-tile edges)."""
+    lens = [0, 1, 127, 128, 1023, 1024, 1025, 2049, 3000, 4100]
+    wl = workloads.custom(f"fp8_long_p{partition_size}", 41, 32, 8, 128, 16, lens)
+    run_parity(wl, (0.0173, 0.05), partition_size, what=f"P={partition_size}")
+
+
 def test_fp8_rejects_bad_scales_and_strides():
     kc = torch.zeros((4, 16, 1, 64), dtype=torch.uint8, device="cuda")
     k = torch.zeros((1, 1, 64), dtype=torch.bfloat16, device="cuda")
