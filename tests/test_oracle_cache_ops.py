@@ -41,6 +41,14 @@ def test_padding_and_out_of_range_slots_are_skipped():
     assert np.array_equal(flat[3], k[1]) and np.array_equal(flat[0], k[3])
     assert np.all(flat[1] == 0) and np.all(flat[2] == 0)
     assert np.array_equal(vc.reshape(4, 1, 4)[3], v[1])
+    # a padding id with no later write to the last row: that row (where a
+    # negative index would land) and the row a past-the-end slot would
+    # alias stay untouched
+    kc[:] = 0
+    vc[:] = 0
+    cache_ops.reshape_and_cache(kc, vc, k, v, np.array([-1, 1, 4, -1]))
+    assert np.array_equal(flat[1], k[1]) and np.array_equal(vc.reshape(4, 1, 4)[1], v[1])
+    assert np.all(flat[[0, 2, 3]] == 0) and np.all(vc.reshape(4, 1, 4)[[0, 2, 3]] == 0)
 
 
 def test_copy_blocks_matches_fancy_index():
