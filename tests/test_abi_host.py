@@ -220,6 +220,28 @@ def test_r7_walk_native(golden):
     assert B.pa_pool_num_free(p) == e["free_before"] - e["to_allocate"]
 
 
+def test_pinned_blocks_are_not_reused_until_unpinned_native():
+    """The library's pool on the oracle pin's scenario: a pinned, freed
+    sequence's blocks stay out of the free queue until the unpin."""
+    p = B.pa_pool_create(8, 4)
+    B.pa_pool_add_seq(p, 0)
+    B.pa_pool_append(p, 0, 10)
+    table, _ = B.pa_pool_block_table(p, [0], 3)
+    blocks = table[0].tolist()
+    assert list(B.pa_pool_pin(p, 0, 5)) == blocks
+    B.pa_pool_free_seq(p, 0)
+    assert B.pa_pool_num_free(p) == 5 and not set(blocks) & set(list(B.pa_pool_free_order(p)))
+    B.pa_pool_add_seq(p, 1)
+    B.pa_pool_append(p, 1, 20)
+    table, _ = B.pa_pool_block_table(p, [1], 5)
+    assert not set(table[0].tolist()) & set(blocks)
+    with pytest.raises(B.NoSpace):
+        B.pa_pool_append(p, 1, 1)
+    B.pa_pool_unpin(p, 5)
+    assert list(B.pa_pool_free_order(p)) == blocks[::-1]
+    B.pa_pool_check(p)
+
+
 def test_failed_append_is_all_or_nothing_native():
     p = B.pa_pool_create(1, 4)
     B.pa_pool_add_seq(p, 0)

@@ -12,18 +12,20 @@ against that mistake.  Everything runs on the CPU.
 import numpy as np
 import pytest
 
-from oracle import attention, cache_ops, fp8
+from oracle import attention, cache_ops, fp8, sizing
 from oracle import pool_model as pm
 from tests import test_oracle_attention as TA
 from tests import test_oracle_cache_ops as TC
 from tests import test_oracle_fp8 as TF
 from tests import test_oracle_pool as TP
+from tests import test_oracle_sizing as TS
 
 _softmax = attention.softmax_attend
 _gather = attention.gather_sequence
 _reshape = cache_ops.reshape_and_cache
 _copy = cache_ops.copy_blocks
 _decode8 = fp8.decode
+_hash = pm.block_hash
 
 
 def _golden():
@@ -78,6 +80,32 @@ POOL_PINS = [
     TP.test_free_puts_tail_block_at_head,
     TP.test_shared_blocks_survive_free,
     lambda: TP.test_randomized_against_list_model(0),
+]
+
+PREFIX_PINS = [
+    TP.test_fnv1a_published_vectors,
+    TP.test_block_hash_chain_captures_position,
+    TP.test_prefix_hit_after_free_and_eviction_on_reuse,
+    TP.test_duplicate_content_keeps_first_block,
+    TP.test_pinned_sole_owner_copies_its_partial_tail,
+    TP.test_pinned_blocks_are_not_reused_until_unpinned,
+    TP.test_copy_endpoints_retained_until_copies_done,
+    lambda: TP.test_randomized_prefix_cache_and_pins(0),
+]
+SIZING_PINS = [
+    lambda: TS.test_bytes_per_token(GOLDEN),
+    lambda: TS.test_pool_blocks_two_floor_divisions(GOLDEN),
+    lambda: TS.test_contiguous_reservation_arithmetic(GOLDEN),
+    lambda: TS.test_paged_concurrency_ceiling(GOLDEN),
+    lambda: TS.test_internal_fragmentation_bound(GOLDEN),
+    lambda: TS.test_table_metadata(GOLDEN),
+    lambda: TS.test_r7_sizing(GOLDEN),
+    lambda: TS.test_partial_hit_index(GOLDEN),
+    lambda: TS.test_tail_waste_distribution(GOLDEN),
+    lambda: TS.test_tail_waste_bound(16),
+    lambda: TS.test_llama70b_sizing(GOLDEN),
+    lambda: TS.test_lab_and_interactive(GOLDEN),
+    TS.test_shared_prefix_blocks,
 ]
 
 
@@ -408,6 +436,103 @@ def test_pool_pins_catch(monkeypatch, name):
     assert failures(POOL_PINS) > 0, name
 
 
+# ---------------------------------------------------------------- prefix cache and pins
+
+
+def hash_without_parent(parent, tokens):
+    return _hash(0, tokens)                              # planted: the chain's parent is dropped
+
+
+def hash_two_byte_tokens(parent, tokens):
+    h = pm.FNV_OFFSET
+    data = (int(parent) & pm.MASK64).to_bytes(8, "little")
+    for t in tokens:
+        data += (int(t) & 0xFFFF).to_bytes(2, "little")   # planted: token ids as 2 bytes
+    for byte in data:
+        h = ((h ^ byte) * pm.FNV_PRIME) & pm.MASK64
+    return h
+
+
+def release_hashed_to_head(self, blocks):
+    self.free.extendleft(reversed(list(blocks)))         # planted: cached blocks evicted first
+
+
+def touch_keeps_free(self, b):
+    self.ref[b] += 1                                     # planted: a reused cached block stays queued
+
+
+def copies_done_keeps_holds(self):
+    self.pending = []                                    # planted: copy endpoints never released
+
+
+def pin_tail_only(self, seq, transfer):
+    if seq not in self.tables:
+        raise pm.InvalidArgument(f"unknown sequence {seq}")
+    if transfer in self.transfers:
+        raise pm.InvalidArgument(f"transfer {transfer} exists")
+    blocks = list(self.tables[seq])[-1:]                 # planted: only the tail block pinned
+    for b in blocks:
+        self.pins[b] += 1
+    self.transfers[transfer] = blocks
+    return list(self.tables[seq])
+
+
+def cache_blocks_last_wins(self, seq, tokens):
+    if seq not in self.tables:
+        raise pm.InvalidArgument(f"unknown sequence {seq}")
+    B = self.block_size
+    h = 0
+    for j in range(len(tokens) // B):
+        h = pm.block_hash(h, tokens[j * B:(j + 1) * B])
+        b = self.tables[seq][j]
+        if self.hash_of[b] is None:
+            old = self.cached.get(h)
+            if old is not None:
+                self.hash_of[old] = None
+            self.cached[h] = b                           # planted: a duplicate replaces the first block
+            self.hash_of[b] = h
+
+
+PREFIX_MUTANTS = {
+    "FNV prime off by two": (pm, "FNV_PRIME", pm.FNV_PRIME + 2),
+    "FNV offset basis zero": (pm, "FNV_OFFSET", 0),
+    "chain parent dropped": (pm, "block_hash", hash_without_parent),
+    "token ids hashed as two bytes": (pm, "block_hash", hash_two_byte_tokens),
+    "cached blocks released to the head": (pm.PoolModel, "_release", release_hashed_to_head),
+    "a prefix hit leaves the block queued": (pm.PoolModel, "_touch", touch_keeps_free),
+    "copy endpoints never released": (pm.PoolModel, "copies_done", copies_done_keeps_holds),
+    "pin covers the tail block only": (pm.PoolModel, "pin", pin_tail_only),
+    "duplicate content replaces the first block": (pm.PoolModel, "cache_blocks", cache_blocks_last_wins),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFIX_MUTANTS))
+def test_prefix_cache_pins_catch(monkeypatch, name):
+    target, attr, value = PREFIX_MUTANTS[name]
+    monkeypatch.setattr(target, attr, value)
+    assert failures(PREFIX_PINS) > 0, name
+
+
+# ---------------------------------------------------------------- closed forms
+
+
+SIZING_MUTANTS = {
+    "K or V only": ("kv_bytes_per_token", lambda L, H, D, e: L * H * D * e),
+    "pool blocks rounded up": ("blocks_for_bytes", lambda pool, bpt, B: -(-(pool // bpt) // B)),
+    "blocks for tokens floored": ("blocks_for_tokens", lambda n, B: n // B),
+    "tail waste as the remainder": ("tail_waste", lambda n, B: n % B),
+    "shared blocks include the partial tail": ("shared_full_blocks", lambda n, B: -(-n // B)),
+    "table bytes per request row": ("block_table_bytes", lambda r, m, B, ib=4: r * m * ib),
+}
+
+
+@pytest.mark.parametrize("name", list(SIZING_MUTANTS))
+def test_sizing_pins_catch(monkeypatch, name):
+    attr, fn = SIZING_MUTANTS[name]
+    monkeypatch.setattr(sizing, attr, fn)
+    assert failures(SIZING_PINS) > 0, name
+
+
 def test_unmutated_oracle_passes_every_pin():
-    for pins in (ATTENTION_PINS, CACHE_PINS, FP8_PINS, POOL_PINS):
+    for pins in (ATTENTION_PINS, CACHE_PINS, FP8_PINS, POOL_PINS, PREFIX_PINS, SIZING_PINS):
         assert failures(pins) == 0

@@ -172,6 +172,30 @@ def test_pinned_sole_owner_copies_its_partial_tail():
         p.pin(0, 8)                              # handles are unique
 
 
+def test_pinned_blocks_are_not_reused_until_unpinned():
+    """A pin covers every block the table names when the transfer is pinned
+    (reading 24, the CPU reference allocator section): none of them returns
+    to the free queue while pinned, even after its sequence is freed and
+    the rest of the pool is allocated; the unpin releases them tail first,
+    as freeing a sequence does."""
+    p = PoolModel(8, 4)
+    p.add_seq(0)
+    p.append(0, 10)                              # 3 blocks, the last one partial
+    blocks = p.block_table(0)
+    assert p.pin(0, 5) == blocks
+    p.free_seq(0)
+    assert p.num_free() == 5 and not set(blocks) & set(p.free_order())
+    p.check()
+    p.add_seq(1)
+    p.append(1, 20)                              # takes the 5 free blocks
+    assert not set(p.block_table(1)) & set(blocks)
+    with pytest.raises(NoSpace):
+        p.append(1, 1)
+    p.unpin(5)
+    assert p.free_order() == blocks[::-1]        # the tail block at the head, as a free does
+    p.check()
+
+
 def test_copy_endpoints_retained_until_copies_done():
     """A free in the same step cannot recycle a copy's source: both endpoints
     stay retained until the copies are reported done."""
