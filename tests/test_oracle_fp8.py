@@ -117,6 +117,12 @@ def test_decode_over_fp8_caches_equals_bf16_caches_of_the_same_values(k_scale, v
         k = (rng.standard_normal((n, hkv, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         v = (rng.standard_normal((n, hkv, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
         cache_ops.reshape_and_cache_fp8(kc8, vc8, k, v, np.array(slots[s]), k_scale, v_scale)
+        # each cache's codes are torch's E4M3 of value * fp32(1 / its own scale)
+        for cache, bits, sc in ((kc8, k, k_scale), (vc8, v, v_scale)):
+            x = torch.from_numpy((bits.astype(np.uint32) << 16).view(np.float32))
+            want = (x * torch.tensor(np.float32(1.0) / np.float32(sc))).to(torch.float8_e4m3fn)
+            got = cache.reshape(nb * bs, hkv, d)[np.array(slots[s])]
+            assert np.array_equal(got, want.view(torch.uint8).numpy())
 
     def to_bf16_bits(codes, scale):
         f = (fp8.decode(codes) * scale).astype(np.float32)

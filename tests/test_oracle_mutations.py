@@ -51,6 +51,7 @@ ATTENTION_PINS = [
     TA.test_empty_sequence,
 ]
 CACHE_PINS = [
+    lambda: TF.test_decode_over_fp8_caches_equals_bf16_caches_of_the_same_values(0.25, 2.0),
     TC.test_scatter_round_trips_through_table_gather,
     TC.test_padding_and_out_of_range_slots_are_skipped,
     TC.test_copy_blocks_matches_fancy_index,
@@ -302,7 +303,29 @@ def decode_append_length_kept(block_tables, seq_lens, key_cache, value_cache, ke
     _reshape(key_cache, value_cache, key, value, np.asarray(slots, dtype=np.int64))
 
 
+def decode_append_table_kept(block_tables, seq_lens, key_cache, value_cache, key, value, slots, positions):
+    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
+        if slot >= 0:
+            seq_lens[i] = int(positions[i]) + 1          # planted: the table mirror is not updated
+    _reshape(key_cache, value_cache, key, value, np.asarray(slots, dtype=np.int64))
+
+
+def copy_blocks_first_cache_only(caches, pairs, num_blocks):
+    _copy(list(caches)[:1], pairs, num_blocks)           # planted: the other caches are not copied
+
+
+def reshape_fp8_one_scale(key_cache, value_cache, key, value, slot_mapping, k_scale, v_scale):
+    _reshape(key_cache, value_cache, fp8.quantize_bf16(key, k_scale),
+             fp8.quantize_bf16(value, k_scale), slot_mapping)   # planted: V written at K's scale
+
+
 CACHE_MUTANTS = {
+    "table mirror not updated by the append": ("decode_append", decode_append_table_kept),
+    "only the first cache copied": ("copy_blocks", copy_blocks_first_cache_only),
+    "V written at K's scale": ("reshape_and_cache_fp8", reshape_fp8_one_scale),
+    "kernel ids reversed within a block": ("map_to_kernel_blocks", lambda ids, k: np.array(
+        [int(b) * int(k) + (int(k) - 1 - j) for b in np.asarray(ids).reshape(-1) for j in range(int(k))],
+        dtype=np.int64)),
     "slot without its offset in the block": ("slot_mapping", slot_mapping_mutant(offset=False)),
     "step tokens taken from the front": ("slot_mapping", slot_mapping_mutant(from_front=True)),
     "padding slot written": ("reshape_and_cache", reshape_wrapping),
