@@ -39,6 +39,7 @@ def _golden():
 GOLDEN = _golden()
 
 ATTENTION_PINS = [
+    lambda: TF.test_decode_over_fp8_caches_equals_bf16_caches_of_the_same_values(0.25, 2.0),
     lambda: TA.test_decode_matches_torch_sdpa(16, (8, 2)),
     lambda: TA.test_decode_matches_torch_sdpa(1, (6, 1)),
     TA.test_lse_matches_scipy_logsumexp,
@@ -216,7 +217,17 @@ def paged_prefill_mask(strict=False, shift=0):
     return run
 
 
+_decode_real = attention.paged_decode
+
+
+def paged_decode_one_scale(q_bits, key_cache, value_cache, block_tables, seq_lens, scale, k_scale=1.0,
+                           v_scale=1.0):
+    return _decode_real(q_bits, key_cache, value_cache, block_tables, seq_lens, scale, k_scale,
+                        k_scale)                         # planted: V read at K's scale
+
+
 ATTENTION_MUTANTS = {
+    "V read at K's scale": ("paged_decode", paged_decode_one_scale),
     "scale dropped": ("softmax_attend", lambda q, k, v, scale, visible=None: _softmax(q, k, v, 1.0, visible)),
     "scale squared": ("softmax_attend", lambda q, k, v, scale, visible=None: _softmax(q, k, v, scale * scale,
                                                                                      visible)),
@@ -442,7 +453,21 @@ def append_mutant(cow_when_full=False, capacity_without_copy=False, slot_off_by_
     return run
 
 
+def free_head_first(self, seq):
+    if seq not in self.tables:
+        raise pm.InvalidArgument(f"unknown sequence {seq}")
+    released = []
+    for b in self.tables[seq]:                           # planted: head first, not tail first
+        self.ref[b] -= 1
+        if not self._retained(b):
+            released.append(b)
+    self._release(released)
+    del self.tables[seq]
+    del self.lens[seq]
+
+
 POOL_MUTANTS = {
+    "free walks the table head first": ("free_seq", free_head_first),
     "freed blocks to the tail": ("_release", release_to_tail),
     "allocation from the tail": ("_pop", pop_from_tail),
     "fork takes no references": ("fork", fork_without_refs),
