@@ -68,6 +68,12 @@ def test_mixed_batch_matches_oracle_and_separate_calls(d, hq, hkv, bs):
     assert torch.equal(out[qsl[nd]:].view(torch.int16), op.view(torch.int16))
 
 
+@pytest.mark.parametrize("bs", [2, 64, 256])
+def test_mixed_batch_at_other_block_sizes(bs):
+    """The same checks at block sizes the benched steps do not use."""
+    test_mixed_batch_matches_oracle_and_separate_calls(128, 32, 8, bs)
+
+
 @pytest.mark.parametrize("case", ["decode_only", "prefill_only", "unsplit", "not_causal"])
 def test_mixed_batch_edge_cases(case):
     if case == "decode_only":
