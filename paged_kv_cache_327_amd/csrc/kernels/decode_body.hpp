@@ -10,7 +10,7 @@
 namespace pa {
 namespace decode_body {
 
-// Waves of a head-layout work-group: E4M3 rows with at most 4 query heads
+// Waves of a head-layout work-group: E4M3 caches with at most 4 query heads
 // per KV head take 8 (their registers leave room for four waves per SIMD, so
 // two 8-wave work-groups share a CU); every other case 4.
 template <bool F8, int G>
