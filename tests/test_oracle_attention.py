@@ -224,3 +224,21 @@ def test_bf16_conversion_exact():
     ours = workloads.f32_to_bf16_bits(x.numpy())
     theirs = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, theirs)
+
+
+def test_prefill_row_subset_equals_the_full_rows():
+    """paged_prefill(rows=...) computes the listed (request, query row) pairs
+    exactly as the full call does and leaves every other row zero."""
+    lens, q_lens = [30, 70, 9], [10, 70, 4]
+    ks, vs = logical_kv(14, lens, 2, 32)
+    _, kc, vc, bt, sl = paged_from_logical(ks, vs, 4, 40, np.random.default_rng(14).permutation(40))
+    qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    q = workloads.query_bits(14, int(qsl[-1]), 4, 32)
+    full = attention.paged_prefill(q, kc, vc, bt, qsl, sl, 0.21)
+    rows = [(0, 0), (0, 9), (1, 33), (1, 69), (2, 3)]
+    part = attention.paged_prefill(q, kc, vc, bt, qsl, sl, 0.21, rows=rows)
+    picked = np.zeros(int(qsl[-1]), dtype=bool)
+    for i, j in rows:
+        picked[qsl[i] + j] = True
+    np.testing.assert_allclose(part[picked], full[picked], rtol=0, atol=1e-14)
+    assert np.all(part[~picked] == 0)
